@@ -1,0 +1,367 @@
+"""Pins for the CPU oracle against what the BitNet b1.58 page and mathematics fix.
+
+Each test checks the oracle against something other than itself: a closed
+form, an invariant, brute force on a tiny input, a textbook transform, a
+library routine on a special case, or a worked example derived by hand.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import bitlinear_oracle as O
+
+
+def f32(x):
+    return np.float32(x)
+
+
+# ---------------------------------------------------------------- f32_nearest
+def test_f32_nearest_matches_numpy_double_to_float():
+    # numpy's float64 -> float32 cast is one IEEE round-to-nearest-even; any
+    # float64 value is an exact rational, so the two must agree everywhere.
+    rng = np.random.default_rng(1)
+    mant = rng.random(4000) + 1.0
+    expo = rng.integers(-160, 130, size=4000)
+    vals = np.ldexp(mant, expo) * np.where(rng.random(4000) < 0.5, -1.0, 1.0)
+    for d in vals:
+        got = O.f32_nearest(Fraction(float(d)))
+        want = np.float32(d)
+        assert got.tobytes() == want.tobytes(), d
+
+
+def test_f32_nearest_ties_and_subnormals():
+    two = Fraction(2)
+    assert O.f32_nearest(1 + two ** -24) == f32(1.0)                  # tie -> even
+    assert O.f32_nearest(1 + 3 * two ** -24) == f32(1 + 2.0 ** -22)   # tie -> even (up)
+    assert O.f32_nearest(two ** -150) == f32(0.0)                     # tie below min subnormal
+    assert O.f32_nearest(3 * two ** -150) == f32(2.0 ** -148)
+    assert O.f32_nearest(Fraction(1, 3)) == np.float32(1.0 / 3.0)
+    assert O.f32_nearest(Fraction(-7, 10)) == np.float32(-0.7)
+    assert np.isinf(O.f32_nearest(two ** 128))
+
+
+# ---------------------------------------------------------------- gamma
+@pytest.mark.parametrize("a", [1.0, 0.02, 0.0123456789, 3.0e30, 1.0e-42, 2.0 ** -149])
+def test_gamma_constant_magnitude(a):
+    # |W| constant = a  =>  mean |W| = a exactly.
+    rng = np.random.default_rng(2)
+    a32 = f32(a)
+    W = (np.where(rng.random((37, 48)) < 0.5, -1.0, 1.0) * a32).astype(np.float32)
+    assert O.absmean_gamma(W) == a32
+
+
+def test_gamma_bruteforce_fraction_tiny():
+    # Exponent range from subnormal to large, plus zeros and signed zeros.
+    rng = np.random.default_rng(3)
+    for trial in range(20):
+        N, K = int(rng.integers(1, 6)), 16 * int(rng.integers(1, 4))
+        mant = rng.random((N, K)) + 0.5
+        expo = rng.integers(-150, 40, size=(N, K))
+        W = np.ldexp(mant, expo).astype(np.float32)
+        W[rng.random((N, K)) < 0.2] = 0.0
+        W[rng.random((N, K)) < 0.5] *= -1
+        exact = sum((Fraction(float(abs(v))) for v in W.reshape(-1)), Fraction(0))
+        want = O.f32_nearest(exact / (N * K))
+        assert O.absmean_gamma(W).tobytes() == want.tobytes()
+
+
+def test_gamma_matches_fsum_on_gaussian():
+    # math.fsum returns the correctly rounded float64 sum; dividing and
+    # rounding to fp32 lands on the same fp32 except in double-rounding cases
+    # of probability ~2^-29 (none for this seed).
+    rng = np.random.default_rng(4)
+    W = (rng.standard_normal((300, 1024)) * 0.02).astype(np.float32)
+    want = np.float32(math.fsum(np.abs(W).astype(np.float64).ravel()) / W.size)
+    assert O.absmean_gamma(W) == want
+
+
+def test_gamma_statistics_gaussian():
+    # E|w| = sigma sqrt(2/pi) for w ~ N(0, sigma^2); sd of |w| = sigma sqrt(1-2/pi).
+    from synth import make_weight
+    sigma = 0.02
+    W = make_weight(0, "pin/gamma-stats", 512, 4096, sigma)
+    g = float(O.absmean_gamma(W))
+    se = sigma * math.sqrt(1 - 2 / math.pi) / math.sqrt(W.size)
+    assert abs(g - sigma * math.sqrt(2 / math.pi)) < 5 * se
+
+
+def test_gamma_zero_weight():
+    W = np.zeros((4, 32), np.float32)
+    assert O.absmean_gamma(W) == 0.0
+    assert (O.ternarize(W, O.absmean_gamma(W)) == 0).all()
+
+
+# ---------------------------------------------------------------- RoundClip / ternarize
+def test_round_clip_edge_table():
+    half_below = np.nextafter(f32(0.5), f32(0))        # 0.49999997
+    below_mhalf = np.nextafter(f32(-0.5), f32(-1))     # -0.50000006
+    z = np.array([0.5, half_below, -0.5, below_mhalf, 1.7, -3.0, 0.0, -0.0,
+                  1.5, -1.5, np.inf, -np.inf], dtype=np.float32)
+    want = [1, 0, 0, -1, 1, -1, 0, 0, 1, -1, 1, -1]
+    assert O.round_clip(z, -1, 1).tolist() == want
+    # wider range: floor(z + 0.5) half up
+    z2 = np.array([2.5, -2.5, 126.5, -126.5, 127.49, 300.0, -300.0], dtype=np.float32)
+    assert O.round_clip(z2, -127, 127).tolist() == [3, -2, 127, -126, 127, 127, -127]
+
+
+def test_ternarize_edges_at_power_of_two_scale():
+    # Pick gamma so that gamma + eps rounds to exactly 0.5; then W = z * 0.5 is
+    # exact and W / (gamma + eps) = z exactly.
+    gamma = f32(0.5) - f32(1e-5)
+    assert f32(gamma + O.EPS) == f32(0.5)
+    half_below = np.nextafter(f32(0.5), f32(0))
+    below_mhalf = np.nextafter(f32(-0.5), f32(-1))
+    z = np.array([0.5, half_below, -0.5, below_mhalf, 1.7, -3.0, 0.0, 0.25,
+                  -0.25, 1e-30, 2.0 ** 100, -2.0 ** 100, 0.75, -0.75, 1.0, -1.0],
+                 dtype=np.float32)
+    W = (z * f32(0.5)).astype(np.float32)[None, :]
+    want = [1, 0, 0, -1, 1, -1, 0, 0, 0, 0, 1, -1, 1, -1, 1, -1]
+    assert O.ternarize(W, gamma)[0].tolist() == want
+
+
+def test_ternarize_alphabet_and_zero_fraction():
+    # P(|w| < gamma/2) for Gaussian w: 2 Phi(sqrt(2/pi)/2) - 1 = 0.3101 (any sigma).
+    from synth import make_weight
+    W = make_weight(0, "pin/zero-frac", 512, 2048, 0.02)
+    Wt = O.ternarize(W, O.absmean_gamma(W))
+    assert set(np.unique(Wt).tolist()) <= {-1, 0, 1}
+    p0 = 2 * 0.5 * (1 + math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))) - 1
+    assert abs(p0 - 0.3101) < 1e-4
+    frac0 = float((Wt == 0).mean())
+    se = math.sqrt(p0 * (1 - p0) / W.size)
+    assert abs(frac0 - p0) < 6 * se
+    # symmetric halves
+    assert abs(float((Wt == 1).mean()) - float((Wt == -1).mean())) < 0.003
+
+
+def test_ternarize_sylvester_hadamard_is_fixed_point():
+    from scipy.linalg import hadamard
+    H = hadamard(64).astype(np.float32)
+    assert O.absmean_gamma(H) == 1.0
+    assert (O.ternarize(H, O.absmean_gamma(H)) == H).all()
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_worked_bytes():
+    Wt = np.array([[1, -1, 0, 0, 1, -1, 0, 0, 1, -1, 0, 0, 1, 0, -1, 0],
+                   [1, -1] * 8], dtype=np.int8)
+    # codes row 0: 2,0,1,1, 2,0,1,1, 2,0,1,1, 2,1,0,1
+    # byte i collects weights i, 4+i, 8+i, 12+i at bits 0,2,4,6:
+    #   byte0 = 2|2<<2|2<<4|2<<6 = 0xAA; byte1 = 0|0|0|1<<6 = 0x40;
+    #   byte2 = 1|1<<2|1<<4|0 = 0x15;   byte3 = 1|1<<2|1<<4|1<<6 = 0x55
+    # row 1 codes alternate 2,0: bytes 0,2 = 0xAA and bytes 1,3 = 0x00
+    P = O.pack_codes(Wt)
+    assert P.tobytes().hex() == "aa401555" + "aa00aa00"
+
+
+def test_pack_zero_group_and_size_and_roundtrip():
+    rng = np.random.default_rng(5)
+    assert O.pack_codes(np.zeros((2, 32), np.int8)).tobytes() == b"\x55" * 16
+    for (N, K) in [(1, 16), (3, 48), (7, 160), (16, 1040)]:
+        Wt = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        P = O.pack_codes(Wt)
+        assert P.shape == (N, K // 4) and P.dtype == np.uint8
+        assert (O.unpack_codes(P, K) == Wt).all()
+        # no 2-bit field ever holds 3
+        fields = np.stack([(P >> s) & 3 for s in (0, 2, 4, 6)])
+        assert not (fields == 3).any()
+
+
+def test_pack_word_shift_mask_gives_consecutive_codes():
+    # (word >> 2j) & 0x03030303 must hold the codes of k = 16g+4j .. 16g+4j+3
+    # in byte order (little endian), i.e. ready as four int8 operands.
+    rng = np.random.default_rng(6)
+    Wt = rng.integers(-1, 2, size=(3, 64)).astype(np.int8)
+    words = O.pack_codes(Wt).view("<u4").reshape(3, 4)
+    for n in range(3):
+        for g in range(4):
+            for j in range(4):
+                v = (int(words[n, g]) >> (2 * j)) & 0x03030303
+                got = [(v >> (8 * i)) & 0xFF for i in range(4)]
+                want = [int(Wt[n, 16 * g + 4 * j + i]) + 1 for i in range(4)]
+                assert got == want
+
+
+# ---------------------------------------------------------------- activations
+def test_quant_round_half_up_at_unit_scale():
+    # absmax b = 127 - 2^-17 makes b + eps round to exactly 127.0, so the
+    # per-token factor is exactly 1 and q = X.
+    b = f32(127.0) - f32(2.0 ** -17)
+    assert f32(b + O.EPS) == f32(127.0)
+    X = np.array([[b, 0.5, -0.5, 2.5, -2.5, np.nextafter(f32(0.5), f32(0)),
+                   np.nextafter(f32(-0.5), f32(-1)), 100.5, -b, 0.0, 63.25, -63.75,
+                   1.0, -1.0, 126.5, -126.5]], dtype=np.float32)
+    Xq, s, xs, beta = O.quantize_activations(X)
+    assert Xq[0].tolist() == [127, 1, 0, 3, -2, 0, -1, 101, -127, 0, 63, -64, 1, -1, 127, -126]
+    assert beta[0] == b and s[0] == np.float32(b) / np.float32(127)
+    assert xs[0] == sum(Xq[0].astype(int))
+
+
+def test_quant_factor_grouping_and_exact_rounding():
+    # The page groups the factor (Q_b - 1)/(beta + eps) before multiplying X.
+    # Brute force with exact rationals: factor = RN32(127 / RN32(beta + eps)),
+    # q = RN32(x * factor), x~ = floor(q + 1/2); x is placed within a few ulps
+    # of every k + 1/2 boundary, where a different grouping or a rounding slip
+    # changes the integer.
+    for beta in (4.0, 0.7431, 37.25, 1e-3):
+        b = f32(beta)
+        den = O.f32_nearest(Fraction(float(b)) + Fraction(float(O.EPS)))
+        factor = O.f32_nearest(Fraction(127) / Fraction(float(den)))
+        qb = O.f32_nearest(Fraction(float(b)) * Fraction(float(factor)))
+        xs = [b]
+        want = [min(127, math.floor(Fraction(float(qb)) + Fraction(1, 2)))]
+        for k in range(-126, 127, 3):
+            x0 = O.f32_nearest((Fraction(k) + Fraction(1, 2)) / Fraction(float(factor)))
+            for d in (-2, -1, 0, 1, 2):
+                x = x0
+                for _ in range(abs(d)):
+                    x = np.nextafter(x, f32(np.sign(d) * np.inf))
+                if abs(x) > b:
+                    continue
+                q = O.f32_nearest(Fraction(float(x)) * Fraction(float(factor)))
+                xs.append(x)
+                want.append(math.floor(Fraction(float(q)) + Fraction(1, 2)))
+        Xq, s, xsum, beta_o = O.quantize_activations(np.array([xs], dtype=np.float32))
+        assert Xq[0].tolist() == want
+
+
+def test_quant_scale_is_exactly_rounded_quotient():
+    # x_scale = beta / 127 rounded once to fp32.
+    rng = np.random.default_rng(11)
+    X = (rng.standard_normal((400, 16)) * np.exp(rng.uniform(-8, 8, size=(400, 1)))).astype(np.float32)
+    _, s, _, beta = O.quantize_activations(X)
+    for m in range(400):
+        assert s[m] == O.f32_nearest(Fraction(float(beta[m])) / 127)
+
+
+def test_quant_invariants_gaussian_with_outliers():
+    from synth import make_acts
+    X = make_acts(0, "pin/quant", 64, 4096,
+                  {"outlier_frac": Fraction(1, 200), "outlier_scale": 100.0})
+    Xq, s, xs, beta = O.quantize_activations(X)
+    assert np.abs(Xq.astype(int)).max() <= 127
+    # beta is exactly the absmax, and the absmax element maps to +-127
+    # (true whenever beta >= 253 eps).
+    am = np.abs(X).argmax(axis=1)
+    assert (beta == np.abs(X).max(axis=1)).all()
+    assert (np.abs(Xq[np.arange(64), am].astype(int)) == 127).all()
+    # reconstruction: |X - X~ (beta+eps)/127| <= (beta+eps)/254 (+ fp32 slack)
+    step = (beta.astype(np.float64) + 1e-5) / 127
+    err = np.abs(X - Xq.astype(np.float64) * step[:, None])
+    assert (err <= step[:, None] * (0.5 + 1e-5)).all()
+    assert (xs == Xq.astype(np.int64).sum(axis=1)).all()
+
+
+def test_quant_zero_token():
+    X = np.zeros((2, 32), np.float32)
+    X[1, 5] = -3.0
+    Xq, s, xs, beta = O.quantize_activations(X)
+    assert (Xq[0] == 0).all() and s[0] == 0 and xs[0] == 0
+    assert Xq[1, 5] == -127 and s[1] == np.float32(3.0) / np.float32(127)
+
+
+# ---------------------------------------------------------------- accumulation
+def test_three_accumulation_routes_agree():
+    rng = np.random.default_rng(7)
+    for (M, N, K) in [(1, 1, 16), (3, 5, 48), (4, 9, 128)]:
+        Wt = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        Xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+        a = O.integer_matmul(Wt, Xq)
+        assert (a == O.integer_matmul_loops(Wt, Xq)).all()
+        assert (a == O.masked_add_matmul(Wt, Xq)).all()
+
+
+def _fwht(v):
+    # Textbook fast Walsh-Hadamard transform (Sylvester / natural order).
+    v = np.array(v, dtype=np.int64)
+    h = 1
+    while h < len(v):
+        for i in range(0, len(v), 2 * h):
+            a = v[i:i + h].copy()
+            b = v[i + h:i + 2 * h].copy()
+            v[i:i + h] = a + b
+            v[i + h:i + 2 * h] = a - b
+        h *= 2
+    return v
+
+
+def test_accumulation_special_matrices():
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(8)
+    K = 64
+    Xq = rng.integers(-127, 128, size=(3, K)).astype(np.int8)
+    # identity rows give x~ back
+    assert (O.integer_matmul(np.eye(K, dtype=np.int8), Xq) == Xq).all()
+    # an all-(+1) row gives sum x~, an all-(-1) row gives -sum x~
+    Wt = np.stack([np.ones(K, np.int8), -np.ones(K, np.int8), np.zeros(K, np.int8)])
+    acc = O.integer_matmul(Wt, Xq)
+    assert (acc[:, 0] == Xq.astype(int).sum(1)).all()
+    assert (acc[:, 1] == -Xq.astype(int).sum(1)).all() and (acc[:, 2] == 0).all()
+    # Sylvester-Hadamard rows give the Walsh-Hadamard transform of x~
+    H = hadamard(K).astype(np.int8)
+    acc = O.integer_matmul(H, Xq)
+    for m in range(3):
+        assert (acc[m] == _fwht(Xq[m])).all()
+    # bound |acc| <= 127 * nnz(row)
+    Wt = rng.integers(-1, 2, size=(20, K)).astype(np.int8)
+    acc = O.integer_matmul(Wt, Xq)
+    assert (np.abs(acc) <= 127 * (Wt != 0).sum(1)[None, :]).all()
+
+
+def test_accumulation_linear_in_x():
+    rng = np.random.default_rng(9)
+    Wt = rng.integers(-1, 2, size=(11, 96)).astype(np.int8)
+    a = rng.integers(-60, 61, size=(2, 96)).astype(np.int8)
+    b = rng.integers(-60, 61, size=(2, 96)).astype(np.int8)
+    lhs = O.integer_matmul(Wt, (a.astype(int) + b.astype(int)).astype(np.int8))
+    assert (lhs == O.integer_matmul(Wt, a) + O.integer_matmul(Wt, b)).all()
+
+
+# ---------------------------------------------------------------- rescale
+def test_rescale_matches_bruteforce_float_product():
+    # y = sum_k (W~ gamma)(X~ beta/127): brute force with exact fsum.
+    rng = np.random.default_rng(10)
+    W = (rng.standard_normal((6, 48)) * 0.02).astype(np.float32)
+    X = rng.standard_normal((3, 48)).astype(np.float32)
+    r = O.bitlinear(W, X)
+    for m in range(3):
+        for n in range(6):
+            terms = [float(r["Wt"][n, k]) * float(r["gamma"]) * float(r["Xq"][m, k])
+                     * float(r["beta"][m]) / 127 for k in range(48)]
+            assert abs(r["y"][m, n] - math.fsum(terms)) <= 1e-12 * (1 + abs(r["y"][m, n]))
+
+
+# ---------------------------------------------------------------- worked example
+def test_worked_example_end_to_end():
+    """Hand-derived example (no page prints one); every value below was worked
+    out by hand from the formulas:
+
+    |W| sums: row 0 = 9.625, row 1 = 16 * 0.5 = 8  ->  gamma = 17.625/32 = 141/256.
+    gamma + eps = 0.55079125 -> fp32 0.55079126; W / that: |1| -> 1.82, |.5| -> 0.91,
+    |.25| -> 0.45, |.125| -> 0.23, |2| -> 3.6, so W~ row 0 below and row 1 = (+1, -1)*8.
+    absmax(X) = 4; 127 / fp32(4 + 1e-5) = 31.74992; q = X * 31.74992 rounded half up.
+    acc row 0 = 32 + 63 - 127 - 32 - 63 + 24 - 48 = -151;
+    acc row 1 = (sum even x~ = -31) - (sum odd x~ = 238) = -269.
+    """
+    W = np.array([[1, -1, .25, -.25, .5, -.5, 0, 0, 2, -2, .125, 0, 1, 0, -1, 0],
+                  [.5, -.5] * 8], dtype=np.float32)
+    X = np.array([[1, -2, .5, 3, -4, 0, .25, 1, -1, 2, 0, 0, .75, -.5, 1.5, 4]],
+                 dtype=np.float32)
+    r = O.bitlinear(W, X)
+    assert r["gamma"] == np.float32(141 / 256)
+    assert r["Wt"].tolist() == [[1, -1, 0, 0, 1, -1, 0, 0, 1, -1, 0, 0, 1, 0, -1, 0],
+                                [1, -1] * 8]
+    assert r["packed"].tobytes().hex() == "aa401555aa00aa00"
+    assert r["Xq"][0].tolist() == [32, -63, 16, 95, -127, 0, 8, 32, -32, 63, 0, 0,
+                                   24, -16, 48, 127]
+    assert r["x_sum"][0] == 207
+    assert r["beta"][0] == 4.0 and r["x_scale"][0] == np.float32(4.0) / np.float32(127)
+    assert r["acc"][0].tolist() == [-151, -269]
+    assert abs(r["y"][0, 0] - (-151 * 141 / 256 * 4 / 127)) < 1e-12
+    assert abs(r["y"][0, 0] - (-2.6194636)) < 1e-6
+    assert abs(r["y"][0, 1] - (-4.6664616)) < 1e-6
+    # codes route: sum c x~ - sum x~ with c = W~ + 1
+    c = r["Wt"].astype(int) + 1
+    assert (c @ r["Xq"][0].astype(int) - 207).tolist() == [-151, -269]
