@@ -1,0 +1,173 @@
+/*
+ * bitlinear.h - C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear library.
+ *
+ * The library computes the ternary-weight / int8-activation projection
+ *
+ *     Y = (X~ W~^T) * gamma * beta / 127
+ *
+ * defined on the page "BitNet b1.58: Mathematical Foundations of 1.58-Bit
+ * Ternary Quantization, Absmean Scaling, and Multiplication-Free LLM
+ * Architectures" (llms.blog), section 2 "Mathematical Formulation of the
+ * BitLinear b1.58 Layer": the absmean weight quantiser, the absmax activation
+ * quantiser, and the linear transformation with its rescale.  The integer
+ * product X~ W~^T uses only additions and subtractions of int8 values into
+ * int32 (same section, last paragraph; section 6 "Vectorized Ternary GEMV
+ * with SIMD" gives the masked-add form).
+ *
+ * Conventions for every entry point
+ *   - Shapes: N = d_out (rows of W), K = d_in, M = tokens.  W is [N][K]
+ *     row-major fp32, X is [M][K] row-major fp32, Y is [M][N] row-major.
+ *   - All buffers are device memory allocated and owned by the caller.  The
+ *     library never allocates, never frees, and keeps no pointer after a
+ *     call returns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream of the current device).  Buffers must stay valid
+ *     until that work completes.  Calls are stateless and re-entrant; the same
+ *     inputs give the same output bytes on every call.
+ *   - Arguments are validated before any HIP call; an invalid call returns a
+ *     status without touching the GPU.  A launch failure returns
+ *     BITLINEAR_ERR_HIP.  Faults during execution surface at the caller's
+ *     next synchronisation.  bitlinear_last_error() gives a thread-local
+ *     description of the last non-OK status.
+ *   - Inputs must be finite; NaN or infinity give unspecified (but memory
+ *     safe) results.
+ *   - Limits: K % 16 == 0; 1 <= K <= 131072 (so |acc| < 2^24 and the int32
+ *     accumulator converts to fp32 exactly); N*K < 2^31 for packing.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+/* Packed weight format: 2 bits per weight, see bitlinear_pack_weights. */
+#define BITLINEAR_PACK_FORMAT_BLT2_V1 1
+#define BITLINEAR_MAX_K 131072
+
+typedef enum bitlinear_status {
+  BITLINEAR_OK = 0,
+  BITLINEAR_ERR_NULL = 1,      /* a required pointer is NULL */
+  BITLINEAR_ERR_SHAPE = 2,     /* M, N or K < 1, K % 16 != 0, K > BITLINEAR_MAX_K, size limit */
+  BITLINEAR_ERR_ALIGN = 3,     /* a pointer is not aligned as documented */
+  BITLINEAR_ERR_DTYPE = 4,     /* unknown output dtype */
+  BITLINEAR_ERR_NO_DEVICE = 5, /* no HIP device visible */
+  BITLINEAR_ERR_ARCH = 6,      /* current device is not gfx950 */
+  BITLINEAR_ERR_WORKSPACE = 7, /* workspace NULL or smaller than the size query */
+  BITLINEAR_ERR_HIP = 8        /* a HIP runtime call or kernel launch failed */
+} bitlinear_status;
+
+typedef enum bitlinear_dtype {
+  BITLINEAR_F32 = 0,  /* fp32 Y */
+  BITLINEAR_BF16 = 1, /* bf16 Y, rounded to nearest even from the fp32 result */
+  BITLINEAR_I32 = 2   /* raw int32 accumulators X~ W~^T, no rescale */
+} bitlinear_dtype;
+
+/* Version of this ABI (BITLINEAR_ABI_VERSION). */
+int bitlinear_abi_version(void);
+
+/* Bytes of packed weights for an N x K matrix: N * K / 4.  0 if the shape is
+ * invalid. */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Bytes of workspace bitlinear_pack_weights needs for an N x K matrix
+ * (partial sums of the exact |W| accumulator and the two ternary
+ * thresholds).  0 if the shape is invalid. */
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * Absmean ternarisation and 2-bit packing of a latent weight matrix.
+ * Page section 2, "Weight Quantization: Absmean Scaling":
+ *   gamma = mean_ij |W_ij|,   W~_ij = RoundClip(W_ij / (gamma + eps), -1, 1),
+ *   RoundClip(z, a, b) = max(a, min(b, floor(z + 0.5))),  eps = 1e-5.
+ *
+ * gamma is the exact mean of |W| rounded once to fp32 (nearest, ties to
+ * even); gamma + eps is an fp32 addition; z = W / (gamma + eps) is the
+ * correctly rounded fp32 quotient and floor(z + 0.5) is taken exactly.
+ *
+ * W          [N][K] fp32, device, 16-byte aligned (read only).
+ * W_packed   [N][K/4] bytes, device, 16-byte aligned (written).  Format
+ *            BLT2-v1: code c = W~ + 1 in {0,1,2} (3 never occurs).  Row n is
+ *            K/16 little-endian 32-bit words at byte n*K/4; word g holds
+ *            k = 16g + t, t = 0..15, and weight t = 4j + i sits in byte i at
+ *            bits 2j..2j+1.  So (word >> 2j) & 0x03030303 holds the codes of
+ *            k = 16g+4j .. 16g+4j+3 in byte order.  An all-zero group is
+ *            0x55555555.
+ * gamma      one fp32, device, 4-byte aligned (written): the absmean scale.
+ * workspace  device, 16-byte aligned, >= bitlinear_pack_workspace_bytes(N, K).
+ *            Contents need no initialisation and are scratch after the call.
+ * stream     hipStream_t or NULL.
+ */
+bitlinear_status bitlinear_pack_weights(const float* W, int64_t N, int64_t K,
+                                        uint8_t* W_packed, float* gamma,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * Per-token absmax int8 quantisation of activations.  Page section 2,
+ * "Activation Quantization: Absmax Scaling" (per-token variant, symmetric
+ * range, Q_b - 1 = 127):
+ *   beta_m = max_k |X_mk|,
+ *   X~_mk = RoundClip(X_mk * (127 / (beta_m + eps)), -127, 127).
+ * The factor 127 / (beta_m + eps) is formed in fp32 (add, then correctly
+ * rounded divide), each element is multiplied by it in fp32, and
+ * floor(q + 0.5) is taken exactly.
+ *
+ * X        [M][K] fp32, device, 16-byte aligned (read only).
+ * X_q      [M][K] int8, device, 16-byte aligned (written).
+ * x_scale  [M] fp32, device, 4-byte aligned (written): beta_m / 127 rounded
+ *          to fp32 (the per-token factor of the rescale).
+ * x_sum    [M] int32, device, 4-byte aligned (written): sum_k X~_mk.  The
+ *          forward pass needs it (it stores W~ + 1 and subtracts this sum).
+ */
+bitlinear_status bitlinear_quant_acts(const float* X, int64_t M, int64_t K,
+                                      int8_t* X_q, float* x_scale, int32_t* x_sum,
+                                      void* stream);
+
+/* Bytes of workspace bitlinear_forward needs (0 for every shape in this
+ * version; a NULL workspace is then accepted). */
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The projection on packed weights and quantised activations.  Page section
+ * 2, "The Linear Transformation and Rescaling":
+ *   acc[m][n] = sum_k W~[n][k] X~[m][k]        (exact, int32)
+ *   Y[m][n]   = acc[m][n] * gamma * x_scale[m]  (fp32: (float)acc * gamma,
+ *               then * x_scale; bf16 rounds that fp32 value to nearest even)
+ * The scale is applied once per output after the integer sum (page section
+ * 6, "Scaling Factor Fusion").
+ *
+ * W_packed  [N][K/4] BLT2-v1 bytes from bitlinear_pack_weights, device,
+ *           16-byte aligned.
+ * gamma     one fp32, device.
+ * X_q, x_scale, x_sum   as written by bitlinear_quant_acts (device; X_q
+ *           16-byte aligned).  x_sum must equal sum_k X_q[m][k].
+ * Y         [M][N], device, aligned to its element size; fp32, bf16 or int32
+ *           (BITLINEAR_I32 stores acc itself and ignores gamma/x_scale).
+ * workspace may be NULL when bitlinear_forward_workspace_bytes() is 0.
+ * Integer results are bit-exact and independent of the launch shape.
+ */
+bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma,
+                                   int64_t N, int64_t K,
+                                   const int8_t* X_q, const float* x_scale,
+                                   const int32_t* x_sum, int64_t M,
+                                   void* Y, bitlinear_dtype y_dtype,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Static English name of a status. */
+const char* bitlinear_status_string(bitlinear_status s);
+
+/* Thread-local detail for the last non-OK status returned on this thread
+ * ("" if none).  Valid until the next call on the same thread. */
+const char* bitlinear_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,19 @@
+"""MI355X (gfx950) BitNet b1.58 BitLinear: ternary weights x int8 activations.
+
+The projection runs in hand-written HIP kernels behind the C ABI declared in
+include/bitlinear.h; this package is its Python binding.
+"""
+from .binding import (  # noqa: F401
+    DTYPES,
+    LIB_PATH,
+    SIGNATURES,
+    STATUS,
+    BitLinearError,
+    bitlinear_forward,
+    bitlinear_pack_weights,
+    bitlinear_quant_acts,
+    forward_workspace_bytes,
+    load,
+    pack_workspace_bytes,
+    packed_bytes,
+)

@@ -1,0 +1,163 @@
+"""ctypes binding of libbitlinear.so (argument marshalling only).
+
+Torch supplies device memory and streams; every step of the projection runs
+in the library's HIP kernels.  There is no CPU fallback: if the library is
+missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbitlinear.so")
+
+STATUS = {
+    0: "BITLINEAR_OK", 1: "BITLINEAR_ERR_NULL", 2: "BITLINEAR_ERR_SHAPE", 3: "BITLINEAR_ERR_ALIGN",
+    4: "BITLINEAR_ERR_DTYPE", 5: "BITLINEAR_ERR_NO_DEVICE", 6: "BITLINEAR_ERR_ARCH",
+    7: "BITLINEAR_ERR_WORKSPACE", 8: "BITLINEAR_ERR_HIP",
+}
+DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
+
+# Every symbol the header declares, with its ctypes signature.
+_c_i64, _c_size, _vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = {
+    "bitlinear_abi_version": (ctypes.c_int, []),
+    "bitlinear_packed_bytes": (_c_size, [_c_i64, _c_i64]),
+    "bitlinear_pack_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "bitlinear_pack_weights": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_size, _vp]),
+    "bitlinear_quant_acts": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "bitlinear_forward_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "bitlinear_forward": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp,
+                                         ctypes.c_int, _vp, _c_size, _vp]),
+    "bitlinear_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "bitlinear_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the library once.  torch is imported first so that the library binds
+    to the HIP runtime torch already loaded (same soname), which makes torch's
+    stream handles valid inside the library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (HIP runtime first)
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with ternary_bitlinear_amd.build.build()")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise BitLinearError(status, _lib.bitlinear_last_error().decode())
+
+
+def _stream(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return load().bitlinear_packed_bytes(N, K)
+
+
+def pack_workspace_bytes(N: int, K: int) -> int:
+    return load().bitlinear_pack_workspace_bytes(N, K)
+
+
+def forward_workspace_bytes(M: int, N: int, K: int) -> int:
+    return load().bitlinear_forward_workspace_bytes(M, N, K)
+
+
+def bitlinear_pack_weights(W, W_packed=None, gamma=None, workspace=None, stream=None):
+    """W [N][K] fp32 -> (W_packed uint8 [N][K/4], gamma fp32 [1]) on W's device."""
+    import torch
+    lib = load()
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    need = lib.bitlinear_pack_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=W.device)
+    _dev(W_packed, torch.uint8, "W_packed")
+    _dev(gamma, torch.float32, "gamma")
+    _check(lib.bitlinear_pack_weights(W.data_ptr(), N, K, W_packed.data_ptr(), gamma.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+    return W_packed, gamma
+
+
+def bitlinear_quant_acts(X, X_q=None, x_scale=None, x_sum=None, stream=None):
+    """X [M][K] fp32 -> (X_q int8 [M][K], x_scale fp32 [M], x_sum int32 [M])."""
+    import torch
+    lib = load()
+    _dev(X, torch.float32, "X")
+    M, K = X.shape
+    if X_q is None:
+        X_q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    if x_sum is None:
+        x_sum = torch.empty(M, dtype=torch.int32, device=X.device)
+    _dev(X_q, torch.int8, "X_q")
+    _dev(x_scale, torch.float32, "x_scale")
+    _dev(x_sum, torch.int32, "x_sum")
+    _check(lib.bitlinear_quant_acts(X.data_ptr(), M, K, X_q.data_ptr(), x_scale.data_ptr(),
+                                    x_sum.data_ptr(), _stream(stream)))
+    return X_q, x_scale, x_sum
+
+
+def bitlinear_forward(W_packed, gamma, X_q, x_scale, x_sum, N=None, K=None, y_dtype="bf16",
+                      Y=None, workspace=None, stream=None):
+    """Packed W~ and quantised X -> Y [M][N] (fp32, bf16 or raw int32 accumulators)."""
+    import torch
+    lib = load()
+    _dev(W_packed, torch.uint8, "W_packed")
+    _dev(X_q, torch.int8, "X_q")
+    M, Kx = X_q.shape
+    K = Kx if K is None else K
+    N = W_packed.shape[0] if N is None else N
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[y_dtype]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=tdt, device=X_q.device)
+    _dev(Y, tdt, "Y")
+    ws_need = lib.bitlinear_forward_workspace_bytes(M, N, K)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=X_q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.bitlinear_forward(W_packed.data_ptr(), gamma.data_ptr(), N, K, X_q.data_ptr(),
+                                 x_scale.data_ptr(), x_sum.data_ptr(), M, Y.data_ptr(),
+                                 DTYPES[y_dtype], ws_ptr, ws_bytes, _stream(stream)))
+    return Y

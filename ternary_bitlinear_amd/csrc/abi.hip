@@ -1,0 +1,167 @@
+// C ABI of the BitLinear library: argument validation, device checks and
+// dispatch to the kernel launchers.  Every check that can fail runs before
+// the first HIP call of an entry point.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/bitlinear.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bitlinear_status fail(bitlinear_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bitlinear_status fail(bitlinear_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool shape_ok_k(int64_t K) { return K >= 16 && K % 16 == 0 && K <= BITLINEAR_MAX_K; }
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch_ok[64];
+
+bitlinear_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count == 0)
+      return fail(BITLINEAR_ERR_NO_DEVICE, "no HIP device visible");
+    return fail(BITLINEAR_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  }
+  if (dev >= 64) return fail(BITLINEAR_ERR_ARCH, "device index %d not supported", dev);
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(BITLINEAR_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(BITLINEAR_ERR_ARCH, "device %d is not gfx950", dev);
+  return BITLINEAR_OK;
+}
+
+bitlinear_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BITLINEAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_last_error.clear();
+  return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || N > kMaxDim || !shape_ok_k(K)) return 0;
+  return (size_t)(N * (K / 4));
+}
+
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 1 || N > kMaxDim || !shape_ok_k(K) || N * K > kMaxDim) return 0;
+  return bl::pack_workspace_bytes(N, K);
+}
+
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  (void)M; (void)N; (void)K;
+  return 0;
+}
+
+bitlinear_status bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
+                                        float* gamma, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (!W || !W_packed || !gamma) return fail(BITLINEAR_ERR_NULL, "pack_weights: NULL buffer");
+  if (N < 1 || N > kMaxDim || !shape_ok_k(K) || N * K > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "pack_weights: invalid shape N=%lld K=%lld (need N>=1, "
+                "K%%16==0, 16<=K<=%d, N*K<2^31)", (long long)N, (long long)K, BITLINEAR_MAX_K);
+  if (!aligned(W, 16) || !aligned(W_packed, 16) || !aligned(gamma, 4))
+    return fail(BITLINEAR_ERR_ALIGN, "pack_weights: W and W_packed need 16-byte alignment, "
+                "gamma 4-byte");
+  const size_t need = bl::pack_workspace_bytes(N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(BITLINEAR_ERR_WORKSPACE, "pack_weights: workspace of %zu bytes needed, got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(BITLINEAR_ERR_ALIGN, "pack_weights: workspace alignment");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_pack(W, N, K, W_packed, gamma, workspace,
+                                  reinterpret_cast<hipStream_t>(stream)),
+                  "pack_weights launch");
+}
+
+bitlinear_status bitlinear_quant_acts(const float* X, int64_t M, int64_t K, int8_t* X_q,
+                                      float* x_scale, int32_t* x_sum, void* stream) {
+  if (!X || !X_q || !x_scale || !x_sum) return fail(BITLINEAR_ERR_NULL, "quant_acts: NULL buffer");
+  if (M < 1 || M > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "quant_acts: invalid shape M=%lld K=%lld", (long long)M,
+                (long long)K);
+  if (!aligned(X, 16) || !aligned(X_q, 16) || !aligned(x_scale, 4) || !aligned(x_sum, 4))
+    return fail(BITLINEAR_ERR_ALIGN, "quant_acts: X and X_q need 16-byte alignment");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_quant(X, M, K, X_q, x_scale, x_sum,
+                                   reinterpret_cast<hipStream_t>(stream)),
+                  "quant_acts launch");
+}
+
+bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma, int64_t N,
+                                   int64_t K, const int8_t* X_q, const float* x_scale,
+                                   const int32_t* x_sum, int64_t M, void* Y,
+                                   bitlinear_dtype y_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (!W_packed || !gamma || !X_q || !x_scale || !x_sum || !Y)
+    return fail(BITLINEAR_ERR_NULL, "forward: NULL buffer");
+  if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "forward: invalid shape M=%lld N=%lld K=%lld", (long long)M,
+                (long long)N, (long long)K);
+  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+    return fail(BITLINEAR_ERR_DTYPE, "forward: unknown y_dtype %d", (int)y_dtype);
+  const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
+  if (!aligned(W_packed, 16) || !aligned(X_q, 16) || !aligned(gamma, 4) || !aligned(x_scale, 4) ||
+      !aligned(x_sum, 4) || !aligned(Y, ya))
+    return fail(BITLINEAR_ERR_ALIGN, "forward: W_packed/X_q need 16-byte alignment, Y its "
+                "element size");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward(W_packed, gamma, N, K, X_q, x_scale, x_sum, M, Y,
+                                     (int)y_dtype, reinterpret_cast<hipStream_t>(stream)),
+                  "forward launch");
+}
+
+const char* bitlinear_status_string(bitlinear_status s) {
+  switch (s) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_ERR_NULL: return "null pointer";
+    case BITLINEAR_ERR_SHAPE: return "invalid shape";
+    case BITLINEAR_ERR_ALIGN: return "misaligned pointer";
+    case BITLINEAR_ERR_DTYPE: return "invalid dtype";
+    case BITLINEAR_ERR_NO_DEVICE: return "no HIP device";
+    case BITLINEAR_ERR_ARCH: return "device is not gfx950";
+    case BITLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITLINEAR_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* bitlinear_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Device helpers shared by the BitLinear kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+constexpr int kWave = 64;
+
+// ---- integer / bit helpers --------------------------------------------------
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- wave reductions (all lanes receive the result) -------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += (uint64_t)__shfl_xor((unsigned long long)v, o, kWave);
+  return v;
+}
+
+// ---- MFMA int8 operand types --------------------------------------------------
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_i32_16x16x64_i8: C[16x16] += A[16x64] * B[64x16].
+// Lane l supplies A row (l % 16) and B column (l % 16) for k-group (l / 16);
+// the 16 bytes of a lane's A and B operands pair up byte for byte, so any
+// assignment of k values to (k-group, byte) slots works as long as A and B use
+// the same one.  Result: lane l, register r holds C[4 * (l / 16) + r][l % 16].
+__device__ __forceinline__ i32x4 mfma_i8_16x16x64(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Four int8 codes per dword from one packed BLT2 word: dword d holds the codes
+// (W~ + 1, values 0..2) of k = 16g + 4d .. 16g + 4d + 3, i.e. the 16 codes of
+// the word in natural k order.
+__device__ __forceinline__ i32x4 expand_codes(uint32_t w) {
+  i32x4 r;
+  r.x = (int32_t)(w & 0x03030303u);
+  r.y = (int32_t)((w >> 2) & 0x03030303u);
+  r.z = (int32_t)((w >> 4) & 0x03030303u);
+  r.w = (int32_t)((w >> 6) & 0x03030303u);
+  return r;
+}
+
+}  // namespace bl

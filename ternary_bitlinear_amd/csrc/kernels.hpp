@@ -1,0 +1,24 @@
+// Host-side launchers of the BitLinear kernels (called by the C ABI layer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+constexpr int64_t kPackWsHeader = 256;   // bytes before the partial sums
+
+size_t pack_workspace_bytes(int64_t N, int64_t K);
+
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* gamma,
+                       void* workspace, hipStream_t stream);
+
+hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float* x_scale,
+                        int32_t* x_sum, hipStream_t stream);
+
+// y_dtype: 0 fp32, 1 bf16, 2 int32 (raw accumulators).
+hipError_t launch_forward(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
+                          const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
+                          int64_t M, void* Y, int y_dtype, hipStream_t stream);
+
+}  // namespace bl

@@ -1,0 +1,110 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and
+rejects invalid calls before touching HIP (no compute is launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+LIB = os.path.join(ROOT, "ternary_bitlinear_amd", "libbitlinear.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from ternary_bitlinear_amd.build import build
+        build()
+    import ternary_bitlinear_amd as tb
+    return tb.load()
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
+    declared = set(declared_functions())
+    assert declared <= exported, declared - exported
+    assert exported <= declared, exported - declared   # nothing undeclared leaks out
+
+
+def test_binding_covers_every_declared_symbol():
+    import ternary_bitlinear_amd as tb
+    assert set(tb.SIGNATURES) == set(declared_functions())
+
+
+def test_no_torch_types_in_header():
+    text = open(HEADER).read()
+    assert "torch" not in text.lower()
+    assert "at::" not in text and "c10" not in text and "Tensor" not in text
+
+
+def test_size_queries(lib):
+    assert lib.bitlinear_abi_version() == 1
+    assert lib.bitlinear_packed_bytes(8640, 3200) == 8640 * 800
+    assert lib.bitlinear_packed_bytes(3, 48) == 36
+    assert lib.bitlinear_packed_bytes(0, 64) == 0
+    assert lib.bitlinear_packed_bytes(4, 40) == 0          # K % 16 != 0
+    assert lib.bitlinear_packed_bytes(4, 131072 + 16) == 0  # K above the limit
+    ws = lib.bitlinear_pack_workspace_bytes(28672, 8192)
+    assert 256 < ws <= 256 + 8192 * 10 * 8
+    assert lib.bitlinear_pack_workspace_bytes(1, 16) >= 256 + 4 * 80
+    assert lib.bitlinear_pack_workspace_bytes(1 << 20, 1 << 12) == 0   # N*K >= 2^31
+    assert lib.bitlinear_forward_workspace_bytes(64, 4096, 4096) == 0
+
+
+def _last(lib):
+    return lib.bitlinear_last_error().decode()
+
+
+FAKE = 1 << 20          # a 16-byte aligned address; never dereferenced (validation fails first)
+
+
+def test_validation_statuses_without_gpu_calls(lib):
+    st = lib.bitlinear_pack_weights(None, 4, 16, FAKE, FAKE, FAKE, 4096, None)
+    assert st == 1 and "NULL" in _last(lib)
+    assert lib.bitlinear_pack_weights(FAKE, 4, 24, FAKE, FAKE, FAKE, 1 << 20, None) == 2
+    assert lib.bitlinear_pack_weights(FAKE, 0, 16, FAKE, FAKE, FAKE, 1 << 20, None) == 2
+    assert lib.bitlinear_pack_weights(FAKE + 4, 4, 16, FAKE, FAKE, FAKE, 1 << 20, None) == 3
+    assert lib.bitlinear_pack_weights(FAKE, 4, 16, FAKE, FAKE, FAKE, 8, None) == 7
+    assert lib.bitlinear_pack_weights(FAKE, 4, 16, FAKE, FAKE, None, 1 << 20, None) == 7
+    assert lib.bitlinear_quant_acts(FAKE, 2, 16, FAKE, FAKE, None, None) == 1
+    assert lib.bitlinear_quant_acts(FAKE, 2, 8, FAKE, FAKE, FAKE, None) == 2
+    assert lib.bitlinear_quant_acts(FAKE, 2, 16, FAKE + 8, FAKE, FAKE, None) == 3
+    args = [FAKE, FAKE, 16, 64, FAKE, FAKE, FAKE, 4, FAKE, 1, None, 0, None]
+    bad = list(args); bad[8] = None
+    assert lib.bitlinear_forward(*bad) == 1
+    bad = list(args); bad[3] = 72
+    assert lib.bitlinear_forward(*bad) == 2
+    bad = list(args); bad[7] = 0
+    assert lib.bitlinear_forward(*bad) == 2
+    bad = list(args); bad[9] = 7
+    assert lib.bitlinear_forward(*bad) == 4
+    bad = list(args); bad[4] = FAKE + 4
+    assert lib.bitlinear_forward(*bad) == 3
+    bad = list(args); bad[8] = FAKE + 1     # bf16 Y needs 2-byte alignment
+    assert lib.bitlinear_forward(*bad) == 3
+    for s in range(9):
+        assert lib.bitlinear_status_string(s)
+    assert lib.bitlinear_status_string(99) == b"unknown status"
+
+
+def test_binding_raises_on_cpu_tensors():
+    import torch
+    import ternary_bitlinear_amd as tb
+    with pytest.raises(TypeError):
+        tb.bitlinear_quant_acts(torch.zeros(2, 16))

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Bit-exact: gamma, packed bytes, X~, x_scale, x_sum and the int32 accumulators.
+Within tolerance: Y (1e-5 relative for fp32 out, 1e-2 for bf16), with outputs
+of a zero accumulator exactly zero.
+"""
+import numpy as np
+import pytest
+
+from oracle import bitlinear_oracle as O
+from synth import WORKLOADS, make_acts, make_weight
+from tests.gpu_common import assert_equal, check_y, dev, f32_bits, host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_pack(tb, W):
+    Wp, g = tb.bitlinear_pack_weights(dev(W))
+    return host(Wp), host(g)
+
+
+def run_quant(tb, X):
+    Xq, s, xs = tb.bitlinear_quant_acts(dev(X))
+    return host(Xq), host(s), host(xs)
+
+
+# --------------------------------------------------------------------------- pack
+PACK_SHAPES = [(1, 16), (7, 48), (33, 80), (256, 512), (300, 1040), (129, 4096), (3, 8640)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES, ids=[f"N{n}xK{k}" for n, k in PACK_SHAPES])
+def test_pack_gaussian(gpu_lib, N, K):
+    W = make_weight(0, f"test/pack/{N}x{K}", N, K, 0.02)
+    Wp, g = run_pack(gpu_lib, W)
+    gamma = O.absmean_gamma(W)
+    assert_equal(f32_bits(g), f32_bits([gamma]), "gamma bits")
+    assert_equal(Wp, O.pack_codes(O.ternarize(W, gamma)), "packed bytes")
+
+
+def _special_weights():
+    rng = np.random.default_rng(20)
+    out = {}
+    out["zeros"] = np.zeros((5, 32), np.float32)
+    out["const"] = (np.where(rng.random((9, 64)) < 0.5, -1, 1) * np.float32(0.0123)).astype(np.float32)
+    # exponents over the whole fp32 range in one tile (exercises the exact slow path)
+    mant = rng.random((16, 256)) + 0.5
+    expo = rng.integers(-149, 100, size=(16, 256))
+    w = (np.ldexp(mant, expo) * np.where(rng.random((16, 256)) < 0.5, -1, 1)).astype(np.float32)
+    w[rng.random((16, 256)) < 0.1] = 0.0
+    out["wide-exponents"] = w
+    out["subnormal-only"] = (np.ldexp(rng.random((4, 64)), -140)).astype(np.float32)
+    from scipy.linalg import hadamard
+    out["hadamard"] = hadamard(128).astype(np.float32)
+    big = make_weight(0, "test/pack/outlier", 64, 512, 0.02)
+    big[3, 7] = 3.0e3     # one huge weight: most others fall below the tile window
+    out["one-huge"] = big
+    return out
+
+
+SPECIAL = _special_weights()
+
+
+@pytest.mark.parametrize("name", list(SPECIAL))
+def test_pack_special(gpu_lib, name):
+    W = SPECIAL[name]
+    Wp, g = run_pack(gpu_lib, W)
+    gamma = O.absmean_gamma(W)
+    assert_equal(f32_bits(g), f32_bits([gamma]), "gamma bits")
+    assert_equal(Wp, O.pack_codes(O.ternarize(W, gamma)), "packed bytes")
+
+
+def test_pack_threshold_neighbours(gpu_lib):
+    """Weights placed on and one ulp either side of the +-1/2 decision
+    boundaries of z = W / (gamma + eps), for the gamma the matrix itself has."""
+    W = make_weight(0, "test/pack/thresholds", 16, 256, 0.02)
+    probes = [(r, c) for r in range(2) for c in range(8)]
+    for _ in range(20):
+        gamma = O.absmean_gamma(W)
+        g = np.float32(gamma + O.EPS)
+        vals = []
+        for side in (0.5, -0.5):
+            t = np.float32(np.float64(g) * side)
+            vals += [t, np.nextafter(t, np.float32(np.inf)), np.nextafter(t, np.float32(-np.inf)),
+                     np.nextafter(np.nextafter(t, np.float32(np.inf)), np.float32(np.inf))]
+        for (r, c), v in zip(probes, vals + vals):
+            W[r, c] = v
+        if O.absmean_gamma(W) == gamma:
+            break
+    gamma = O.absmean_gamma(W)
+    Wt = O.ternarize(W, gamma)
+    codes = {int(Wt[r, c]) for (r, c) in probes}
+    assert codes == {-1, 0, 1}, "probes must straddle the boundaries"
+    Wp, g = run_pack(gpu_lib, W)
+    assert_equal(f32_bits(g), f32_bits([gamma]), "gamma bits")
+    assert_equal(Wp, O.pack_codes(Wt), "packed bytes")
+
+
+# --------------------------------------------------------------------------- quant
+QUANT_SHAPES = [(1, 16), (3, 48), (5, 512), (64, 4096), (2, 8640), (17, 3200), (300, 128)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES, ids=[f"M{m}xK{k}" for m, k in QUANT_SHAPES])
+def test_quant_parity(gpu_lib, M, K):
+    from fractions import Fraction
+    X = make_acts(0, f"test/quant/{M}x{K}", M, K,
+                  {"outlier_frac": Fraction(1, 200), "outlier_scale": 100.0})
+    Xq, s, xs = run_quant(gpu_lib, X)
+    oq, os_, oxs, _ = O.quantize_activations(X)
+    assert_equal(Xq, oq, "X~")
+    assert_equal(f32_bits(s), f32_bits(os_), "x_scale bits")
+    assert_equal(xs.astype(np.int64), oxs, "x_sum")
+
+
+def test_quant_edge_rows(gpu_lib):
+    K = 32
+    rows = []
+    rows.append(np.zeros(K, np.float32))                                   # zero token
+    b = np.float32(127.0) - np.float32(2.0 ** -17)                          # factor exactly 1
+    r = np.zeros(K, np.float32)
+    r[:16] = [b, 0.5, -0.5, 2.5, -2.5, np.nextafter(np.float32(0.5), np.float32(0)),
+              np.nextafter(np.float32(-0.5), np.float32(-1)), 100.5, -b, 0.0, 63.25, -63.75,
+              1.0, -1.0, 126.5, -126.5]
+    rows.append(r)
+    rows.append(np.full(K, np.float32(1e-40)))                              # subnormal inputs
+    rows.append(np.linspace(-3e30, 2e30, K).astype(np.float32))            # huge inputs
+    rows.append(-np.abs(np.random.default_rng(3).standard_normal(K)).astype(np.float32))
+    rows.append(np.full(K, np.float32(2.5e-3)))                             # absmax near 253 eps
+    X = np.stack(rows).astype(np.float32)
+    Xq, s, xs = run_quant(gpu_lib, X)
+    oq, os_, oxs, _ = O.quantize_activations(X)
+    assert_equal(Xq, oq, "X~")
+    assert_equal(f32_bits(s), f32_bits(os_), "x_scale bits")
+    assert_equal(xs.astype(np.int64), oxs, "x_sum")
+
+
+# --------------------------------------------------------------------------- forward
+FWD_SHAPES = [
+    # decode path (M <= 16)
+    (1, 1, 16), (1, 16, 64), (1, 17, 80), (2, 33, 1040), (5, 129, 512), (16, 300, 4096),
+    (7, 64, 8640), (1, 3200, 8640),
+    # GEMM path (M > 16): ragged tiles and K tails
+    (17, 16, 64), (33, 130, 144), (64, 256, 4096), (130, 300, 1040), (300, 129, 128),
+    (257, 513, 2048),
+]
+
+
+def _random_operands(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    Wt = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    return Wt, Xq
+
+
+@pytest.mark.parametrize("M,N,K", FWD_SHAPES, ids=[f"M{m}N{n}K{k}" for m, n, k in FWD_SHAPES])
+def test_forward_int32_handbuilt(gpu_lib, M, N, K):
+    """Packed tensors built by the oracle (bypassing pack_weights) and random int8
+    activations: the accumulators must be exact."""
+    Wt, Xq = _random_operands(M, N, K, seed=M * 7919 + N * 31 + K)
+    P = O.pack_codes(Wt)
+    xsum = Xq.astype(np.int64).sum(1).astype(np.int32)
+    import torch
+    acc = gpu_lib.bitlinear_forward(dev(P), dev(np.array([1.0], np.float32)), dev(Xq),
+                                    dev(np.ones(M, np.float32)), dev(xsum), N=N, K=K,
+                                    y_dtype="i32")
+    torch.cuda.synchronize()
+    assert_equal(host(acc).astype(np.int64), O.integer_matmul(Wt, Xq), "int32 accumulators")
+
+
+def test_forward_extreme_accumulators(gpu_lib):
+    """All weights +1 (or -1) and all activations +-127: |acc| = 127 K."""
+    M, N, K = 20, 48, 4096
+    Wt = np.ones((N, K), np.int8)
+    Wt[1::2] = -1
+    Xq = np.full((M, K), 127, np.int8)
+    Xq[1::2] = -127
+    xsum = Xq.astype(np.int64).sum(1).astype(np.int32)
+    for m in (M, 3):
+        acc = gpu_lib.bitlinear_forward(dev(O.pack_codes(Wt)), dev(np.array([1.0], np.float32)),
+                                        dev(Xq[:m]), dev(np.ones(m, np.float32)), dev(xsum[:m]),
+                                        N=N, K=K, y_dtype="i32")
+        assert_equal(host(acc).astype(np.int64), O.integer_matmul(Wt, Xq[:m]), "accumulators")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(1, 100, 512), (9, 77, 1040), (48, 200, 2048)])
+def test_forward_rescale(gpu_lib, M, N, K, out):
+    W = make_weight(0, f"test/fwd/{N}x{K}", N, K, 0.02)
+    X = make_acts(0, f"test/fwd/X{M}x{K}", M, K, {})
+    r = O.bitlinear(W, X)
+    Y = gpu_lib.bitlinear_forward(dev(r["packed"]), dev(np.array([r["gamma"]], np.float32)),
+                                  dev(r["Xq"]), dev(r["x_scale"]),
+                                  dev(r["x_sum"].astype(np.int32)), N=N, K=K, y_dtype=out)
+    check_y(Y, r["y"], out)
+
+
+def test_forward_deterministic_on_side_stream(gpu_lib):
+    import torch
+    M, N, K = 40, 300, 1024
+    Wt, Xq = _random_operands(M, N, K, seed=5)
+    args = (dev(O.pack_codes(Wt)), dev(np.array([0.5], np.float32)), dev(Xq),
+            dev(np.full(M, 0.25, np.float32)), dev(Xq.astype(np.int64).sum(1).astype(np.int32)))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y1 = gpu_lib.bitlinear_forward(*args, N=N, K=K, y_dtype="f32", stream=s)
+        y2 = gpu_lib.bitlinear_forward(*args, N=N, K=K, y_dtype="f32", stream=s)
+    s.synchronize()
+    assert torch.equal(y1, y2)
+
+
+# --------------------------------------------------------------------------- whole path
+def _whole_path(tb, W, X, out):
+    import torch
+    Wp, g = tb.bitlinear_pack_weights(dev(W))
+    Xq, s, xs = tb.bitlinear_quant_acts(dev(X))
+    N, K = W.shape
+    acc = tb.bitlinear_forward(Wp, g, Xq, s, xs, N=N, K=K, y_dtype="i32")
+    Y = tb.bitlinear_forward(Wp, g, Xq, s, xs, N=N, K=K, y_dtype=out)
+    torch.cuda.synchronize()
+    return dict(packed=host(Wp), gamma=host(g), Xq=host(Xq), x_scale=host(s), x_sum=host(xs),
+                acc=host(acc), Y=Y)
+
+
+def _compare_whole(got, W, X, out):
+    r = O.bitlinear(W, X)
+    assert_equal(f32_bits(got["gamma"]), f32_bits([r["gamma"]]), "gamma bits")
+    assert_equal(got["packed"], r["packed"], "packed bytes")
+    assert_equal(got["Xq"], r["Xq"], "X~")
+    assert_equal(f32_bits(got["x_scale"]), f32_bits(r["x_scale"]), "x_scale bits")
+    assert_equal(got["x_sum"].astype(np.int64), r["x_sum"], "x_sum")
+    assert_equal(got["acc"].astype(np.int64), r["acc"], "int32 accumulators")
+    check_y(got["Y"], r["y"], out)
+
+
+def test_layer_512x256_fp32(gpu_lib):
+    wl = WORKLOADS["layer-512x256"]
+    p = wl.projections[0]
+    W, X = wl.weight(p), wl.acts(p, 4)
+    _compare_whole(_whole_path(gpu_lib, W, X, "f32"), W, X, "f32")
+
+
+FULL = [(wl.name, p.name) for wl in WORKLOADS.values() if wl.name != "layer-512x256"
+        for p in wl.projections]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wname,pname", FULL, ids=[f"{w}:{p}" for w, p in FULL])
+def test_workload_full_size(gpu_lib, wname, pname):
+    """Every intermediate of the whole path at the workload's real sizes, for
+    every token count of the workload, compared in full."""
+    wl = WORKLOADS[wname]
+    p = next(q for q in wl.projections if q.name == pname)
+    W = wl.weight(p)
+    gamma = O.absmean_gamma(W)
+    Wt = O.ternarize(W, gamma)
+    import torch
+    Wp, g = gpu_lib.bitlinear_pack_weights(dev(W))
+    assert_equal(f32_bits(host(g)), f32_bits([gamma]), "gamma bits")
+    assert_equal(host(Wp), O.pack_codes(Wt), "packed bytes")
+    for M in wl.tokens:
+        X = wl.acts(p, M)
+        oq, os_, oxs, beta = O.quantize_activations(X)
+        Xq, s, xs = gpu_lib.bitlinear_quant_acts(dev(X))
+        assert_equal(host(Xq), oq, f"X~ M={M}")
+        assert_equal(f32_bits(host(s)), f32_bits(os_), f"x_scale M={M}")
+        assert_equal(host(xs).astype(np.int64), oxs, f"x_sum M={M}")
+        acc_ref = O.integer_matmul(Wt, oq)
+        acc = gpu_lib.bitlinear_forward(Wp, g, Xq, s, xs, N=p.N, K=p.K, y_dtype="i32")
+        assert_equal(host(acc).astype(np.int64), acc_ref, f"accumulators M={M}")
+        Y = gpu_lib.bitlinear_forward(Wp, g, Xq, s, xs, N=p.N, K=p.K, y_dtype=wl.out_dtype)
+        check_y(Y, O.rescale(acc_ref, gamma, beta), wl.out_dtype)
+        torch.cuda.synchronize()
