@@ -159,6 +159,34 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Bytes of workspace bitlinear_forward_f32 needs when the caller passes no
+ * quantiser output buffers: 0 when the shape runs as one fused launch, else
+ * room for X~, x_scale and x_sum.  0 if the shape is invalid. */
+size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Activation quantisation fused with the projection: fp32 X in, Y out.
+ * Computes exactly bitlinear_quant_acts followed by bitlinear_forward (same
+ * X~, same x_scale, same x_sum, same accumulators; page section 2, absmax
+ * activation quantiser and the linear transformation), as one launch for
+ * decode shapes (M <= 8 tokens whose int8 rows fit the on-chip staging;
+ * every workgroup quantises the activations it needs), else as those two
+ * launches.  This is the quantiser folded into the projection's prologue.
+ *
+ * X        [M][K] fp32, device, 16-byte aligned (read only).
+ * Y        [M][N], device, as in bitlinear_forward.
+ * X_q_out, x_scale_out, x_sum_out  optional (all three or none): receive the
+ *          quantiser outputs, as bitlinear_quant_acts would write them.
+ * workspace  needed only when the outputs are not given, of
+ *          bitlinear_forward_f32_workspace_bytes(M, N, K) bytes (16-byte
+ *          aligned); may be NULL when that is 0.
+ */
+bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gamma,
+                                       int64_t N, int64_t K, const float* X, int64_t M,
+                                       void* Y, bitlinear_dtype y_dtype,
+                                       int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static English name of a status. */
 const char* bitlinear_status_string(bitlinear_status s);
 

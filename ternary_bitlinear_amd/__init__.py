@@ -10,8 +10,10 @@ from .binding import (  # noqa: F401
     STATUS,
     BitLinearError,
     bitlinear_forward,
+    bitlinear_forward_f32,
     bitlinear_pack_weights,
     bitlinear_quant_acts,
+    forward_f32_workspace_bytes,
     forward_workspace_bytes,
     load,
     pack_workspace_bytes,

@@ -30,6 +30,9 @@ SIGNATURES = {
     "bitlinear_forward_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "bitlinear_forward": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp,
                                          ctypes.c_int, _vp, _c_size, _vp]),
+    "bitlinear_forward_f32_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "bitlinear_forward_f32": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, ctypes.c_int,
+                                             _vp, _vp, _vp, _vp, _c_size, _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -160,4 +163,38 @@ def bitlinear_forward(W_packed, gamma, X_q, x_scale, x_sum, N=None, K=None, y_dt
     _check(lib.bitlinear_forward(W_packed.data_ptr(), gamma.data_ptr(), N, K, X_q.data_ptr(),
                                  x_scale.data_ptr(), x_sum.data_ptr(), M, Y.data_ptr(),
                                  DTYPES[y_dtype], ws_ptr, ws_bytes, _stream(stream)))
+    return Y
+
+
+def forward_f32_workspace_bytes(M: int, N: int, K: int) -> int:
+    return load().bitlinear_forward_f32_workspace_bytes(M, N, K)
+
+
+def bitlinear_forward_f32(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None, X_q_out=None,
+                          x_scale_out=None, x_sum_out=None, workspace=None, stream=None):
+    """Quantise fp32 X [M][K] and project in one call -> Y [M][N]."""
+    import torch
+    lib = load()
+    _dev(W_packed, torch.uint8, "W_packed")
+    _dev(X, torch.float32, "X")
+    M, K = X.shape
+    N = W_packed.shape[0] if N is None else N
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[y_dtype]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=tdt, device=X.device)
+    _dev(Y, tdt, "Y")
+    outs = (X_q_out, x_scale_out, x_sum_out)
+    if X_q_out is not None:
+        _dev(X_q_out, torch.int8, "X_q_out")
+        _dev(x_scale_out, torch.float32, "x_scale_out")
+        _dev(x_sum_out, torch.int32, "x_sum_out")
+    need = 0 if X_q_out is not None else lib.bitlinear_forward_f32_workspace_bytes(M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ptr = [o.data_ptr() if o is not None else None for o in outs]
+    _check(lib.bitlinear_forward_f32(W_packed.data_ptr(), gamma.data_ptr(), N, K, X.data_ptr(), M,
+                                     Y.data_ptr(), DTYPES[y_dtype], ptr[0], ptr[1], ptr[2],
+                                     ws_ptr, ws_bytes, _stream(stream)))
     return Y

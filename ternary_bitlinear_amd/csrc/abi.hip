@@ -147,6 +147,44 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma, 
                   "forward launch");
 }
 
+size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K)) return 0;
+  return bl::forward_f32_workspace_bytes(M, N, K);
+}
+
+bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N,
+                                       int64_t K, const float* X, int64_t M, void* Y,
+                                       bitlinear_dtype y_dtype, int8_t* X_q_out,
+                                       float* x_scale_out, int32_t* x_sum_out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (!W_packed || !gamma || !X || !Y) return fail(BITLINEAR_ERR_NULL, "forward_f32: NULL buffer");
+  const int given = (X_q_out != nullptr) + (x_scale_out != nullptr) + (x_sum_out != nullptr);
+  if (given != 0 && given != 3)
+    return fail(BITLINEAR_ERR_NULL, "forward_f32: X_q_out, x_scale_out and x_sum_out go together");
+  if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "forward_f32: invalid shape M=%lld N=%lld K=%lld",
+                (long long)M, (long long)N, (long long)K);
+  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+    return fail(BITLINEAR_ERR_DTYPE, "forward_f32: unknown y_dtype %d", (int)y_dtype);
+  const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
+  if (!aligned(W_packed, 16) || !aligned(X, 16) || !aligned(gamma, 4) || !aligned(Y, ya) ||
+      (X_q_out && (!aligned(X_q_out, 16) || !aligned(x_scale_out, 4) || !aligned(x_sum_out, 4))))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_f32: W_packed, X and X_q_out need 16-byte "
+                "alignment, Y its element size");
+  const size_t need = given ? 0 : bl::forward_f32_workspace_bytes(M, N, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "forward_f32: workspace of %zu bytes needed, got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned(workspace, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_f32: workspace alignment");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward_f32(W_packed, gamma, N, K, X, M, Y, (int)y_dtype, X_q_out,
+                                         x_scale_out, x_sum_out, workspace,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                  "forward_f32 launch");
+}
+
 const char* bitlinear_status_string(bitlinear_status s) {
   switch (s) {
     case BITLINEAR_OK: return "ok";

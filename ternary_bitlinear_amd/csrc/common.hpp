@@ -19,6 +19,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// ---- activation quantiser ----------------------------------------------------
+// x~ = RoundClip(x * inv, -127, 127) with inv = 127 / (beta + eps) already in
+// fp32: one fp32 multiply, then floor(q + 1/2) taken exactly as
+// floor(q) + (q - floor(q) >= 1/2) (q - floor(q) is exact for |q| < 2^23).
+// Sources are built without contraction, so the multiply never fuses with the
+// subtraction.
+__device__ __forceinline__ int32_t quant1(float x, float inv) {
+  const float q = x * inv;
+  const float r = floorf(q);
+  int32_t v = (int32_t)r + ((q - r) >= 0.5f ? 1 : 0);
+  return max(-127, min(127, v));
+}
+
+// Four values -> four int8 codes packed little endian; adds them to `sum`.
+__device__ __forceinline__ uint32_t quant4(const float4& f, float inv, int32_t& sum) {
+  const int32_t a = quant1(f.x, inv), b = quant1(f.y, inv), c = quant1(f.z, inv),
+                d = quant1(f.w, inv);
+  sum += a + b + c + d;
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+__device__ __forceinline__ uint32_t absmax4(const float4& f) {
+  return max(max(abs_bits(f.x), abs_bits(f.y)), max(abs_bits(f.z), abs_bits(f.w)));
+}
+
 // ---- wave reductions (all lanes receive the result) -------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

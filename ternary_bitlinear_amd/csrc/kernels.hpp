@@ -21,4 +21,13 @@ hipError_t launch_forward(const uint8_t* W_packed, const float* gamma, int64_t N
                           const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
                           int64_t M, void* Y, int y_dtype, hipStream_t stream);
 
+// Quantisation fused with the projection (fp32 activations in).  Optional
+// X_q_out / x_scale_out / x_sum_out receive the quantiser's outputs (all or
+// none); with none, the two-launch fallback uses `workspace`.
+size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
+                              const float* X, int64_t M, void* Y, int y_dtype, int8_t* X_q_out,
+                              float* x_scale_out, int32_t* x_sum_out, void* workspace,
+                              hipStream_t stream);
+
 }  // namespace bl

@@ -96,7 +96,8 @@ def test_pack_threshold_neighbours(gpu_lib):
 
 
 # --------------------------------------------------------------------------- quant
-QUANT_SHAPES = [(1, 16), (3, 48), (5, 512), (64, 4096), (2, 8640), (17, 3200), (300, 128)]
+QUANT_SHAPES = [(1, 16), (3, 48), (5, 512), (64, 4096), (2, 8640), (17, 3200), (300, 128),
+                (2, 33280), (1, 131072), (3, 28672)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES, ids=[f"M{m}xK{k}" for m, k in QUANT_SHAPES])
@@ -138,6 +139,8 @@ FWD_SHAPES = [
     # decode path (M <= 16)
     (1, 1, 16), (1, 16, 64), (1, 17, 80), (2, 33, 1040), (5, 129, 512), (16, 300, 4096),
     (7, 64, 8640), (1, 3200, 8640),
+    # decode with 2 and 4 row blocks per workgroup (needs >= 256 workgroups), ragged N
+    (7, 8200, 80), (13, 16400, 1040), (16, 16384, 256),
     # GEMM path (M > 16): ragged tiles and K tails
     (17, 16, 64), (33, 130, 144), (64, 256, 4096), (130, 300, 1040), (300, 129, 128),
     (257, 513, 2048),
@@ -267,5 +270,52 @@ def test_workload_full_size(gpu_lib, wname, pname):
         acc = gpu_lib.bitlinear_forward(Wp, g, Xq, s, xs, N=p.N, K=p.K, y_dtype="i32")
         assert_equal(host(acc).astype(np.int64), acc_ref, f"accumulators M={M}")
         Y = gpu_lib.bitlinear_forward(Wp, g, Xq, s, xs, N=p.N, K=p.K, y_dtype=wl.out_dtype)
-        check_y(Y, O.rescale(acc_ref, gamma, beta), wl.out_dtype)
+        y_ref = O.rescale(acc_ref, gamma, beta)
+        check_y(Y, y_ref, wl.out_dtype)
+        # the fused entry point the bench times for decode shapes
+        Xd = dev(X)
+        accf = gpu_lib.bitlinear_forward_f32(Wp, g, Xd, N=p.N, y_dtype="i32")
+        assert_equal(host(accf).astype(np.int64), acc_ref, f"fused accumulators M={M}")
+        check_y(gpu_lib.bitlinear_forward_f32(Wp, g, Xd, N=p.N, y_dtype=wl.out_dtype), y_ref,
+                wl.out_dtype)
         torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- fused quant + forward
+FUSED_SHAPES = [
+    (1, 1, 16), (1, 40, 80), (2, 33, 1040), (3, 300, 4096), (5, 129, 512), (8, 64, 2048),
+    (1, 8640, 3200), (1, 3200, 8640), (1, 64, 28672), (4, 100, 8192),
+    # outside the fused kernel's reach: two launches
+    (9, 77, 1040), (16, 300, 4096), (8, 64, 8640), (40, 130, 1024), (2, 50, 40960),
+]
+
+
+@pytest.mark.parametrize("with_outputs", [True, False], ids=["outs", "noouts"])
+@pytest.mark.parametrize("M,N,K", FUSED_SHAPES, ids=[f"M{m}N{n}K{k}" for m, n, k in FUSED_SHAPES])
+def test_forward_f32_fused(gpu_lib, M, N, K, with_outputs):
+    """Quantisation fused into the projection: the same X~, scales, sums and
+    accumulators as the two separate calls, checked against the oracle."""
+    import torch
+    from fractions import Fraction
+    W = make_weight(0, f"test/fused/W{N}x{K}", N, K, 0.02)
+    X = make_acts(0, f"test/fused/X{M}x{K}", M, K,
+                  {"outlier_frac": Fraction(1, 200), "outlier_scale": 100.0})
+    r = O.bitlinear(W, X)
+    P = dev(r["packed"])
+    g = dev(np.array([r["gamma"]], np.float32))
+    Xd = dev(X)
+    outs = {}
+    if with_outputs:
+        outs = dict(X_q_out=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                    x_scale_out=torch.empty(M, dtype=torch.float32, device="cuda"),
+                    x_sum_out=torch.empty(M, dtype=torch.int32, device="cuda"))
+    acc = gpu_lib.bitlinear_forward_f32(P, g, Xd, N=N, y_dtype="i32", **outs)
+    torch.cuda.synchronize()
+    assert_equal(host(acc).astype(np.int64), r["acc"], "accumulators")
+    if with_outputs:
+        assert_equal(host(outs["X_q_out"]), r["Xq"], "X~ out")
+        assert_equal(f32_bits(host(outs["x_scale_out"])), f32_bits(r["x_scale"]), "x_scale out")
+        assert_equal(host(outs["x_sum_out"]).astype(np.int64), r["x_sum"], "x_sum out")
+    for out in ("f32", "bf16"):
+        Y = gpu_lib.bitlinear_forward_f32(P, g, Xd, N=N, y_dtype=out, **outs)
+        check_y(Y, r["y"], out)
