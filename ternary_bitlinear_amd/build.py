@@ -35,6 +35,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode})")
     if verbose and (r.stdout or r.stderr):
         sys.stderr.write(r.stdout + r.stderr)
+    # A kernel the host pass rejects silently leaves its launch stub undefined;
+    # a shared library links anyway and only fails at load time.  Refuse it.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    stubs = [l for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if nm.returncode == 0 and stubs:
+        os.remove(tmp)
+        raise RuntimeError("undefined kernel stubs in the built library:\n" + "\n".join(stubs[:10]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -76,6 +76,16 @@ __device__ __forceinline__ i32x4 mfma_i8_16x16x64(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_i32_32x32x32_i8: C[32x32] += A[32x32] * B[32x32].  Lane l supplies A
+// row (l % 32) and B column (l % 32) for k-group (l / 32), 16 bytes each,
+// paired byte for byte as in the 16x16 form.  Result: lane l, register r
+// holds C[8 * (r / 4) + 4 * (l / 32) + (r % 4)][l % 32].
+__device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
 // Four int8 codes per dword from one packed BLT2 word: dword d holds the codes
 // (W~ + 1, values 0..2) of k = 16g + 4d .. 16g + 4d + 3, i.e. the 16 codes of
 // the word in natural k order.

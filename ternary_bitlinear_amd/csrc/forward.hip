@@ -16,8 +16,8 @@
 //   k_decode (M <= 16): a software-pipelined stream over packed rows, see
 //     below; the activation operand comes straight from global memory
 //     (L2-resident) and is reused across the workgroup's row blocks.
-//   k_gemm (M > 16): 128 x 128 output tiles, K in steps of 128, activations and
-//     packed codes staged in LDS; codes are expanded in registers.
+//   k_gemm (M > 16): output tiles up to 256 x 256, K in steps of 128 through
+//     double-buffered LDS; codes are expanded in registers (see below).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,6 +36,27 @@ __device__ __forceinline__ void store_out(void* Y, int64_t idx, int32_t acc, flo
     const float y = ((float)acc * gamma) * scale;
     if constexpr (OUT == kOutF32) reinterpret_cast<float*>(Y)[idx] = y;
     else reinterpret_cast<uint16_t*>(Y)[idx] = f32_to_bf16_rne(y);
+  }
+}
+
+// Four consecutive outputs Y[idx .. idx + 3] (idx a multiple of 4, Y aligned
+// for the vector), one store.
+template <int OUT>
+__device__ __forceinline__ void store_out4(void* Y, int64_t idx, i32x4 acc, float gamma,
+                                           float scale) {
+  if constexpr (OUT == kOutI32) {
+    *reinterpret_cast<i32x4*>(reinterpret_cast<int32_t*>(Y) + idx) = acc;
+  } else {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = ((float)acc[j] * gamma) * scale;
+    if constexpr (OUT == kOutF32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + idx) = make_float4(y[0], y[1], y[2], y[3]);
+    } else {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + idx) = make_uint2(lo, hi);
+    }
   }
 }
 
@@ -96,25 +117,32 @@ __device__ __forceinline__ void decode_store(const DecodeArgs& da, int n, int g,
   if (n >= da.N) return;
   const float gamma = da.gamma[0];
   const int32_t vals[4] = {sum.x, sum.y, sum.z, sum.w};
+  // Every token's sum and scale are read before the first store: Y may alias
+  // them as far as the compiler knows, so reads placed between stores would
+  // each wait a full memory round trip.
+  int32_t sx[4];
+  float sc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = min(4 * g + r, da.M - 1);
+    if constexpr (AM == kAFuse) {
+      uint32_t bm = 0;
+      int32_t s = 0;
+      for (int w2 = 0; w2 < gw; ++w2) {
+        bm = max(bm, s_wmax[m * gw + w2]);
+        s += s_wsum[m * gw + w2];
+      }
+      sx[r] = s;
+      sc[r] = __uint_as_float(bm) / 127.0f;
+    } else {
+      sx[r] = da.xsum[m];
+      sc[r] = da.xs[m];
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * g + r;
-    if (m >= da.M) continue;
-    int32_t sx;
-    float sc;
-    if constexpr (AM == kAFuse) {
-      uint32_t bm = 0;
-      sx = 0;
-      for (int w2 = 0; w2 < gw; ++w2) {
-        bm = max(bm, s_wmax[m * gw + w2]);
-        sx += s_wsum[m * gw + w2];
-      }
-      sc = __uint_as_float(bm) / 127.0f;
-    } else {
-      sx = da.xsum[m];
-      sc = da.xs[m];
-    }
-    store_out<OUT>(da.Y, (int64_t)m * da.N + n, vals[r] - sx, gamma, sc);
+    if (m < da.M) store_out<OUT>(da.Y, (int64_t)m * da.N + n, vals[r] - sx[r], gamma, sc[r]);
   }
 }
 
@@ -432,101 +460,329 @@ hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t s
 
 // ---------------------------------------------------------------------------
 // GEMM: M > 16 tokens.
+//
+// A workgroup of 4 waves (WM x WN) computes a BM x BN output tile (tokens x
+// weight rows).  K advances in steps of 128 through a ring of three LDS
+// stages filled by direct global->LDS loads (each lane's 16 bytes land at
+// base + 16 x lane), issued two steps ahead of the matrix instructions; one
+// barrier per step.  The stages are three separate LDS arrays and the loop is
+// unrolled by three, so every access names its stage at compile time.
+//
+// Stage layouts (both read conflict-free with 16-byte reads whether the LDS
+// serves 8 or 16 lanes of such a read per cycle):
+//   activations  BM rows of 128 bytes; piece p (k = 16p .. 16p + 15 of the
+//                step) of row r sits at r * 128 + 16 * (p ^ aswz(r)),
+//                aswz(r) = (r & 7) ^ ((r >> 3) & 1);
+//   codes        two halves of BN 16-byte chunks; chunk (n, h) = packed words
+//                4h .. 4h + 3 of code row n (k = 64h .. 64h + 63 of the step)
+//                sits at h * BN * 16 + n * 16.
+//
+// The 32x32x32 matrix instruction takes 16 k per lane, k group lane / 32.
+// Slice ks (0..3) of a step gives lane group g the k of piece 4g + ks, so a
+// lane reads its column's codes for the whole step as one 16-byte chunk
+// (words 4g .. 4g + 3) and the activation fragment of piece 4g + ks.  Each
+// packed word is expanded once and reused across the wave's row blocks.
+// Codes are the instruction's first operand and activations its second, so
+// the result is the transposed tile: a lane holds one token row and, per
+// register group, four consecutive outputs of it, which the epilogue writes
+// as one vector store with that row's scale and sum loaded once.
+//
+// Full steps read activations at row-clamped addresses (rows past M only feed
+// outputs that are not stored).  A K tail (K % 128 != 0) is one more step
+// loaded through registers with exact zero fill.  Tiles are dealt so that the
+// workgroups of one XCD (workgroups go round-robin over the 8 XCDs) take a
+// contiguous run of tiles, sharing activation rows in that XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int kGemmThreads = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kSA = kBK + 16;        // LDS row stride of the activation tile (bytes)
-constexpr int kSB = kBK / 4 + 4;     // LDS row stride of the packed code tile (bytes)
+constexpr int kGBK = 128;
 
-template <bool kAligned64, int OUT>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(
-    const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int N, int K,
-    const int8_t* __restrict__ Xq, const float* __restrict__ xs,
-    const int32_t* __restrict__ xsum, int M, void* __restrict__ Y, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[kBM * kSA];
-  __shared__ __attribute__((aligned(16))) uint32_t sB[kBN * kSB / 4];
+struct GemmArgs {
+  const uint8_t* Wp;
+  const float* gamma;
+  int N, K, M;
+  const int8_t* Xq;
+  const float* xs;
+  const int32_t* xsum;
+  void* Y;
+  int tiles_m, tiles_n;
+  int vec_out;   // N % 4 == 0 and Y aligned for 4-wide stores
+};
+
+__device__ __forceinline__ int aswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int a_off(int row, int piece) { return row * 128 + 16 * (piece ^ aswz(row)); }
+template <int BN>
+__device__ __forceinline__ int b_off(int row, int word) {
+  return (word >> 2) * BN * 16 + row * 16 + 4 * (word & 3);
+}
+
+// vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+template <int NV>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((NV & 0xF) | ((NV >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup rendezvous without a memory fence.  __syncthreads() would also
+// wait for every direct-to-LDS load still in flight (its release fence covers
+// them), draining the prefetch ring; here each wave first waits only for the
+// loads of the stage about to be read (wait_vmcnt), whose LDS writes are done
+// when the counter drops.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One pipeline step: issue the direct loads of a later stage into (An, Bn)
+// and run the matrix instructions on the current stage (Ac, Bc).  The
+// __restrict__ qualifiers tell the compiler the two stages are disjoint, so it
+// need not wait for the loads in flight before reading the current stage, and
+// it schedules the fragment reads itself.
+template <int BN, int MB, int NB, int A_INS, int B_INS>
+__device__ __forceinline__ void gemm_step(const int8_t* __restrict__ Ac, const uint8_t* __restrict__ Bc,
+                                          int8_t* __restrict__ An, uint8_t* __restrict__ Bn,
+                                          bool do_issue, const int8_t* const (&asrc)[A_INS],
+                                          const uint8_t* const (&bsrc)[B_INS],
+                                          const int (&bblk)[B_INS], int k0n, int wave,
+                                          int a_row0, int b_row0, int lane_sw, int g2,
+                                          i32x16 (&acc)[MB][NB]) {
+  if (do_issue) {
+#pragma unroll
+    for (int qi = 0; qi < A_INS; ++qi)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(asrc[qi] + k0n),
+                                       static_cast<void*>(An + (qi * 4 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int qi = 0; qi < B_INS; ++qi)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bsrc[qi] + k0n / 4),
+                                       static_cast<void*>(Bn + bblk[qi] * 1024), 16, 0, 0);
+  }
+  constexpr int KS = kGBK / 32;
+  i32x4 bw[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    bw[nb] = *reinterpret_cast<const i32x4*>(Bc + g2 * BN * 16 + (b_row0 + nb * 32) * 16);
+  i32x4 af[KS][MB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      af[ks][mb] = *reinterpret_cast<const i32x4*>(Ac + (a_row0 + mb * 32) * 128 +
+                                                    16 * ((4 * g2 + ks) ^ lane_sw));
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const i32x4 bf = expand_codes((uint32_t)bw[nb][ks]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma_i8_32x32x32(bf, af[ks][mb], acc[mb][nb]);
+    }
+  }
+}
+
+template <bool kAligned64, int OUT, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
+  static_assert(WM * WN == kGemmThreads / kWave, "4 waves");
+  constexpr int MB = BM / WM / 32, NB = BN / WN / 32;   // 32x32 blocks per wave
+  static_assert(MB >= 1 && NB >= 1 && BN % 64 == 0, "tile");
+  constexpr int A_INS = BM / 8 / 4;            // 1 KB direct loads per wave per stage (8 rows each)
+  constexpr int B_BLK = BN / 32;               // 1 KB blocks of codes per stage (64 chunks each)
+  constexpr int B_INS = (B_BLK + 3) / 4;       // per wave
+  static_assert(A_INS >= 1, "tile");
+  __shared__ __attribute__((aligned(1024))) int8_t sA0[BM * 128], sA1[BM * 128], sA2[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 32], sB1[BN * 32], sB2[BN * 32];
+
+  const int N = ga.N, K = ga.K, M = ga.M;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int i = lane & 15, g = lane >> 4;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r32 = lane & 31, g2 = lane >> 5;   // row/column within a 32 block, k group
   const int kw = K / 16;
 
-  i32x4 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = i32x4{0, 0, 0, 0};
+  // Bijective XCD-aware tile order: XCD x (= b % 8) takes tiles
+  // [x q + min(x, r), ...) where T = 8 q + r.
+  const int T = ga.tiles_m * ga.tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, q8 = T >> 3, r8 = T & 7;
+  const int t = xcd * q8 + min(xcd, r8) + (b >> 3);
+  const int tm = t / ga.tiles_n, tn = t % ga.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
 
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    // activations: 128 rows x 128 bytes, 16-byte pieces
+  // Per-lane source addresses of the direct loads (k offset added per step).
+  // Activation block blk holds rows 8 blk .. 8 blk + 7; lane l fills slot
+  // l & 7 of row 8 blk + (l >> 3), i.e. piece (l & 7) ^ aswz(row).
+  const int8_t* asrc[A_INS];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int chunk = tid + kGemmThreads * q;
-      const int r = chunk >> 3, c16 = chunk & 7;
-      const int m = m0 + r, k = k0 + 16 * c16;
-      i32x4 v = {0, 0, 0, 0};
-      if (m < M && k < K) v = *reinterpret_cast<const i32x4*>(Xq + (int64_t)m * K + k);
-      *reinterpret_cast<i32x4*>(sA + r * kSA + 16 * c16) = v;
+  for (int qi = 0; qi < A_INS; ++qi) {
+    const int blk = qi * 4 + wave;
+    const int r = blk * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ aswz(r);
+    asrc[qi] = ga.Xq + (int64_t)min(m0 + r, M - 1) * K + 16 * piece;
+  }
+  // Code block bb holds half h = bb / (BN / 64) of rows 64 (bb % (BN / 64))
+  // + lane.  Every wave issues B_INS code loads per stage, so all waves have
+  // the same count in flight; a wave past the last block repeats it (same
+  // bytes to the same place).
+  const uint8_t* bsrc[B_INS];
+  int bblk[B_INS];
+#pragma unroll
+  for (int qi = 0; qi < B_INS; ++qi) {
+    bblk[qi] = min(qi * 4 + wave, B_BLK - 1);
+    const int h = bblk[qi] / (BN / 64);
+    const int r = (bblk[qi] % (BN / 64)) * 64 + lane;
+    bsrc[qi] = ga.Wp + (int64_t)min(n0 + r, N - 1) * (K / 4) + 16 * h;
+  }
+  auto issue = [&](int kt, int8_t* A, uint8_t* B) {
+    const int k0 = kt * kGBK;
+#pragma unroll
+    for (int qi = 0; qi < A_INS; ++qi)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(asrc[qi] + k0),
+                                       static_cast<void*>(A + (qi * 4 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int qi = 0; qi < B_INS; ++qi)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bsrc[qi] + k0 / 4),
+                                       static_cast<void*>(B + bblk[qi] * 1024), 16, 0, 0);
+  };
+
+  i32x16 acc[MB][NB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][c][e] = 0;
+
+  // This lane's token rows in the epilogue; their sums and scales are read
+  // now so the loads are long done by then.
+  int32_t sxv[MB];
+  float scv[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = min(m0 + wm * MB * 32 + mb * 32 + r32, M - 1);
+    sxv[mb] = ga.xsum[m];
+    scv[mb] = ga.xs[m];
+  }
+
+  // Fragment rows of this lane; aswz of an activation row depends only on
+  // r32 (row blocks are 32 apart).
+  const int a_row0 = wm * MB * 32 + r32;
+  const int b_row0 = wn * NB * 32 + r32;
+  const int lane_sw = aswz(r32);
+
+  // Every step issues exactly NLD loads (the last two steps re-load the last
+  // stage into buffers nobody reads again), so before step kt the only loads
+  // younger than stage kt's are stage kt + 1's and one unconditional
+  // vmcnt(NLD) wait suffices.  Uniform counts also let the compiler see that
+  // the wait retires the stage being read, so it adds no drain of its own.
+  constexpr int NLD = A_INS + B_INS;
+  const int nkf = K / kGBK;                 // full steps
+  if (nkf > 0) {
+    issue(0, sA0, sB0);
+    issue(min(1, nkf - 1), sA1, sB1);
+  }
+  auto step = [&](int kt, int8_t* Ac, uint8_t* Bc, int8_t* An, uint8_t* Bn) {
+    wait_vmcnt<NLD>();
+    // Also orders this wave's reads of stage kt - 1 (the buffer refilled
+    // below) before the other waves' refills: every wave has finished
+    // step kt - 1 when it reaches this barrier.
+    stage_barrier();
+    gemm_step<BN, MB, NB, A_INS, B_INS>(Ac, Bc, An, Bn, true, asrc, bsrc, bblk,
+                                        min(kt + 2, nkf - 1) * kGBK, wave, a_row0, b_row0,
+                                        lane_sw, g2, acc);
+  };
+  for (int kt = 0; kt < nkf; kt += 3) {
+    step(kt, sA0, sB0, sA2, sB2);
+    // Nested, so no path reaches the third step without the second's loads.
+    if (kt + 1 < nkf) {
+      step(kt + 1, sA1, sB1, sA0, sB0);
+      if (kt + 2 < nkf) step(kt + 2, sA2, sB2, sA1, sB1);
     }
-    // codes: 128 rows x 8 words
-    {
-      const int r = tid >> 1, h = tid & 1;
-      const int n = n0 + r;
-      const int wi0 = k0 / 16 + 4 * h;
-      uint32_t w[4] = {0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u};
-      if (n < N) {
-        const uint32_t* row = reinterpret_cast<const uint32_t*>(Wp + (int64_t)n * (K / 4));
-        if (kAligned64 && wi0 + 4 <= kw) {
-          const uint4 v = *reinterpret_cast<const uint4*>(row + wi0);
-          w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  // No direct load may still be writing LDS when the tail refills a stage or
+  // the workgroup ends.
+  wait_vmcnt<0>();
+  if (K % kGBK) {
+    // Tail step through registers, exact zero fill, into the stage no load
+    // targets any more.
+    int8_t* A = (nkf % 3 == 0) ? sA0 : (nkf % 3 == 1 ? sA1 : sA2);
+    uint8_t* B = (nkf % 3 == 0) ? sB0 : (nkf % 3 == 1 ? sB1 : sB2);
+    const int k0 = nkf * kGBK;
+    __syncthreads();
+    for (int qd = tid; qd < BM * 8; qd += kGemmThreads) {
+      const int r = qd >> 3, piece = qd & 7;
+      const int m = m0 + r, k = k0 + 16 * piece;
+      i32x4 v = {0, 0, 0, 0};
+      if (m < M && k < K) v = *reinterpret_cast<const i32x4*>(ga.Xq + (int64_t)m * K + k);
+      *reinterpret_cast<i32x4*>(A + a_off(r, piece)) = v;
+    }
+    for (int qd = tid; qd < BN * 8; qd += kGemmThreads) {
+      const int r = qd >> 3, word = qd & 7;
+      const int n = min(n0 + r, N - 1);
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(ga.Wp + (int64_t)n * (K / 4));
+      *reinterpret_cast<uint32_t*>(B + b_off<BN>(r, word)) = load_word(row, k0 / 16 + word, kw);
+    }
+    __syncthreads();
+    gemm_step<BN, MB, NB, A_INS, B_INS>(A, B, nullptr, nullptr, false, asrc, bsrc, bblk, 0, wave,
+                                        a_row0, b_row0, lane_sw, g2, acc);
+  }
+
+  // Epilogue: lane (r32, g2), register 4 i + j of block (mb, nb) holds the
+  // output of token m0 + (row block) + r32 and weight row
+  // n0 + (column block) + 8 i + 4 g2 + j.
+  const float gamma = ga.gamma[0];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + wm * MB * 32 + mb * 32 + r32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + wn * NB * 32 + nb * 32 + 8 * i + 4 * g2;
+        const int64_t idx = (int64_t)m * N + n;
+        i32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][4 * i + j] - sxv[mb];
+        if (ga.vec_out) {
+          if (n < N) store_out4<OUT>(ga.Y, idx, v, gamma, scv[mb]);
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) w[t] = load_word(row, wi0 + t, kw);
+          for (int j = 0; j < 4; ++j)
+            if (n + j < N) store_out<OUT>(ga.Y, idx + j, v[j], gamma, scv[mb]);
         }
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sB[(r * kSB) / 4 + 4 * h + t] = w[t];
     }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      i32x4 af[4];
-      uint32_t bw[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const i32x4*>(sA + (wm * 64 + mb * 16 + i) * kSA + ks * 64 +
-                                                  g * 16);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) bw[nb] = sB[((wn * 64 + nb * 16 + i) * kSB) / 4 + ks * 4 + g];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const i32x4 bf = expand_codes(bw[nb]);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma_i8_16x16x64(af[mb], bf, acc[mb][nb]);
-      }
-    }
-    __syncthreads();
   }
+}
 
-  const float gamma = gamma_p[0];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 64 + mb * 16 + 4 * g + r;
-      if (m >= M) continue;
-      const int32_t sx = xsum[m];
-      const float sc = xs[m];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = n0 + wn * 64 + nb * 16 + i;
-        if (n < N) store_out<OUT>(Y, (int64_t)m * N + n, acc[mb][nb][r] - sx, gamma, sc);
-      }
-    }
-  }
+struct GemmCfg {
+  int bm, bn;
+};
+
+template <bool A64, int OUT, int BM, int BN, int WM, int WN>
+hipError_t launch_gemm_t(GemmArgs ga, hipStream_t stream) {
+  ga.tiles_m = (ga.M + BM - 1) / BM;
+  ga.tiles_n = (ga.N + BN - 1) / BN;
+  const int tiles = ga.tiles_m * ga.tiles_n;
+  k_gemm<A64, OUT, BM, BN, WM, WN><<<dim3(tiles), dim3(kGemmThreads), 0, stream>>>(ga);
+  return hipGetLastError();
+}
+
+// 64 x 64 tiles up to 128 tokens (more workgroups to fill the chip), else
+// 128 x 128.
+inline GemmCfg gemm_cfg(int M, int N, int K) {
+  (void)N;
+  (void)K;
+  if (M <= 128) return {64, 64};
+  return {128, 128};
+}
+
+template <bool A64, int OUT>
+hipError_t launch_gemm(const GemmCfg& c, const GemmArgs& ga, hipStream_t stream) {
+  if (c.bm == 128 && c.bn == 128) return launch_gemm_t<A64, OUT, 128, 128, 2, 2>(ga, stream);
+  if (c.bm == 64 && c.bn == 64) return launch_gemm_t<A64, OUT, 64, 64, 2, 2>(ga, stream);
+  return hipErrorInvalidValue;
 }
 
 template <bool A64, int OUT>
@@ -535,13 +791,11 @@ hipError_t dispatch(const uint8_t* Wp, const float* gamma, int N, int K, const i
   if (M <= 16) {
     DecodeArgs da{Wp, gamma, N, K, M, Xq, xs, xsum, nullptr, nullptr, nullptr, nullptr, Y};
     return launch_decode<A64, OUT>(decode_cfg(M, N, K, false), da, stream);
-  } else {
-    const int tiles_n = (N + kBN - 1) / kBN;
-    const int64_t tiles = (int64_t)tiles_n * ((M + kBM - 1) / kBM);
-    k_gemm<A64, OUT><<<dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream>>>(
-        Wp, gamma, N, K, Xq, xs, xsum, M, Y, tiles_n);
   }
-  return hipGetLastError();
+  const uintptr_t vec_bytes = OUT == kOutBF16 ? 8 : 16;
+  const int vec_out = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % vec_bytes == 0);
+  GemmArgs ga{Wp, gamma, N, K, M, Xq, xs, xsum, Y, 0, 0, vec_out};
+  return launch_gemm<A64, OUT>(gemm_cfg(M, N, K), ga, stream);
 }
 
 template <int OUT>

@@ -196,6 +196,31 @@ def test_forward_rescale(gpu_lib, M, N, K, out):
     check_y(Y, r["y"], out)
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("M,N,K", [(4, 256, 1024), (96, 256, 1024), (300, 260, 512)])
+def test_forward_unaligned_output(gpu_lib, M, N, K, out):
+    """Y one element past an aligned address (no vector stores possible): the same
+    bytes as an aligned Y, and the oracle's values."""
+    import torch
+    W = make_weight(0, f"test/fwdu/{N}x{K}", N, K, 0.02)
+    X = make_acts(0, f"test/fwdu/X{M}x{K}", M, K, {})
+    r = O.bitlinear(W, X)
+    args = (dev(r["packed"]), dev(np.array([r["gamma"]], np.float32)), dev(r["Xq"]),
+            dev(r["x_scale"]), dev(r["x_sum"].astype(np.int32)))
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[out]
+    buf = torch.zeros(M * N + 1, dtype=tdt, device="cuda")
+    Yu = buf[1:].view(M, N)
+    gpu_lib.bitlinear_forward(*args, N=N, K=K, y_dtype=out, Y=Yu)
+    Ya = gpu_lib.bitlinear_forward(*args, N=N, K=K, y_dtype=out)
+    torch.cuda.synchronize()
+    assert torch.equal(Yu, Ya)
+    assert buf[0].item() == 0
+    if out == "i32":
+        assert_equal(host(Ya).astype(np.int64), r["acc"], "int32 accumulators")
+    else:
+        check_y(Ya, r["y"], out)
+
+
 def test_forward_deterministic_on_side_stream(gpu_lib):
     import torch
     M, N, K = 40, 300, 1024
