@@ -49,6 +49,12 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="M; default: the workload's first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run one plain copy of known size, then bitlinear_forward once per "
+                         "projection and weight copy, and exit (for rocprofv3 --pmc runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn the FETCH_SIZE and WRITE_SIZE counter runs of "
+                         "--traffic-probe into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -75,6 +81,9 @@ class Timer:
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode)", file=sys.stderr)
@@ -121,6 +130,10 @@ def main():
         need = tb.forward_f32_workspace_bytes(M, q["p"].N, q["p"].K)
         q["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         q["fused"] = need == 0
+
+    if args.traffic_probe:
+        traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl)
+        return
 
     def step(r):
         # quantise + project; one launch when the shape fuses, else two
@@ -169,37 +182,14 @@ def main():
         value, unit = wbytes_step / (elapsed / args.steps) / 1e9, "GB/s"
 
     # ---------------- the dominant kernel: the projection (bitlinear_forward on
-    # pre-quantised activations) on the largest projection of the workload
+    # pre-quantised activations) on every projection of the workload, back to
+    # back over the rotated weight copies
+    with torch.cuda.stream(stream):
+        for q in projs:
+            tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
+    roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream)
     dom = max(projs, key=lambda q: q["p"].N * q["p"].K)
     P = dom["p"]
-    reps = max(1, 2000 // copies) if not prefill else max(1, 200 // copies)
-    with torch.cuda.stream(stream):
-        tb.bitlinear_quant_acts(dom["X"], dom["Xq"], dom["s"], dom["xs"], stream=stream)
-
-    def fwd_q(r):
-        tb.bitlinear_forward(dom["Wc"][r % copies], dom["g"], dom["Xq"], dom["s"], dom["xs"],
-                             N=P.N, K=P.K, y_dtype=out, Y=dom["Y"], stream=stream)
-    g_fq = graph_of([lambda r=r: fwd_q(r) for r in range(copies)])
-    g_fq.replay()
-    t_fq = timer(g_fq.replay, reps) / (reps * copies)
-    # algorithmic bytes of one launch: packed W, X~, x_scale, x_sum, Y, gamma
-    alg_bytes = P.N * P.K // 4 + M * P.K + 8 * M + OUT_BYTES[out] * M * P.N + 4
-    kname = "k_decode" if M <= 16 else "k_gemm"
-    if prefill:
-        achieved = 2 * M * P.N * P.K / t_fq / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    else:
-        achieved = alg_bytes / t_fq / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": None, "kernel": kname, "shape": f"M{M} {P.K}->{P.N}",
-                 "us_per_launch": round(t_fq * 1e6, 3), "algorithmic_bytes": alg_bytes,
-                 "timing": "HIP events around a graph of back-to-back launches over the "
-                           "rotated weight copies, on the launch stream"})
-    traffic = load_traffic(kname, P, M)
-    if traffic is not None:
-        roof["traffic"] = traffic
 
     # quantise + project as the step runs it (one launch when fused)
     def fwd(r):
@@ -207,6 +197,7 @@ def main():
                                  Y=dom["Y"], workspace=dom["ws"], stream=stream)
     g_fwd = graph_of([lambda r=r: fwd(r) for r in range(copies)])
     g_fwd.replay()
+    reps = max(1, (2000 if not prefill else 200) // copies)
     t_fwd = timer(g_fwd.replay, reps) / (reps * copies)
 
     # ---------------- every step of the path, timed on its own
@@ -235,7 +226,7 @@ def main():
         ("TOP/s" if prefill else "GB/s"): roof["achieved"],
         "epilogue": f"gamma*beta rescale fused, {out} out"}
     f32_bytes = P.N * P.K // 4 + 4 * M * P.K + OUT_BYTES[out] * M * P.N + 4
-    rows["forward_f32"] = {"shape": roof["shape"], "us": round(t_fwd * 1e6, 3),
+    rows["forward_f32"] = {"shape": f"M{M} {P.K}->{P.N}", "us": round(t_fwd * 1e6, 3),
                            "fused": dom["fused"],
                            ("TOP/s" if prefill else "GB/s"): round(
                                (2 * M * P.N * P.K / t_fwd / 1e12) if prefill
@@ -260,20 +251,165 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def load_traffic(kernel, P, M):
-    """HBM bytes per launch from committed rocprofv3 counter summaries
-    (profiles/traffic.json), when they were taken on the current kernel source."""
+def alg_bytes(P, M, out):
+    """Algorithmic bytes of one projection launch: packed W, X~, x_scale and
+    x_sum, Y, gamma."""
+    return P.N * P.K // 4 + M * P.K + 8 * M + OUT_BYTES[out] * M * P.N + 4
+
+
+def kernel_family(M):
+    return "k_decode" if M <= 16 else "k_gemm"
+
+
+def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream):
+    """Average launch of bitlinear_forward over the workload's projections,
+    timed with HIP events on the launch stream around a graph of back-to-back
+    launches over the rotated weight copies."""
+    def fwd_all(r):
+        for q in projs:
+            tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
+                                 N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
+    g = graph_of([lambda r=r: fwd_all(r) for r in range(copies)])
+    g.replay()
+    launches_per_replay = copies * len(projs)
+    reps = max(1, (4000 if not prefill else 200) // launches_per_replay)
+    t_all = timer(g.replay, reps)
+    n_launch = reps * launches_per_replay
+    t_launch = t_all / n_launch
+    bytes_launch = sum(alg_bytes(q["p"], M, out) for q in projs) / len(projs)
+    ops_launch = sum(2 * M * q["p"].N * q["p"].K for q in projs) / len(projs)
+    if prefill:
+        achieved = ops_launch / t_launch / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    else:
+        achieved = bytes_launch / t_launch / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    shapes = ", ".join(f"{q['p'].K}->{q['p'].N}" for q in projs)
+    roof.update({
+        "traffic": load_traffic(kernel_family(M), projs, M, out, bytes_launch),
+        "kernel": kernel_family(M), "shape": f"M{M} {shapes}",
+        "us_per_launch": round(t_launch * 1e6, 3), "launches_timed": n_launch,
+        "algorithmic_bytes_per_launch": int(bytes_launch),
+        "ops_per_launch": int(ops_launch),
+        "timing": "HIP events on the launch stream around a graph of back-to-back "
+                  "bitlinear_forward launches (every projection, rotated weight copies)"})
+    return roof, t_launch
+
+CAL_BYTES = 256 << 20        # the calibration copy reads and writes this many bytes
+
+
+def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl):
+    """One elementwise copy of CAL_BYTES (torch.neg on int32: reads and writes
+    CAL_BYTES), then bitlinear_forward once per projection and weight copy."""
+    src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    with torch.cuda.stream(stream):
+        for q in projs:
+            tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
+        for r in range(copies):
+            for q in projs:
+                tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
+                                     N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": traffic_key(kernel_family(M), [q["p"] for q in projs], M, out),
+                      "workload": wl.name, "calibration_bytes": CAL_BYTES,
+                      "launches": copies * len(projs)}), flush=True)
+
+
+def _counters(d, name):
+    """{dispatch id: (kernel name, value)} of one counter from a rocprofv3 csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    res = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != name:
+                    continue
+                k = (fn, r["Dispatch_Id"])
+                kn, v = res.get(k, (r["Kernel_Name"], 0.0))
+                res[k] = (kn, v + float(r["Counter_Value"]))
+    return res
+
+
+def traffic_from(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the probe's launches, each
+    scaled by known bytes / counter for the calibration copy, into
+    profiles/traffic.json and a text summary beside it."""
+    from synth import WORKLOADS
+    wl = WORKLOADS[args.workload]
+    M = args.tokens or wl.tokens[0]
+    fam = kernel_family(M)
+    shapes = list(wl.projections)
+    key = traffic_key(fam, shapes, M, wl.out_dtype)
+    out = {}
+    for what, d, cname in (("fetch", args.traffic_from[0], "FETCH_SIZE"),
+                           ("write", args.traffic_from[1], "WRITE_SIZE")):
+        c = _counters(d, cname)
+        cal = [v for kn, v in c.values() if "neg" in kn.lower()]
+        ker = [v for kn, v in c.values() if fam in kn]
+        if len(cal) != 1 or not ker:
+            raise SystemExit(f"{d}: expected one calibration copy and >= 1 {fam} dispatch, "
+                             f"found {len(cal)} and {len(ker)}")
+        factor = CAL_BYTES / (cal[0] * 1024.0)
+        kib = sum(ker) / len(ker)
+        out[what] = {"counter": cname, "calibration_kib": cal[0], "factor": round(factor, 5),
+                     "kernel_kib_per_dispatch": round(kib, 2), "dispatches": len(ker),
+                     "bytes_per_launch": kib * 1024.0 * factor}
+    alg = sum(alg_bytes(P, M, wl.out_dtype) for P in shapes) / len(shapes)
+    total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    ent = {"bytes_per_launch": int(total), "algorithmic_bytes_per_launch": int(alg),
+           "ratio_to_algorithmic": round(total / alg, 4),
+           "fetch": out["fetch"], "write": out["write"],
+           "source_sha256_16": forward_source_digest(),
+           "commands": [f"rocprofv3 --pmc {c} -d <dir> -o pmc --output-format csv -- "
+                        f"python3 bench.py --traffic-probe --workload {wl.name} --tokens {M}"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {"entries": {}}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data.setdefault("entries", {})[key] = ent
+    data["note"] = ("HBM bytes per launch of bitlinear_forward's kernel: rocprofv3 FETCH_SIZE "
+                    "and WRITE_SIZE (KiB per dispatch), each scaled by CAL_BYTES / the same "
+                    "counter on one torch.neg copy of CAL_BYTES int32 bytes in the same run.")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({key: ent}))
+
+
+def traffic_key(kernel, shapes, M, out):
+    """shapes: the workload's projections (objects with K and N)."""
+    return f"{kernel} M{M} " + ",".join(f"{P.K}->{P.N}" for P in shapes) + f" {out}"
+
+
+def forward_source_digest():
+    import hashlib
+    src = os.path.join(ROOT, "ternary_bitlinear_amd", "csrc", "forward.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel, projs, M, out, bytes_launch):
+    """HBM bytes per launch (read + written) from profiles/traffic.json, when the
+    counters there were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    import hashlib
     with open(path) as f:
         data = json.load(f)
-    src = os.path.join(ROOT, "ternary_bitlinear_amd", "csrc", "forward.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    key = f"{kernel} M{M} {P.K}->{P.N}"
-    ent = data.get(key)
-    if not ent or ent.get("source_sha256_16") != digest:
+    ent = data.get("entries", {}).get(traffic_key(kernel, [q["p"] for q in projs], M, out))
+    if not ent or ent.get("source_sha256_16") != forward_source_digest():
         return None
     return ent.get("bytes_per_launch")
 
