@@ -335,33 +335,27 @@ def test_rescale_matches_bruteforce_float_product():
 
 # ---------------------------------------------------------------- worked example
 def test_worked_example_end_to_end():
-    """Hand-derived example (no page prints one); every value below was worked
-    out by hand from the formulas:
-
-    |W| sums: row 0 = 9.625, row 1 = 16 * 0.5 = 8  ->  gamma = 17.625/32 = 141/256.
-    gamma + eps = 0.55079125 -> fp32 0.55079126; W / that: |1| -> 1.82, |.5| -> 0.91,
-    |.25| -> 0.45, |.125| -> 0.23, |2| -> 3.6, so W~ row 0 below and row 1 = (+1, -1)*8.
-    absmax(X) = 4; 127 / fp32(4 + 1e-5) = 31.74992; q = X * 31.74992 rounded half up.
-    acc row 0 = 32 + 63 - 127 - 32 - 63 + 24 - 48 = -151;
-    acc row 1 = (sum even x~ = -31) - (sum odd x~ = 238) = -269.
-    """
-    W = np.array([[1, -1, .25, -.25, .5, -.5, 0, 0, 2, -2, .125, 0, 1, 0, -1, 0],
-                  [.5, -.5] * 8], dtype=np.float32)
-    X = np.array([[1, -2, .5, 3, -4, 0, .25, 1, -1, 2, 0, 0, .75, -.5, 1.5, 4]],
-                 dtype=np.float32)
+    """Hand-derived example (tests/golden/worked_example.json, with its citation
+    and derivation; no page prints one)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+    W = np.array(g["W"], dtype=np.float32)
+    X = np.array(g["X"], dtype=np.float32)
     r = O.bitlinear(W, X)
-    assert r["gamma"] == np.float32(141 / 256)
-    assert r["Wt"].tolist() == [[1, -1, 0, 0, 1, -1, 0, 0, 1, -1, 0, 0, 1, 0, -1, 0],
-                                [1, -1] * 8]
-    assert r["packed"].tobytes().hex() == "aa401555aa00aa00"
-    assert r["Xq"][0].tolist() == [32, -63, 16, 95, -127, 0, 8, 32, -32, 63, 0, 0,
-                                   24, -16, 48, 127]
-    assert r["x_sum"][0] == 207
-    assert r["beta"][0] == 4.0 and r["x_scale"][0] == np.float32(4.0) / np.float32(127)
-    assert r["acc"][0].tolist() == [-151, -269]
-    assert abs(r["y"][0, 0] - (-151 * 141 / 256 * 4 / 127)) < 1e-12
-    assert abs(r["y"][0, 0] - (-2.6194636)) < 1e-6
-    assert abs(r["y"][0, 1] - (-4.6664616)) < 1e-6
+    num, den = g["gamma_num_den"]
+    assert r["gamma"] == np.float32(num / den)
+    assert r["Wt"].tolist() == g["W_ternary"]
+    assert r["packed"].tobytes().hex() == g["packed_hex"]
+    assert r["Xq"].tolist() == g["X_q"]
+    assert r["x_sum"].tolist() == g["x_sum"]
+    assert r["beta"].tolist() == g["beta"]
+    assert r["x_scale"][0] == np.float32(g["beta"][0]) / np.float32(127)
+    assert r["acc"].tolist() == g["acc"]
+    acc0 = g["acc"][0]
+    assert abs(r["y"][0, 0] - (acc0[0] * num / den * g["beta"][0] / 127)) < 1e-12
+    for n in range(2):
+        assert abs(r["y"][0, n] - g["y_approx"][0][n]) < 1e-6
     # codes route: sum c x~ - sum x~ with c = W~ + 1
     c = r["Wt"].astype(int) + 1
-    assert (c @ r["Xq"][0].astype(int) - 207).tolist() == [-151, -269]
+    assert (c @ r["Xq"][0].astype(int) - g["x_sum"][0]).tolist() == acc0
