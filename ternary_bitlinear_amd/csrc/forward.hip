@@ -109,40 +109,55 @@ struct DecodeArgs {
   void* Y;
 };
 
-// Epilogue of one 16-row block: lane (j, g) holds C[4g + r][j] in vals.
-template <int OUT, int AM>
-__device__ __forceinline__ void decode_store(const DecodeArgs& da, int n, int g, const i32x4& sum,
-                                             const uint32_t* s_wmax, const int32_t* s_wsum,
-                                             int gw) {
-  if (n >= da.N) return;
-  const float gamma = da.gamma[0];
-  const int32_t vals[4] = {sum.x, sum.y, sum.z, sum.w};
-  // Every token's sum and scale are read before the first store: Y may alias
-  // them as far as the compiler knows, so reads placed between stores would
-  // each wait a full memory round trip.
+// Per-token epilogue inputs of lane group g (tokens 4g .. 4g + 3), read when
+// the kernel starts so that no memory round trip follows the reduction.
+struct DecodeEpi {
+  float gamma;
   int32_t sx[4];
   float sc[4];
+};
+
+__device__ __forceinline__ DecodeEpi decode_epi_load(const DecodeArgs& da, int g) {
+  DecodeEpi e;
+  e.gamma = da.gamma[0];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = min(4 * g + r, da.M - 1);
-    if constexpr (AM == kAFuse) {
-      uint32_t bm = 0;
-      int32_t s = 0;
-      for (int w2 = 0; w2 < gw; ++w2) {
-        bm = max(bm, s_wmax[m * gw + w2]);
-        s += s_wsum[m * gw + w2];
-      }
-      sx[r] = s;
-      sc[r] = __uint_as_float(bm) / 127.0f;
-    } else {
-      sx[r] = da.xsum[m];
-      sc[r] = da.xs[m];
-    }
+    e.sx[r] = da.xsum[m];
+    e.sc[r] = da.xs[m];
   }
+  return e;
+}
+
+// Fused mode: the token sums and scales come from the prologue's LDS
+// partials (gw waves per token).
+__device__ __forceinline__ void decode_epi_fused(DecodeEpi& e, int g, int M,
+                                                 const uint32_t* s_wmax, const int32_t* s_wsum,
+                                                 int gw) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = min(4 * g + r, M - 1);
+    uint32_t bm = 0;
+    int32_t sum = 0;
+    for (int w2 = 0; w2 < gw; ++w2) {
+      bm = max(bm, s_wmax[m * gw + w2]);
+      sum += s_wsum[m * gw + w2];
+    }
+    e.sx[r] = sum;
+    e.sc[r] = __uint_as_float(bm) / 127.0f;
+  }
+}
+
+// Epilogue of one 16-row block: lane (j, g) holds C[4g + r][j] in sum.
+template <int OUT>
+__device__ __forceinline__ void decode_store(const DecodeArgs& da, int n, int g, const i32x4& sum,
+                                             const DecodeEpi& e) {
+  if (n >= da.N) return;
+  const int32_t vals[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * g + r;
-    if (m < da.M) store_out<OUT>(da.Y, (int64_t)m * da.N + n, vals[r] - sx[r], gamma, sc[r]);
+    if (m < da.M) store_out<OUT>(da.Y, (int64_t)m * da.N + n, vals[r] - e.sx[r], e.gamma, e.sc[r]);
   }
 }
 
@@ -181,6 +196,10 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_lds(DecodeArgs da) {
   int mp = 1;
   while (mp < M) mp <<= 1;
   const int gw = NW / mp;                    // fused: waves per token (host ensures M <= NW)
+
+  DecodeEpi epi;
+  if constexpr (AM == kAFuse) epi.gamma = da.gamma[0];
+  else epi = decode_epi_load(da, g);
 
   // Fused prologue, part 1: the fp32 activations are requested before the
   // weights so that they do not queue behind the weight stream.
@@ -291,7 +310,8 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_lds(DecodeArgs da) {
     const i32x4 o = red[w2 * kWave + lane];
     sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
   }
-  decode_store<OUT, AM>(da, n0 + j, g, sum, s_wmax, s_wsum, gw);
+  if constexpr (AM == kAFuse) decode_epi_fused(epi, g, M, s_wmax, s_wsum, gw);
+  decode_store<OUT>(da, n0 + j, g, sum, epi);
 }
 
 template <bool kAligned64, int OUT, int RB, int NW, int P>
@@ -315,6 +335,7 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_reg(DecodeArgs da) {
         da.Wp + (int64_t)min(16 * (rb0 + rb) + j, N - 1) * (K / 4));
   const bool tok_ok = j < M;
   const int8_t* xrow = da.Xq + (int64_t)min(j, M - 1) * K;
+  const DecodeEpi epi = decode_epi_load(da, g);
 
   uint32_t wb[P][RB][4];
   i32x4 ab[P][4];
@@ -372,7 +393,7 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_reg(DecodeArgs da) {
     const i32x4 o = red[(w2 * RB + rb) * kWave + lane];
     sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
   }
-  decode_store<OUT, kAReg>(da, 16 * (rb0 + rb) + j, g, sum, nullptr, nullptr, 0);
+  decode_store<OUT>(da, 16 * (rb0 + rb) + j, g, sum, epi);
 }
 
 // Launch geometry of the decode kernels for one shape.
@@ -421,10 +442,10 @@ inline DecodeCfg decode_cfg(int M, int N, int K, bool fused) {
   return c;
 }
 
-template <bool A64, int OUT, int NW, int AM>
+template <bool A64, int OUT, int NW, int P, int AM>
 hipError_t launch_decode_lds_t(const DecodeCfg& c, const DecodeArgs& da, hipStream_t stream) {
   const size_t lds = decode_lds_bytes(NW, da.M, da.K);
-  auto kern = k_decode_lds<A64, OUT, NW, 2, AM>;
+  auto kern = k_decode_lds<A64, OUT, NW, P, AM>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -443,11 +464,11 @@ hipError_t launch_decode_reg_t(const DecodeCfg& c, const DecodeArgs& da, hipStre
 template <bool A64, int OUT>
 hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t stream) {
   if (c.am == kALds || c.am == kAFuse) {
-#define BL_DL(NW)                                                                          \
-  if (c.nw == NW)                                                                          \
-    return c.am == kALds ? launch_decode_lds_t<A64, OUT, NW, kALds>(c, da, stream)         \
-                         : launch_decode_lds_t<A64, OUT, NW, kAFuse>(c, da, stream);
-    BL_DL(8) BL_DL(4) BL_DL(2) BL_DL(1)
+#define BL_DL(NW, P)                                                                       \
+  if (c.nw == NW && c.p == P)                                                              \
+    return c.am == kALds ? launch_decode_lds_t<A64, OUT, NW, P, kALds>(c, da, stream)      \
+                         : launch_decode_lds_t<A64, OUT, NW, P, kAFuse>(c, da, stream);
+    BL_DL(8, 2) BL_DL(4, 2) BL_DL(2, 2) BL_DL(1, 2)
 #undef BL_DL
   } else if (c.am == kAReg) {
 #define BL_DR(RB, NW, P) \
@@ -505,7 +526,8 @@ struct GemmArgs {
   const int32_t* xsum;
   void* Y;
   int tiles_m, tiles_n;
-  int vec_out;   // N % 4 == 0 and Y aligned for 4-wide stores
+  int vec_out;   // store width: 2 (bf16 via LDS, 16 B), 1 (4 outputs), 0 (scalar)
+  int band;      // tile-order band width in column tiles (see k_gemm)
 };
 
 __device__ __forceinline__ int aswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -600,13 +622,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   const int r32 = lane & 31, g2 = lane >> 5;   // row/column within a 32 block, k group
   const int kw = K / 16;
 
-  // Bijective XCD-aware tile order: XCD x (= b % 8) takes tiles
-  // [x q + min(x, r), ...) where T = 8 q + r.
+  // Bijective XCD-aware tile order.  XCD x (= b % 8) takes positions
+  // [x q + min(x, r), ...) of the tile order, T = 8 q + r.  The order walks
+  // bands of `band` column tiles; inside a band, token row tiles, then the
+  // band's columns.  The workgroups resident on one XCD then share a few
+  // activation row blocks and one band of code blocks in that XCD's L2.
   const int T = ga.tiles_m * ga.tiles_n;
   const int b = blockIdx.x;
   const int xcd = b & 7, q8 = T >> 3, r8 = T & 7;
   const int t = xcd * q8 + min(xcd, r8) + (b >> 3);
-  const int tm = t / ga.tiles_n, tn = t % ga.tiles_n;
+  const int band_tiles = ga.tiles_m * ga.band;
+  const int bi = t / band_tiles;
+  const int within = t - bi * band_tiles;
+  const int bw = min(ga.band, ga.tiles_n - bi * ga.band);
+  const int tm = within / bw, tn = bi * ga.band + within % bw;
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Per-lane source addresses of the direct loads (k offset added per step).
@@ -731,6 +760,54 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   // output of token m0 + (row block) + r32 and weight row
   // n0 + (column block) + 8 i + 4 g2 + j.
   const float gamma = ga.gamma[0];
+  if constexpr (OUT == kOutBF16) {
+    if (ga.vec_out == 2) {
+      // Rows of 16-byte pieces through LDS: each wave stages one 32-row block
+      // of its sub-tile at a time in a stage buffer of its own (4 KB or 2 KB),
+      // then writes whole row segments (NB * 64 bytes) with 16-byte stores.
+      // Piece c of staged row r sits at slot c ^ ((r / RPL) % CH), which
+      // keeps both the 8-byte writes and the 16-byte reads conflict-free.
+      constexpr int CH = NB * 4;            // 16-byte pieces per staged row
+      constexpr int RPL = 16 / CH;          // staged rows per 256-byte bank row
+      static_assert(32 * CH * 16 <= BN * 32, "a code stage holds one block");
+      uint8_t* buf = wave == 0 ? reinterpret_cast<uint8_t*>(sA0)
+                   : wave == 1 ? reinterpret_cast<uint8_t*>(sA1)
+                   : wave == 2 ? reinterpret_cast<uint8_t*>(sA2) : sB0;
+      __syncthreads();   // every wave is done with the stage buffers
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int sw = (r32 / RPL) % CH;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float y[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              y[jj] = ((float)(acc[mb][nb][4 * i + jj] - sxv[mb]) * gamma) * scv[mb];
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16);
+            *reinterpret_cast<uint2*>(buf + r32 * (CH * 16) + 16 * ((nb * 4 + i) ^ sw) + 8 * g2) =
+                make_uint2(lo, hi);
+          }
+        }
+        // The wave's LDS accesses complete in order, so its reads below see
+        // its writes above, and the next block's writes follow these reads.
+#pragma unroll
+        for (int q = 0; q < 32 * CH / kWave; ++q) {
+          const int row = q * (kWave / CH) + lane / CH;
+          const int c = lane % CH;
+          const uint4 v = *reinterpret_cast<const uint4*>(
+              buf + row * (CH * 16) + 16 * (c ^ ((row / RPL) % CH)));
+          const int m = m0 + wm * MB * 32 + mb * 32 + row;
+          const int n = n0 + wn * NB * 32 + 8 * c;
+          if (m < M && n < N)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ga.Y) + (int64_t)m * N + n) = v;
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + wm * MB * 32 + mb * 32 + r32;
@@ -764,6 +841,7 @@ template <bool A64, int OUT, int BM, int BN, int WM, int WN>
 hipError_t launch_gemm_t(GemmArgs ga, hipStream_t stream) {
   ga.tiles_m = (ga.M + BM - 1) / BM;
   ga.tiles_n = (ga.N + BN - 1) / BN;
+  if (ga.band <= 0 || ga.band > ga.tiles_n) ga.band = ga.tiles_n;
   const int tiles = ga.tiles_m * ga.tiles_n;
   k_gemm<A64, OUT, BM, BN, WM, WN><<<dim3(tiles), dim3(kGemmThreads), 0, stream>>>(ga);
   return hipGetLastError();
@@ -792,9 +870,11 @@ hipError_t dispatch(const uint8_t* Wp, const float* gamma, int N, int K, const i
     DecodeArgs da{Wp, gamma, N, K, M, Xq, xs, xsum, nullptr, nullptr, nullptr, nullptr, Y};
     return launch_decode<A64, OUT>(decode_cfg(M, N, K, false), da, stream);
   }
-  const uintptr_t vec_bytes = OUT == kOutBF16 ? 8 : 16;
-  const int vec_out = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % vec_bytes == 0);
-  GemmArgs ga{Wp, gamma, N, K, M, Xq, xs, xsum, Y, 0, 0, vec_out};
+  // 2: bf16 rows through LDS with 16-byte stores; 1: 4-wide stores; 0: scalar.
+  const uintptr_t ya = reinterpret_cast<uintptr_t>(Y);
+  int vec_out = (N % 4 == 0) && (ya % (OUT == kOutBF16 ? 8 : 16) == 0);
+  if (OUT == kOutBF16 && N % 8 == 0 && ya % 16 == 0) vec_out = 2;
+  GemmArgs ga{Wp, gamma, N, K, M, Xq, xs, xsum, Y, 0, 0, vec_out, 8};
   return launch_gemm<A64, OUT>(gemm_cfg(M, N, K), ga, stream);
 }
 

@@ -197,7 +197,8 @@ def test_forward_rescale(gpu_lib, M, N, K, out):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "i32"])
-@pytest.mark.parametrize("M,N,K", [(4, 256, 1024), (96, 256, 1024), (300, 260, 512)])
+@pytest.mark.parametrize("M,N,K", [(4, 256, 1024), (96, 256, 1024), (300, 260, 512),
+                                   (300, 264, 512), (130, 136, 1040)])
 def test_forward_unaligned_output(gpu_lib, M, N, K, out):
     """Y one element past an aligned address (no vector stores possible): the same
     bytes as an aligned Y, and the oracle's values."""
