@@ -128,8 +128,10 @@ bitlinear_status bitlinear_quant_acts(const float* X, int64_t M, int64_t K,
                                       int8_t* X_q, float* x_scale, int32_t* x_sum,
                                       void* stream);
 
-/* Bytes of workspace bitlinear_forward needs (0 for every shape in this
- * version; a NULL workspace is then accepted). */
+/* Bytes of workspace bitlinear_forward needs: int32 partial accumulators
+ * when the shape runs with K split across workgroups (few output tiles and a
+ * long K, e.g. 17 <= M <= 128 on a few-thousand-row matrix), else 0 (a NULL
+ * workspace is then accepted).  0 if the shape is invalid. */
 size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -148,8 +150,12 @@ size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *           16-byte aligned).  x_sum must equal sum_k X_q[m][k].
  * Y         [M][N], device, aligned to its element size; fp32, bf16 or int32
  *           (BITLINEAR_I32 stores acc itself and ignores gamma/x_scale).
- * workspace may be NULL when bitlinear_forward_workspace_bytes() is 0.
- * Integer results are bit-exact and independent of the launch shape.
+ * workspace device, 16-byte aligned, >= bitlinear_forward_workspace_bytes(M,
+ *           N, K) bytes; contents need no initialisation and are scratch after
+ *           the call (two calls in flight at once need two workspaces).  May
+ *           be NULL when the size query returns 0.
+ * Integer results are bit-exact and independent of the launch shape (split
+ * partial sums are added in exact int32 arithmetic).
  */
 bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma,
                                    int64_t N, int64_t K,
@@ -159,9 +165,10 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
 
-/* Bytes of workspace bitlinear_forward_f32 needs when the caller passes no
- * quantiser output buffers: 0 when the shape runs as one fused launch, else
- * room for X~, x_scale and x_sum.  0 if the shape is invalid. */
+/* Bytes of workspace bitlinear_forward_f32 needs: 0 when the shape runs as
+ * one fused launch, else room for X~, x_scale and x_sum followed by the
+ * projection's own workspace (bitlinear_forward_workspace_bytes).  0 if the
+ * shape is invalid. */
 size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -177,9 +184,10 @@ size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Y        [M][N], device, as in bitlinear_forward.
  * X_q_out, x_scale_out, x_sum_out  optional (all three or none): receive the
  *          quantiser outputs, as bitlinear_quant_acts would write them.
- * workspace  needed only when the outputs are not given, of
- *          bitlinear_forward_f32_workspace_bytes(M, N, K) bytes (16-byte
- *          aligned); may be NULL when that is 0.
+ * workspace  bitlinear_forward_f32_workspace_bytes(M, N, K) bytes (16-byte
+ *          aligned), scratch after the call.  May be NULL when that is 0, or
+ *          when the outputs are given and bitlinear_forward_workspace_bytes
+ *          (M, N, K) is 0.
  */
 bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gamma,
                                        int64_t N, int64_t K, const float* X, int64_t M,

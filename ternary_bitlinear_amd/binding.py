@@ -188,7 +188,9 @@ def bitlinear_forward_f32(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None, X_
         _dev(X_q_out, torch.int8, "X_q_out")
         _dev(x_scale_out, torch.float32, "x_scale_out")
         _dev(x_sum_out, torch.int32, "x_sum_out")
-    need = 0 if X_q_out is not None else lib.bitlinear_forward_f32_workspace_bytes(M, N, K)
+    need = lib.bitlinear_forward_f32_workspace_bytes(M, N, K)
+    if X_q_out is not None and (M <= 16 or lib.bitlinear_forward_workspace_bytes(M, N, K) == 0):
+        need = 0   # outputs given and the projection needs no workspace of its own
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

@@ -81,8 +81,8 @@ size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
 }
 
 size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
-  return 0;
+  if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K)) return 0;
+  return bl::forward_workspace_bytes(M, N, K);
 }
 
 bitlinear_status bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
@@ -127,7 +127,6 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma, 
                                    const int32_t* x_sum, int64_t M, void* Y,
                                    bitlinear_dtype y_dtype, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   if (!W_packed || !gamma || !X_q || !x_scale || !x_sum || !Y)
     return fail(BITLINEAR_ERR_NULL, "forward: NULL buffer");
   if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K))
@@ -140,10 +139,16 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma, 
       !aligned(x_sum, 4) || !aligned(Y, ya))
     return fail(BITLINEAR_ERR_ALIGN, "forward: W_packed/X_q need 16-byte alignment, Y its "
                 "element size");
+  const size_t need = bl::forward_workspace_bytes(M, N, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "forward: workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned(workspace, 16)) return fail(BITLINEAR_ERR_ALIGN, "forward: workspace alignment");
   bitlinear_status s = check_device();
   if (s != BITLINEAR_OK) return s;
   return launched(bl::launch_forward(W_packed, gamma, N, K, X_q, x_scale, x_sum, M, Y,
-                                     (int)y_dtype, reinterpret_cast<hipStream_t>(stream)),
+                                     (int)y_dtype, need ? workspace : nullptr,
+                                     reinterpret_cast<hipStream_t>(stream)),
                   "forward launch");
 }
 
@@ -171,7 +176,10 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
       (X_q_out && (!aligned(X_q_out, 16) || !aligned(x_scale_out, 4) || !aligned(x_sum_out, 4))))
     return fail(BITLINEAR_ERR_ALIGN, "forward_f32: W_packed, X and X_q_out need 16-byte "
                 "alignment, Y its element size");
-  const size_t need = given ? 0 : bl::forward_f32_workspace_bytes(M, N, K);
+  // With the quantiser outputs given, the workspace is needed only for the
+  // projection's own part (same layout: it follows the quantiser region).
+  const bool proj_ws = M > 16 && bl::forward_workspace_bytes(M, N, K) > 0;
+  const size_t need = (given && !proj_ws) ? 0 : bl::forward_f32_workspace_bytes(M, N, K);
   if (need && (!workspace || workspace_bytes < need))
     return fail(BITLINEAR_ERR_WORKSPACE, "forward_f32: workspace of %zu bytes needed, got %zu",
                 need, workspace ? workspace_bytes : (size_t)0);

@@ -528,6 +528,8 @@ struct GemmArgs {
   int tiles_m, tiles_n;
   int vec_out;   // store width: 2 (bf16 via LDS, 16 B), 1 (4 outputs), 0 (scalar)
   int band;      // tile-order band width in column tiles (see k_gemm)
+  int splits;    // K splits per tile; > 1: raw int32 partial tiles into `part`
+  int32_t* part; // [splits][M][N] partial accumulators (splits > 1)
 };
 
 __device__ __forceinline__ int aswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -602,17 +604,28 @@ __device__ __forceinline__ void gemm_step(const int8_t* __restrict__ Ac, const u
   }
 }
 
-template <bool kAligned64, int OUT, int BM, int BN, int WM, int WN>
+template <bool kAligned64, int OUT, int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   static_assert(WM * WN == kGemmThreads / kWave, "4 waves");
+  static_assert(NS >= 2 && NS <= 8, "ring depth");
   constexpr int MB = BM / WM / 32, NB = BN / WN / 32;   // 32x32 blocks per wave
   static_assert(MB >= 1 && NB >= 1 && BN % 64 == 0, "tile");
   constexpr int A_INS = BM / 8 / 4;            // 1 KB direct loads per wave per stage (8 rows each)
   constexpr int B_BLK = BN / 32;               // 1 KB blocks of codes per stage (64 chunks each)
   constexpr int B_INS = (B_BLK + 3) / 4;       // per wave
   static_assert(A_INS >= 1, "tile");
-  __shared__ __attribute__((aligned(1024))) int8_t sA0[BM * 128], sA1[BM * 128], sA2[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 32], sB1[BN * 32], sB2[BN * 32];
+  // One array per stage, so every access names its stage at compile time.
+  // (sA2 also stages wave 2's epilogue rows, so it keeps 4 KB at NS = 2.)
+#define BL_SA(i) sA##i[NS > i ? BM * 128 : (i == 2 ? 4096 : 16)]
+#define BL_SB(i) sB##i[NS > i ? BN * 32 : 16]
+  __shared__ __attribute__((aligned(1024))) int8_t BL_SA(0), BL_SA(1), BL_SA(2), BL_SA(3),
+      BL_SA(4), BL_SA(5), BL_SA(6), BL_SA(7);
+  __shared__ __attribute__((aligned(1024))) uint8_t BL_SB(0), BL_SB(1), BL_SB(2), BL_SB(3),
+      BL_SB(4), BL_SB(5), BL_SB(6), BL_SB(7);
+#undef BL_SA
+#undef BL_SB
+  int8_t* const sA[8] = {sA0, sA1, sA2, sA3, sA4, sA5, sA6, sA7};
+  uint8_t* const sB[8] = {sB0, sB1, sB2, sB3, sB4, sB5, sB6, sB7};
 
   const int N = ga.N, K = ga.K, M = ga.M;
   const int tid = threadIdx.x;
@@ -627,16 +640,25 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   // bands of `band` column tiles; inside a band, token row tiles, then the
   // band's columns.  The workgroups resident on one XCD then share a few
   // activation row blocks and one band of code blocks in that XCD's L2.
-  const int T = ga.tiles_m * ga.tiles_n;
+  // With K split S ways, the order runs over (tile, split) items, the S
+  // splits of a tile adjacent.
+  const int S = ga.splits;
+  const int TT = ga.tiles_m * ga.tiles_n * S;
   const int b = blockIdx.x;
-  const int xcd = b & 7, q8 = T >> 3, r8 = T & 7;
-  const int t = xcd * q8 + min(xcd, r8) + (b >> 3);
+  const int xcd = b & 7, q8 = TT >> 3, r8 = TT & 7;
+  const int item = xcd * q8 + min(xcd, r8) + (b >> 3);
+  const int t = item / S, split = item - t * S;
   const int band_tiles = ga.tiles_m * ga.band;
   const int bi = t / band_tiles;
   const int within = t - bi * band_tiles;
   const int bw = min(ga.band, ga.tiles_n - bi * ga.band);
   const int tm = within / bw, tn = bi * ga.band + within % bw;
   const int m0 = tm * BM, n0 = tn * BN;
+  // This item's full K steps [kb, kb + nkf); the K tail goes to the last split.
+  const int nk_all = K / kGBK;
+  const int per_split = (nk_all + S - 1) / S;
+  const int kb = min(split * per_split, nk_all);
+  const bool has_tail = (K % kGBK) != 0 && split == S - 1;
 
   // Per-lane source addresses of the direct loads (k offset added per step).
   // Activation block blk holds rows 8 blk .. 8 blk + 7; lane l fills slot
@@ -647,7 +669,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
     const int blk = qi * 4 + wave;
     const int r = blk * 8 + (lane >> 3);
     const int piece = (lane & 7) ^ aswz(r);
-    asrc[qi] = ga.Xq + (int64_t)min(m0 + r, M - 1) * K + 16 * piece;
+    asrc[qi] = ga.Xq + (int64_t)min(m0 + r, M - 1) * K + (int64_t)kb * kGBK + 16 * piece;
   }
   // Code block bb holds half h = bb / (BN / 64) of rows 64 (bb % (BN / 64))
   // + lane.  Every wave issues B_INS code loads per stage, so all waves have
@@ -660,7 +682,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
     bblk[qi] = min(qi * 4 + wave, B_BLK - 1);
     const int h = bblk[qi] / (BN / 64);
     const int r = (bblk[qi] % (BN / 64)) * 64 + lane;
-    bsrc[qi] = ga.Wp + (int64_t)min(n0 + r, N - 1) * (K / 4) + 16 * h;
+    bsrc[qi] = ga.Wp + (int64_t)min(n0 + r, N - 1) * (K / 4) + (int64_t)kb * (kGBK / 4) + 16 * h;
   }
   auto issue = [&](int kt, int8_t* A, uint8_t* B) {
     const int k0 = kt * kGBK;
@@ -699,44 +721,45 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   const int b_row0 = wn * NB * 32 + r32;
   const int lane_sw = aswz(r32);
 
-  // Every step issues exactly NLD loads (the last two steps re-load the last
-  // stage into buffers nobody reads again), so before step kt the only loads
-  // younger than stage kt's are stage kt + 1's and one unconditional
-  // vmcnt(NLD) wait suffices.  Uniform counts also let the compiler see that
-  // the wait retires the stage being read, so it adds no drain of its own.
+  // The ring runs NS - 1 stages ahead.  Every step issues exactly NLD loads
+  // (the last steps re-load the last stage into buffers nobody reads
+  // again), so before step kt the only loads younger than stage kt's are
+  // those of the NS - 2 stages after it, and one unconditional
+  // vmcnt((NS - 2) NLD) wait suffices.  Uniform counts also let the compiler
+  // see that the wait retires the stage being read, so it adds no drain of
+  // its own.
   constexpr int NLD = A_INS + B_INS;
-  const int nkf = K / kGBK;                 // full steps
+  const int nkf = min(per_split, nk_all - kb);   // full steps of this item
   if (nkf > 0) {
-    issue(0, sA0, sB0);
-    issue(min(1, nkf - 1), sA1, sB1);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(min(s, nkf - 1), sA[s], sB[s]);
   }
-  auto step = [&](int kt, int8_t* Ac, uint8_t* Bc, int8_t* An, uint8_t* Bn) {
-    wait_vmcnt<NLD>();
-    // Also orders this wave's reads of stage kt - 1 (the buffer refilled
-    // below) before the other waves' refills: every wave has finished
-    // step kt - 1 when it reaches this barrier.
-    stage_barrier();
-    gemm_step<BN, MB, NB, A_INS, B_INS>(Ac, Bc, An, Bn, true, asrc, bsrc, bblk,
-                                        min(kt + 2, nkf - 1) * kGBK, wave, a_row0, b_row0,
-                                        lane_sw, g2, acc);
-  };
-  for (int kt = 0; kt < nkf; kt += 3) {
-    step(kt, sA0, sB0, sA2, sB2);
-    // Nested, so no path reaches the third step without the second's loads.
-    if (kt + 1 < nkf) {
-      step(kt + 1, sA1, sB1, sA0, sB0);
-      if (kt + 2 < nkf) step(kt + 2, sA2, sB2, sA1, sB1);
+  for (int kt = 0; kt < nkf; kt += NS) {
+    // A break leaves the rest, so no path reaches a step without the loads
+    // of the steps before it.
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (kt + s >= nkf) break;
+      wait_vmcnt<(NS - 2) * NLD>();
+      // Also orders this wave's reads of stage kt + s - 1 (the buffer
+      // refilled below) before the other waves' refills: every wave has
+      // finished that step when it reaches this barrier.
+      stage_barrier();
+      gemm_step<BN, MB, NB, A_INS, B_INS>(sA[s], sB[s], sA[(s + NS - 1) % NS],
+                                          sB[(s + NS - 1) % NS], true, asrc, bsrc, bblk,
+                                          min(kt + s + NS - 1, nkf - 1) * kGBK, wave, a_row0,
+                                          b_row0, lane_sw, g2, acc);
     }
   }
   // No direct load may still be writing LDS when the tail refills a stage or
   // the workgroup ends.
   wait_vmcnt<0>();
-  if (K % kGBK) {
-    // Tail step through registers, exact zero fill, into the stage no load
-    // targets any more.
-    int8_t* A = (nkf % 3 == 0) ? sA0 : (nkf % 3 == 1 ? sA1 : sA2);
-    uint8_t* B = (nkf % 3 == 0) ? sB0 : (nkf % 3 == 1 ? sB1 : sB2);
-    const int k0 = nkf * kGBK;
+  if (has_tail) {
+    // Tail step through registers, exact zero fill; the barrier below waits
+    // until no wave reads a stage any more.
+    int8_t* A = sA0;
+    uint8_t* B = sB0;
+    const int k0 = nk_all * kGBK;
     __syncthreads();
     for (int qd = tid; qd < BM * 8; qd += kGemmThreads) {
       const int r = qd >> 3, piece = qd & 7;
@@ -759,6 +782,35 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   // Epilogue: lane (r32, g2), register 4 i + j of block (mb, nb) holds the
   // output of token m0 + (row block) + r32 and weight row
   // n0 + (column block) + 8 i + 4 g2 + j.
+  if (S > 1) {
+    // Raw partial accumulators of this split; the reduction kernel adds the
+    // splits, subtracts the code offset and rescales.
+    int32_t* P = ga.part + (int64_t)split * M * N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + wm * MB * 32 + mb * 32 + r32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = n0 + wn * NB * 32 + nb * 32 + 8 * i + 4 * g2;
+          const int64_t idx = (int64_t)m * N + n;
+          i32x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][4 * i + j];
+          if (N % 4 == 0) {
+            if (n < N) *reinterpret_cast<i32x4*>(P + idx) = v;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (n + j < N) P[idx + j] = v[j];
+          }
+        }
+      }
+    }
+    return;
+  }
   const float gamma = ga.gamma[0];
   if constexpr (OUT == kOutBF16) {
     if (ga.vec_out == 2) {
@@ -833,39 +885,95 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   }
 }
 
+// Sum of the K splits of every output, then the epilogue: thread i handles
+// outputs 4i .. 4i + 3 of the flattened [M][N] tile set when N % 4 == 0 (one
+// vector load per split), else one output.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs ga) {
+  const int M = ga.M, N = ga.N, S = ga.splits;
+  const int64_t MN = (int64_t)M * N;
+  const float gamma = ga.gamma[0];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (N % 4 == 0) {
+    const int64_t e = 4 * i;
+    if (e >= MN) return;
+    const int m = (int)(e / N);
+    i32x4 v = *reinterpret_cast<const i32x4*>(ga.part + e);
+    for (int sp = 1; sp < S; ++sp) {
+      const i32x4 w = *reinterpret_cast<const i32x4*>(ga.part + sp * MN + e);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    const int32_t sx = ga.xsum[m];
+    v.x -= sx; v.y -= sx; v.z -= sx; v.w -= sx;
+    if (ga.vec_out) {
+      store_out4<OUT>(ga.Y, e, v, gamma, ga.xs[m]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store_out<OUT>(ga.Y, e + j, v[j], gamma, ga.xs[m]);
+    }
+  } else {
+    if (i >= MN) return;
+    const int m = (int)(i / N);
+    int32_t a = 0;
+    for (int sp = 0; sp < S; ++sp) a += ga.part[sp * MN + i];
+    store_out<OUT>(ga.Y, i, a - ga.xsum[m], gamma, ga.xs[m]);
+  }
+}
+
 struct GemmCfg {
   int bm, bn;
+  int splits;   // K splits (1: none)
 };
 
-template <bool A64, int OUT, int BM, int BN, int WM, int WN>
+template <bool A64, int OUT, int BM, int BN, int WM, int WN, int NS = 3>
 hipError_t launch_gemm_t(GemmArgs ga, hipStream_t stream) {
   ga.tiles_m = (ga.M + BM - 1) / BM;
   ga.tiles_n = (ga.N + BN - 1) / BN;
   if (ga.band <= 0 || ga.band > ga.tiles_n) ga.band = ga.tiles_n;
-  const int tiles = ga.tiles_m * ga.tiles_n;
-  k_gemm<A64, OUT, BM, BN, WM, WN><<<dim3(tiles), dim3(kGemmThreads), 0, stream>>>(ga);
+  if (ga.splits < 1) ga.splits = 1;
+  const int items = ga.tiles_m * ga.tiles_n * ga.splits;
+  k_gemm<A64, OUT, BM, BN, WM, WN, NS><<<dim3(items), dim3(kGemmThreads), 0, stream>>>(ga);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ga.splits == 1) return e;
+  const int64_t MN = (int64_t)ga.M * ga.N;
+  const int64_t threads = ga.N % 4 == 0 ? MN / 4 : MN;
+  k_splitk_reduce<OUT><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(ga);
   return hipGetLastError();
 }
 
 // 64 x 64 tiles up to 128 tokens (more workgroups to fill the chip), else
-// 128 x 128.
+// 128 x 128.  At most 128 tiles (a half-empty chip): K split up to 4 ways,
+// each split keeping at least 4 steps of 128 and the partial sums (written
+// and read back: 8 S M N bytes) costing no more traffic than the packed
+// weights (N K / 4 bytes): S <= K / (16 M).  Timed on MI355X: splitting the
+// 172-tile shapes (N = 11008, M <= 128) loses to the reduction's cost.
 inline GemmCfg gemm_cfg(int M, int N, int K) {
-  (void)N;
-  (void)K;
-  if (M <= 128) return {64, 64};
-  return {128, 128};
+  GemmCfg c{128, 128, 1};
+  if (M <= 128) c = {64, 64, 1};
+  const int tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+  const int nk = K / kGBK;
+  if (tiles <= 128) c.splits = max(1, min(4, min(nk / 4, K / (16 * M))));
+  return c;
+}
+
+// Partial accumulators of the split GEMM, 256-byte aligned.
+inline size_t gemm_workspace_bytes(const GemmCfg& c, int64_t M, int64_t N) {
+  if (c.splits <= 1) return 0;
+  return (size_t)(((c.splits * M * N * 4) + 255) / 256 * 256);
 }
 
 template <bool A64, int OUT>
-hipError_t launch_gemm(const GemmCfg& c, const GemmArgs& ga, hipStream_t stream) {
-  if (c.bm == 128 && c.bn == 128) return launch_gemm_t<A64, OUT, 128, 128, 2, 2>(ga, stream);
-  if (c.bm == 64 && c.bn == 64) return launch_gemm_t<A64, OUT, 64, 64, 2, 2>(ga, stream);
+hipError_t launch_gemm(const GemmCfg& c, GemmArgs ga, hipStream_t stream) {
+  ga.splits = c.splits;
+  if (c.bm == 128 && c.bn == 128) return launch_gemm_t<A64, OUT, 128, 128, 2, 2, 3>(ga, stream);
+  if (c.bm == 64 && c.bn == 64) return launch_gemm_t<A64, OUT, 64, 64, 2, 2, 4>(ga, stream);
   return hipErrorInvalidValue;
 }
 
 template <bool A64, int OUT>
 hipError_t dispatch(const uint8_t* Wp, const float* gamma, int N, int K, const int8_t* Xq,
-                    const float* xs, const int32_t* xsum, int M, void* Y, hipStream_t stream) {
+                    const float* xs, const int32_t* xsum, int M, void* Y, void* workspace,
+                    hipStream_t stream) {
   if (M <= 16) {
     DecodeArgs da{Wp, gamma, N, K, M, Xq, xs, xsum, nullptr, nullptr, nullptr, nullptr, Y};
     return launch_decode<A64, OUT>(decode_cfg(M, N, K, false), da, stream);
@@ -874,31 +982,41 @@ hipError_t dispatch(const uint8_t* Wp, const float* gamma, int N, int K, const i
   const uintptr_t ya = reinterpret_cast<uintptr_t>(Y);
   int vec_out = (N % 4 == 0) && (ya % (OUT == kOutBF16 ? 8 : 16) == 0);
   if (OUT == kOutBF16 && N % 8 == 0 && ya % 16 == 0) vec_out = 2;
-  GemmArgs ga{Wp, gamma, N, K, M, Xq, xs, xsum, Y, 0, 0, vec_out, 8};
-  return launch_gemm<A64, OUT>(gemm_cfg(M, N, K), ga, stream);
+  const GemmCfg c = gemm_cfg(M, N, K);
+  GemmArgs ga{Wp, gamma, N, K, M, Xq, xs, xsum, Y, 0, 0, vec_out, 8, 1,
+              reinterpret_cast<int32_t*>(workspace)};
+  return launch_gemm<A64, OUT>(c, ga, stream);
 }
 
 template <int OUT>
 hipError_t dispatch_out(const uint8_t* Wp, const float* gamma, int N, int K, const int8_t* Xq,
-                        const float* xs, const int32_t* xsum, int M, void* Y,
+                        const float* xs, const int32_t* xsum, int M, void* Y, void* workspace,
                         hipStream_t stream) {
-  if (K % 64 == 0) return dispatch<true, OUT>(Wp, gamma, N, K, Xq, xs, xsum, M, Y, stream);
-  return dispatch<false, OUT>(Wp, gamma, N, K, Xq, xs, xsum, M, Y, stream);
+  if (K % 64 == 0) return dispatch<true, OUT>(Wp, gamma, N, K, Xq, xs, xsum, M, Y, workspace, stream);
+  return dispatch<false, OUT>(Wp, gamma, N, K, Xq, xs, xsum, M, Y, workspace, stream);
 }
 
 }  // namespace
 
+size_t forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16) return 0;
+  return gemm_workspace_bytes(gemm_cfg((int)M, (int)N, (int)K), M, N);
+}
+
 hipError_t launch_forward(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
                           const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
-                          int64_t M, void* Y, int y_dtype, hipStream_t stream) {
+                          int64_t M, void* Y, int y_dtype, void* workspace, hipStream_t stream) {
   const int n = (int)N, k = (int)K, m = (int)M;
   switch (y_dtype) {
     case kOutF32:
-      return dispatch_out<kOutF32>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, stream);
+      return dispatch_out<kOutF32>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, workspace,
+                                   stream);
     case kOutBF16:
-      return dispatch_out<kOutBF16>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, stream);
+      return dispatch_out<kOutBF16>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, workspace,
+                                    stream);
     default:
-      return dispatch_out<kOutI32>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, stream);
+      return dispatch_out<kOutI32>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, workspace,
+                                   stream);
   }
 }
 
@@ -906,9 +1024,15 @@ hipError_t launch_forward(const uint8_t* W_packed, const float* gamma, int64_t N
 
 namespace bl {
 
+// Quantiser outputs (when the caller passes none), then the projection's
+// own workspace.
+inline size_t quant_region_bytes(int64_t M, int64_t K) {
+  return (size_t)(((M * K + 255) / 256) * 256 + ((8 * M + 255) / 256) * 256);
+}
+
 size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 && decode_cfg((int)M, (int)N, (int)K, true).am == kAFuse) return 0;
-  return (size_t)(((M * K + 255) / 256) * 256 + ((8 * M + 255) / 256) * 256);
+  return quant_region_bytes(M, K) + forward_workspace_bytes(M, N, K);
 }
 
 namespace {
@@ -941,15 +1065,18 @@ hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64
   int8_t* xq = X_q_out;
   float* xs = x_scale_out;
   int32_t* xsum = x_sum_out;
+  char* w = reinterpret_cast<char*>(workspace);
   if (xq == nullptr) {
-    char* w = reinterpret_cast<char*>(workspace);
     xq = reinterpret_cast<int8_t*>(w);
     xs = reinterpret_cast<float*>(w + ((M * K + 255) / 256) * 256);
     xsum = reinterpret_cast<int32_t*>(xs + M);
   }
+  // The projection's workspace follows the quantiser region (present in the
+  // size query in both cases).
+  void* fws = w ? w + quant_region_bytes(M, K) : nullptr;
   hipError_t e = launch_quant(X, M, K, xq, xs, xsum, stream);
   if (e != hipSuccess) return e;
-  return launch_forward(W_packed, gamma, N, K, xq, xs, xsum, M, Y, y_dtype, stream);
+  return launch_forward(W_packed, gamma, N, K, xq, xs, xsum, M, Y, y_dtype, fws, stream);
 }
 
 }  // namespace bl

@@ -16,14 +16,21 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* W_packed, 
 hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float* x_scale,
                         int32_t* x_sum, hipStream_t stream);
 
-// y_dtype: 0 fp32, 1 bf16, 2 int32 (raw accumulators).
+// Workspace of the projection: split-K partial accumulators for shapes with
+// few output tiles and long K, else 0.
+size_t forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+// y_dtype: 0 fp32, 1 bf16, 2 int32 (raw accumulators).  `workspace` holds at
+// least forward_workspace_bytes(M, N, K) bytes (16-byte aligned) when that is
+// non-zero.
 hipError_t launch_forward(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
                           const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
-                          int64_t M, void* Y, int y_dtype, hipStream_t stream);
+                          int64_t M, void* Y, int y_dtype, void* workspace, hipStream_t stream);
 
 // Quantisation fused with the projection (fp32 activations in).  Optional
 // X_q_out / x_scale_out / x_sum_out receive the quantiser's outputs (all or
-// none); with none, the two-launch fallback uses `workspace`.
+// none).  Unfused shapes use `workspace`: the quantiser region (used only
+// when no outputs are given), then the projection's workspace.
 size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
                               const float* X, int64_t M, void* Y, int y_dtype, int8_t* X_q_out,

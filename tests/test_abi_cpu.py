@@ -64,7 +64,17 @@ def test_size_queries(lib):
     assert 256 < ws <= 256 + 8192 * 10 * 8
     assert lib.bitlinear_pack_workspace_bytes(1, 16) >= 256 + 4 * 80
     assert lib.bitlinear_pack_workspace_bytes(1 << 20, 1 << 12) == 0   # N*K >= 2^31
-    assert lib.bitlinear_forward_workspace_bytes(64, 4096, 4096) == 0
+    # decode (M <= 16) and many-tile shapes need no workspace; few tiles with a
+    # long K split K: S int32 partial tiles, S <= K / (16 M), 256-byte rounded
+    assert lib.bitlinear_forward_workspace_bytes(4, 4096, 4096) == 0
+    assert lib.bitlinear_forward_workspace_bytes(2048, 11008, 4096) == 0
+    ws = lib.bitlinear_forward_workspace_bytes(64, 4096, 4096)
+    assert ws == 4 * 64 * 4096 * 4
+    ws = lib.bitlinear_forward_workspace_bytes(64, 4096, 11008)
+    assert ws % (64 * 4096 * 4) == 0 and 2 <= ws // (64 * 4096 * 4) <= 16
+    assert lib.bitlinear_forward_workspace_bytes(0, 4096, 4096) == 0
+    f32 = lib.bitlinear_forward_f32_workspace_bytes(64, 4096, 4096)
+    assert f32 >= 64 * 4096 + 8 * 64 + 4 * 64 * 4096 * 4
 
 
 def _last(lib):
@@ -97,6 +107,14 @@ def test_validation_statuses_without_gpu_calls(lib):
     bad = list(args); bad[4] = FAKE + 4
     assert lib.bitlinear_forward(*bad) == 3
     bad = list(args); bad[8] = FAKE + 1     # bf16 Y needs 2-byte alignment
+    assert lib.bitlinear_forward(*bad) == 3
+    # a split-K shape: workspace missing, too small, misaligned
+    split = [FAKE, FAKE, 4096, 4096, FAKE, FAKE, FAKE, 64, FAKE, 1, None, 0, None]
+    need = lib.bitlinear_forward_workspace_bytes(64, 4096, 4096)
+    assert lib.bitlinear_forward(*split) == 7 and "workspace" in _last(lib)
+    bad = list(split); bad[10] = FAKE; bad[11] = need - 16
+    assert lib.bitlinear_forward(*bad) == 7
+    bad = list(split); bad[10] = FAKE + 8; bad[11] = need
     assert lib.bitlinear_forward(*bad) == 3
     for s in range(9):
         assert lib.bitlinear_status_string(s)

@@ -144,6 +144,9 @@ FWD_SHAPES = [
     # GEMM path (M > 16): ragged tiles and K tails
     (17, 16, 64), (33, 130, 144), (64, 256, 4096), (130, 300, 1040), (300, 129, 128),
     (257, 513, 2048),
+    # K split across workgroups (partial sums + reduction): with a K tail, with
+    # N % 4 != 0 (scalar partial stores), two row tiles
+    (24, 200, 4160), (40, 130, 2064), (100, 64, 8192),
 ]
 
 
@@ -313,6 +316,8 @@ FUSED_SHAPES = [
     (1, 8640, 3200), (1, 3200, 8640), (1, 64, 28672), (4, 100, 8192),
     # outside the fused kernel's reach: two launches
     (9, 77, 1040), (16, 300, 4096), (8, 64, 8640), (40, 130, 1024), (2, 50, 40960),
+    # two launches with K split across workgroups (workspace needed either way)
+    (48, 200, 4096),
 ]
 
 
