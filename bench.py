@@ -44,7 +44,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least 200 steps and "
+                         "0.5 s, so the GPU clocks have ramped up; the count is reported)")
     ap.add_argument("--workload", default="decode-3b")
     ap.add_argument("--tokens", type=int, default=None, help="M; default: the workload's first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -149,16 +151,34 @@ def main():
                     fn()
         return g
 
-    # ---------------- warm-up (eager, then graph)
+    # ---------------- warm-up: eager steps, then the step graph replayed (by
+    # default until 0.5 s have passed, so that the clocks have ramped up)
+    w_eager = min(args.warmup, 200) if args.warmup is not None else 200
     with torch.cuda.stream(stream):
-        for r in range(args.warmup):
+        for r in range(w_eager):
             step(r)
     torch.cuda.synchronize()
     cycle = min(copies, args.steps)
     g_cycle = graph_of([lambda r=r: step(r) for r in range(cycle)])
     rem = args.steps % cycle
     g_rem = graph_of([lambda r=r: step(r) for r in range(rem)]) if rem else None
-    g_cycle.replay()
+    warmup = w_eager
+    t_w0 = time.perf_counter()
+    while True:
+        if args.warmup is not None:
+            if warmup >= args.warmup:
+                break
+            if args.warmup - warmup < cycle:      # exactly W: finish eagerly
+                with torch.cuda.stream(stream):
+                    for r in range(args.warmup - warmup):
+                        step(r)
+                warmup = args.warmup
+                break
+        elif time.perf_counter() - t_w0 >= 0.5:
+            break
+        g_cycle.replay()
+        warmup += cycle
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # ---------------- timed region: exactly K steps
@@ -239,7 +259,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": M,

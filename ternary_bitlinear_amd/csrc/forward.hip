@@ -93,6 +93,7 @@ __device__ __forceinline__ uint32_t load_word(const uint32_t* row, int wi, int k
 // ---------------------------------------------------------------------------
 constexpr int kAReg = 0, kALds = 1, kAFuse = 2;
 constexpr int kLdsBudget = 76 * 1024;   // keeps >= 2 workgroups per CU (160 KB LDS)
+constexpr int kLdsBudgetFew = 144 * 1024;   // one workgroup per CU
 constexpr int kFuseMaxVec = 16;      // float4 per thread in the fused prologue
 
 struct DecodeArgs {
@@ -405,16 +406,22 @@ struct DecodeCfg {
 };
 
 // The choices below come from timing sweeps on MI355X over the decode shapes
-// (3B, 7B and 70B projections, M = 1, 8, 16), with the weights cold in HBM.
+// (3B, 7B and 70B projections, M = 1, 8, 16), with the weights cold in HBM:
+//  - at most 256 row blocks (no more workgroups than CUs): 16 waves per
+//    workgroup, and the activations may take most of the LDS (one workgroup
+//    per CU is all these shapes run anyway);
+//  - 257..512 row blocks with long rows: a ring of 4 chunk groups;
+//  - 1024 row blocks or more: 4 waves.
 inline DecodeCfg decode_cfg(int M, int N, int K, bool fused) {
   DecodeCfg c{};
   const int nrb = (N + 15) / 16;
   const int ncg = ((K + 63) / 64 + 3) / 4;
   int mp = 1;
   while (mp < M) mp <<= 1;
-  int nw = nrb >= 1024 ? 4 : 8;
+  int nw = nrb >= 1024 ? 4 : (nrb <= 256 ? 16 : 8);
   while (nw > 1 && nw > ncg) nw >>= 1;
-  const bool lds_ok = decode_lds_bytes(nw, M, K) <= (size_t)kLdsBudget;
+  const size_t budget = nrb <= 256 ? kLdsBudgetFew : (size_t)kLdsBudget;
+  const bool lds_ok = decode_lds_bytes(nw, M, K) <= budget;
   if (fused) {
     // Every workgroup re-quantises the fp32 rows it needs; that redundant
     // read pays for itself only while the workgroups are few.
@@ -425,7 +432,7 @@ inline DecodeCfg decode_cfg(int M, int N, int K, bool fused) {
   }
   if (c.am == kAFuse || c.am == kALds) {
     c.nw = nw;
-    c.p = 2;
+    c.p = (nw == 8 && nrb > 256 && nrb <= 512 && ncg >= 8 * nw) ? 4 : 2;
     c.grid = nrb;       // one 16-row block per workgroup
     c.rb = 1;
   } else if (c.am == kAReg) {
@@ -468,7 +475,7 @@ hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t s
   if (c.nw == NW && c.p == P)                                                              \
     return c.am == kALds ? launch_decode_lds_t<A64, OUT, NW, P, kALds>(c, da, stream)      \
                          : launch_decode_lds_t<A64, OUT, NW, P, kAFuse>(c, da, stream);
-    BL_DL(8, 2) BL_DL(4, 2) BL_DL(2, 2) BL_DL(1, 2)
+    BL_DL(16, 2) BL_DL(8, 2) BL_DL(8, 4) BL_DL(4, 2) BL_DL(2, 2) BL_DL(1, 2)
 #undef BL_DL
   } else if (c.am == kAReg) {
 #define BL_DR(RB, NW, P) \
@@ -983,7 +990,7 @@ hipError_t dispatch(const uint8_t* Wp, const float* gamma, int N, int K, const i
   int vec_out = (N % 4 == 0) && (ya % (OUT == kOutBF16 ? 8 : 16) == 0);
   if (OUT == kOutBF16 && N % 8 == 0 && ya % 16 == 0) vec_out = 2;
   const GemmCfg c = gemm_cfg(M, N, K);
-  GemmArgs ga{Wp, gamma, N, K, M, Xq, xs, xsum, Y, 0, 0, vec_out, 8, 1,
+  GemmArgs ga{Wp, gamma, N, K, M, Xq, xs, xsum, Y, 0, 0, vec_out, 16, 1,
               reinterpret_cast<int32_t*>(workspace)};
   return launch_gemm<A64, OUT>(c, ga, stream);
 }
