@@ -377,13 +377,16 @@ def traffic_from(args):
         c = _counters(d, cname)
         cal = [v for kn, v in c.values() if "neg" in kn.lower()]
         ker = [v for kn, v in c.values() if fam in kn]
+        # a projection with K split across workgroups is two dispatches
+        red = [v for kn, v in c.values() if "k_splitk_reduce" in kn]
         if len(cal) != 1 or not ker:
             raise SystemExit(f"{d}: expected one calibration copy and >= 1 {fam} dispatch, "
                              f"found {len(cal)} and {len(ker)}")
         factor = CAL_BYTES / (cal[0] * 1024.0)
-        kib = sum(ker) / len(ker)
+        kib = (sum(ker) + sum(red)) / len(ker)
         out[what] = {"counter": cname, "calibration_kib": cal[0], "factor": round(factor, 5),
                      "kernel_kib_per_dispatch": round(kib, 2), "dispatches": len(ker),
+                     "reduce_dispatches": len(red),
                      "bytes_per_launch": kib * 1024.0 * factor}
     alg = sum(alg_bytes(P, M, wl.out_dtype) for P in shapes) / len(shapes)
     total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
