@@ -141,6 +141,9 @@ FWD_SHAPES = [
     (7, 64, 8640), (1, 3200, 8640),
     # decode with 2 and 4 row blocks per workgroup (needs >= 256 workgroups), ragged N
     (7, 8200, 80), (13, 16400, 1040), (16, 16384, 256),
+    # single token on the vector ALU (K % 64 == 0, K <= 4096): one piece per
+    # row, N below and not a multiple of the rows per wave, full rows
+    (1, 1, 64), (1, 3, 4096), (1, 1001, 192), (1, 8640, 3200), (1, 11008, 4096),
     # GEMM path (M > 16): ragged tiles and K tails
     (17, 16, 64), (33, 130, 144), (64, 256, 4096), (130, 300, 1040), (300, 129, 128),
     (257, 513, 2048),
