@@ -48,6 +48,8 @@ extern "C" {
 /* Packed weight format: 2 bits per weight, see bitlinear_pack_weights. */
 #define BITLINEAR_PACK_FORMAT_BLT2_V1 1
 #define BITLINEAR_MAX_K 131072
+/* Projections per grouped call (bitlinear_forward_grouped). */
+#define BITLINEAR_MAX_GROUP 4
 
 typedef enum bitlinear_status {
   BITLINEAR_OK = 0,
@@ -194,6 +196,57 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
                                        void* Y, bitlinear_dtype y_dtype,
                                        int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Several projections of one activation matrix in one call: the query, key
+ * and value projections of an attention block, or the gate and up
+ * projections of a feed-forward block, which all read the same X~.  For
+ * g < G this computes exactly what bitlinear_forward(W_packed[g], gamma[g],
+ * N[g], K, X_q, x_scale, x_sum, M, Y[g], y_dtype, ...) computes (page
+ * section 2, "The Linear Transformation and Rescaling").  Decode shapes
+ * (M <= 16) run as one launch over the rows of all G matrices, so the group
+ * pays one launch instead of G; larger M runs the projections one after
+ * another.
+ *
+ * G          1 .. BITLINEAR_MAX_GROUP.
+ * W_packed, gamma, N, Y   HOST arrays of G entries (read during the call,
+ *            not kept); the buffers they point to are device memory, laid
+ *            out and aligned as for bitlinear_forward.  All projections share
+ *            K, M, X_q, x_scale and x_sum.
+ * workspace  >= bitlinear_forward_grouped_workspace_bytes(M, G, N, K) bytes
+ *            (16-byte aligned), scratch after the call; may be NULL when that
+ *            is 0 (it is 0 for M <= 16).
+ */
+size_t bitlinear_forward_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K);
+bitlinear_status bitlinear_forward_grouped(int G, const uint8_t* const* W_packed,
+                                           const float* const* gamma, const int64_t* N,
+                                           int64_t K, const int8_t* X_q, const float* x_scale,
+                                           const int32_t* x_sum, int64_t M, void* const* Y,
+                                           bitlinear_dtype y_dtype, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/*
+ * The grouped projection from fp32 activations: X is quantised once (page
+ * section 2, absmax activation quantiser), then every projection as in
+ * bitlinear_forward_grouped; for decode shapes whose rows in total fit the
+ * fused kernel this is a single launch.  Arguments as in
+ * bitlinear_forward_f32, with the per-projection arrays as in
+ * bitlinear_forward_grouped.
+ *
+ * workspace  bitlinear_forward_f32_grouped_workspace_bytes(M, G, N, K) bytes
+ *            (16-byte aligned), scratch after the call.  May be NULL when
+ *            that is 0, or when the quantiser outputs are given and
+ *            bitlinear_forward_grouped_workspace_bytes(M, G, N, K) is 0.
+ */
+size_t bitlinear_forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N,
+                                                     int64_t K);
+bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_packed,
+                                               const float* const* gamma, const int64_t* N,
+                                               int64_t K, const float* X, int64_t M,
+                                               void* const* Y, bitlinear_dtype y_dtype,
+                                               int8_t* X_q_out, float* x_scale_out,
+                                               int32_t* x_sum_out, void* workspace,
+                                               size_t workspace_bytes, void* stream);
 
 /* Static English name of a status. */
 const char* bitlinear_status_string(bitlinear_status s);

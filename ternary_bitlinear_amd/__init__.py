@@ -8,12 +8,17 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     SIGNATURES,
     STATUS,
+    MAX_GROUP,
     BitLinearError,
     bitlinear_forward,
     bitlinear_forward_f32,
+    bitlinear_forward_f32_grouped,
+    bitlinear_forward_grouped,
     bitlinear_pack_weights,
     bitlinear_quant_acts,
+    forward_f32_grouped_workspace_bytes,
     forward_f32_workspace_bytes,
+    forward_grouped_workspace_bytes,
     forward_workspace_bytes,
     load,
     pack_workspace_bytes,

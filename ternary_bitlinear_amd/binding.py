@@ -33,6 +33,13 @@ SIGNATURES = {
     "bitlinear_forward_f32_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "bitlinear_forward_f32": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, ctypes.c_int,
                                              _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bitlinear_forward_grouped_workspace_bytes": (_c_size, [_c_i64, ctypes.c_int, _vp, _c_i64]),
+    "bitlinear_forward_grouped": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp,
+                                                 _c_i64, _vp, ctypes.c_int, _vp, _c_size, _vp]),
+    "bitlinear_forward_f32_grouped_workspace_bytes": (_c_size, [_c_i64, ctypes.c_int, _vp, _c_i64]),
+    "bitlinear_forward_f32_grouped": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i64, _vp, _c_i64,
+                                                     _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_size,
+                                                     _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -199,4 +206,99 @@ def bitlinear_forward_f32(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None, X_
     _check(lib.bitlinear_forward_f32(W_packed.data_ptr(), gamma.data_ptr(), N, K, X.data_ptr(), M,
                                      Y.data_ptr(), DTYPES[y_dtype], ptr[0], ptr[1], ptr[2],
                                      ws_ptr, ws_bytes, _stream(stream)))
+    return Y
+
+
+MAX_GROUP = 4
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _i64_array(vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def forward_grouped_workspace_bytes(M: int, Ns, K: int) -> int:
+    return load().bitlinear_forward_grouped_workspace_bytes(M, len(Ns), _i64_array(Ns), K)
+
+
+def forward_f32_grouped_workspace_bytes(M: int, Ns, K: int) -> int:
+    return load().bitlinear_forward_f32_grouped_workspace_bytes(M, len(Ns), _i64_array(Ns), K)
+
+
+def _outputs(Ns, M, y_dtype, device, Y):
+    import torch
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[y_dtype]
+    if Y is None:
+        Y = [torch.empty((M, n), dtype=tdt, device=device) for n in Ns]
+    if len(Y) != len(Ns):
+        raise ValueError("one output per projection")
+    for y in Y:
+        _dev(y, tdt, "Y")
+    return Y
+
+
+def bitlinear_forward_grouped(W_packed, gamma, X_q, x_scale, x_sum, Ns=None, K=None,
+                              y_dtype="bf16", Y=None, workspace=None, stream=None):
+    """Several packed projections of one quantised X~ -> list of Y [M][N_g]."""
+    import torch
+    lib = load()
+    G = len(W_packed)
+    if len(gamma) != G:
+        raise ValueError("one gamma per projection")
+    for w in W_packed:
+        _dev(w, torch.uint8, "W_packed")
+    _dev(X_q, torch.int8, "X_q")
+    M, Kx = X_q.shape
+    K = Kx if K is None else K
+    Ns = [w.shape[0] for w in W_packed] if Ns is None else list(Ns)
+    Y = _outputs(Ns, M, y_dtype, X_q.device, Y)
+    need = lib.bitlinear_forward_grouped_workspace_bytes(M, G, _i64_array(Ns), K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X_q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.bitlinear_forward_grouped(G, _ptr_array(W_packed), _ptr_array(gamma), _i64_array(Ns),
+                                         K, X_q.data_ptr(), x_scale.data_ptr(), x_sum.data_ptr(), M,
+                                         _ptr_array(Y), DTYPES[y_dtype], ws_ptr, ws_bytes,
+                                         _stream(stream)))
+    return Y
+
+
+def bitlinear_forward_f32_grouped(W_packed, gamma, X, Ns=None, y_dtype="bf16", Y=None,
+                                  X_q_out=None, x_scale_out=None, x_sum_out=None, workspace=None,
+                                  stream=None):
+    """Quantise fp32 X [M][K] once and run every packed projection -> list of Y."""
+    import torch
+    lib = load()
+    G = len(W_packed)
+    if len(gamma) != G:
+        raise ValueError("one gamma per projection")
+    for w in W_packed:
+        _dev(w, torch.uint8, "W_packed")
+    _dev(X, torch.float32, "X")
+    M, K = X.shape
+    Ns = [w.shape[0] for w in W_packed] if Ns is None else list(Ns)
+    Y = _outputs(Ns, M, y_dtype, X.device, Y)
+    outs = (X_q_out, x_scale_out, x_sum_out)
+    if X_q_out is not None:
+        _dev(X_q_out, torch.int8, "X_q_out")
+        _dev(x_scale_out, torch.float32, "x_scale_out")
+        _dev(x_sum_out, torch.int32, "x_sum_out")
+    n_arr = _i64_array(Ns)
+    need = lib.bitlinear_forward_f32_grouped_workspace_bytes(M, G, n_arr, K)
+    if X_q_out is not None and (M <= 16 or lib.bitlinear_forward_grouped_workspace_bytes(
+            M, G, n_arr, K) == 0):
+        need = 0   # outputs given and the projections need no workspace of their own
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ptr = [o.data_ptr() if o is not None else None for o in outs]
+    _check(lib.bitlinear_forward_f32_grouped(G, _ptr_array(W_packed), _ptr_array(gamma), n_arr, K,
+                                             X.data_ptr(), M, _ptr_array(Y), DTYPES[y_dtype],
+                                             ptr[0], ptr[1], ptr[2], ws_ptr, ws_bytes,
+                                             _stream(stream)))
     return Y

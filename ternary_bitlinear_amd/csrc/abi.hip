@@ -12,6 +12,8 @@
 #include "../../include/bitlinear.h"
 #include "kernels.hpp"
 
+static_assert(BITLINEAR_MAX_GROUP == bl::kMaxGroupProjections, "group size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -191,6 +193,111 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
                                          x_scale_out, x_sum_out, workspace,
                                          reinterpret_cast<hipStream_t>(stream)),
                   "forward_f32 launch");
+}
+
+// ---- several projections of one activation matrix -----------------------------
+
+namespace {
+bitlinear_status check_group(const char* who, int G, const uint8_t* const* W_packed,
+                             const float* const* gamma, const int64_t* N, int64_t K, int64_t M,
+                             void* const* Y, bitlinear_dtype y_dtype) {
+  if (G < 1 || G > BITLINEAR_MAX_GROUP)
+    return fail(BITLINEAR_ERR_SHAPE, "%s: G=%d outside 1..%d", who, G, BITLINEAR_MAX_GROUP);
+  if (!W_packed || !gamma || !N || !Y) return fail(BITLINEAR_ERR_NULL, "%s: NULL array", who);
+  if (M < 1 || M > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "%s: invalid shape M=%lld K=%lld", who, (long long)M,
+                (long long)K);
+  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+    return fail(BITLINEAR_ERR_DTYPE, "%s: unknown y_dtype %d", who, (int)y_dtype);
+  const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
+  for (int g = 0; g < G; ++g) {
+    if (!W_packed[g] || !gamma[g] || !Y[g])
+      return fail(BITLINEAR_ERR_NULL, "%s: NULL buffer of projection %d", who, g);
+    if (N[g] < 1 || N[g] > kMaxDim)
+      return fail(BITLINEAR_ERR_SHAPE, "%s: invalid N=%lld of projection %d", who,
+                  (long long)N[g], g);
+    if (!aligned(W_packed[g], 16) || !aligned(gamma[g], 4) || !aligned(Y[g], ya))
+      return fail(BITLINEAR_ERR_ALIGN, "%s: projection %d: W_packed needs 16-byte alignment, "
+                  "Y its element size", who, g);
+  }
+  return BITLINEAR_OK;
+}
+}  // namespace
+
+size_t bitlinear_forward_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K) {
+  if (G < 1 || G > BITLINEAR_MAX_GROUP || !N || M < 1 || M > kMaxDim || !shape_ok_k(K)) return 0;
+  for (int g = 0; g < G; ++g)
+    if (N[g] < 1 || N[g] > kMaxDim) return 0;
+  return bl::forward_grouped_workspace_bytes(M, G, N, K);
+}
+
+bitlinear_status bitlinear_forward_grouped(int G, const uint8_t* const* W_packed,
+                                           const float* const* gamma, const int64_t* N,
+                                           int64_t K, const int8_t* X_q, const float* x_scale,
+                                           const int32_t* x_sum, int64_t M, void* const* Y,
+                                           bitlinear_dtype y_dtype, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  bitlinear_status s = check_group("forward_grouped", G, W_packed, gamma, N, K, M, Y, y_dtype);
+  if (s != BITLINEAR_OK) return s;
+  if (!X_q || !x_scale || !x_sum) return fail(BITLINEAR_ERR_NULL, "forward_grouped: NULL buffer");
+  if (!aligned(X_q, 16) || !aligned(x_scale, 4) || !aligned(x_sum, 4))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_grouped: X_q needs 16-byte alignment");
+  const size_t need = bl::forward_grouped_workspace_bytes(M, G, N, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "forward_grouped: workspace of %zu bytes needed, got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned(workspace, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_grouped: workspace alignment");
+  s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward_grouped(G, W_packed, gamma, N, K, X_q, x_scale, x_sum, M, Y,
+                                             (int)y_dtype, need ? workspace : nullptr,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                  "forward_grouped launch");
+}
+
+size_t bitlinear_forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N,
+                                                     int64_t K) {
+  if (G < 1 || G > BITLINEAR_MAX_GROUP || !N || M < 1 || M > kMaxDim || !shape_ok_k(K)) return 0;
+  for (int g = 0; g < G; ++g)
+    if (N[g] < 1 || N[g] > kMaxDim) return 0;
+  return bl::forward_f32_grouped_workspace_bytes(M, G, N, K);
+}
+
+bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_packed,
+                                               const float* const* gamma, const int64_t* N,
+                                               int64_t K, const float* X, int64_t M,
+                                               void* const* Y, bitlinear_dtype y_dtype,
+                                               int8_t* X_q_out, float* x_scale_out,
+                                               int32_t* x_sum_out, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  bitlinear_status s = check_group("forward_f32_grouped", G, W_packed, gamma, N, K, M, Y, y_dtype);
+  if (s != BITLINEAR_OK) return s;
+  if (!X) return fail(BITLINEAR_ERR_NULL, "forward_f32_grouped: NULL X");
+  const int given = (X_q_out != nullptr) + (x_scale_out != nullptr) + (x_sum_out != nullptr);
+  if (given != 0 && given != 3)
+    return fail(BITLINEAR_ERR_NULL,
+                "forward_f32_grouped: X_q_out, x_scale_out and x_sum_out go together");
+  if (!aligned(X, 16) ||
+      (X_q_out && (!aligned(X_q_out, 16) || !aligned(x_scale_out, 4) || !aligned(x_sum_out, 4))))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_f32_grouped: X and X_q_out need 16-byte alignment");
+  // With the quantiser outputs given, the workspace is needed only for the
+  // projections' own part (same layout: it follows the quantiser region).
+  const bool proj_ws = M > 16 && bl::forward_grouped_workspace_bytes(M, G, N, K) > 0;
+  const size_t need =
+      (given && !proj_ws) ? 0 : bl::forward_f32_grouped_workspace_bytes(M, G, N, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE,
+                "forward_f32_grouped: workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned(workspace, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_f32_grouped: workspace alignment");
+  s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward_f32_grouped(G, W_packed, gamma, N, K, X, M, Y, (int)y_dtype,
+                                                 X_q_out, x_scale_out, x_sum_out, workspace,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                  "forward_f32_grouped launch");
 }
 
 const char* bitlinear_status_string(bitlinear_status s) {

@@ -21,6 +21,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace bl {
 
 namespace {
@@ -96,10 +98,19 @@ constexpr int kLdsBudget = 76 * 1024;   // keeps >= 2 workgroups per CU (160 KB 
 constexpr int kLdsBudgetFew = 144 * 1024;   // one workgroup per CU
 constexpr int kFuseMaxVec = 16;      // float4 per thread in the fused prologue
 
+constexpr int kMaxGroup = kMaxGroupProjections;   // projections of one activation matrix per launch
+
 struct DecodeArgs {
-  const uint8_t* Wp;
-  const float* gamma;
-  int N, K, M;
+  // Projections sharing the activations (G = 1 for a single one): packed
+  // weights, gamma, rows and output of projection g, and the first work unit
+  // (workgroup or wave, as the kernel counts them) that serves it.
+  const uint8_t* Wp[kMaxGroup];
+  const float* gamma[kMaxGroup];
+  int Ng[kMaxGroup];
+  void* Y[kMaxGroup];
+  int first[kMaxGroup + 1];
+  int G;
+  int K, M;
   const int8_t* Xq;        // kAReg / kALds: quantised activations [M][K]
   const float* xs;         //                x_scale [M]
   const int32_t* xsum;     //                x_sum [M]
@@ -107,8 +118,62 @@ struct DecodeArgs {
   int8_t* Xq_out;          // kAFuse: optional copies of the quantiser outputs
   float* xs_out;
   int32_t* xsum_out;
-  void* Y;
 };
+
+inline DecodeArgs decode_args_one(const uint8_t* Wp, const float* gamma, int N, int K, int M,
+                                  void* Y) {
+  DecodeArgs da{};
+  da.Wp[0] = Wp;
+  da.gamma[0] = gamma;
+  da.Ng[0] = N;
+  da.Y[0] = Y;
+  da.G = 1;
+  da.K = K;
+  da.M = M;
+  return da;
+}
+
+// Work units per projection: first[g] = sum over g' < g of ceil(N_g' / rows).
+inline int set_units(DecodeArgs& da, int rows_per_unit) {
+  da.first[0] = 0;
+  for (int g = 0; g < kMaxGroup; ++g)
+    da.first[g + 1] = da.first[g] + (g < da.G ? (da.Ng[g] + rows_per_unit - 1) / rows_per_unit : 0);
+  return da.first[da.G];
+}
+
+// Rows of all projections, each rounded up to whole 16-row blocks (sizes the
+// launch geometry of a grouped launch as one matrix of that many rows).
+inline int decode_rows(const DecodeArgs& da) {
+  int n = 0;
+  for (int g = 0; g < da.G; ++g) n += 16 * ((da.Ng[g] + 15) / 16);
+  return n;
+}
+
+// The projection a work unit serves, and the unit's index within it.  The
+// fields are picked with constant indices (no dynamic indexing of the
+// kernel arguments); `unit` is uniform over the wave.
+struct DecodeView {
+  const uint8_t* Wp;
+  const float* gamma;
+  int N;
+  void* Y;
+  int unit;
+};
+
+__device__ __forceinline__ DecodeView decode_view(const DecodeArgs& da, int unit) {
+  DecodeView v{da.Wp[0], da.gamma[0], da.Ng[0], da.Y[0], unit};
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) {
+    if (i < da.G && unit >= da.first[i]) {
+      v.Wp = da.Wp[i];
+      v.gamma = da.gamma[i];
+      v.N = da.Ng[i];
+      v.Y = da.Y[i];
+      v.unit = unit - da.first[i];
+    }
+  }
+  return v;
+}
 
 // Per-token epilogue inputs of lane group g (tokens 4g .. 4g + 3), read when
 // the kernel starts so that no memory round trip follows the reduction.
@@ -118,9 +183,10 @@ struct DecodeEpi {
   float sc[4];
 };
 
-__device__ __forceinline__ DecodeEpi decode_epi_load(const DecodeArgs& da, int g) {
+__device__ __forceinline__ DecodeEpi decode_epi_load(const DecodeArgs& da, const DecodeView& v,
+                                                    int g) {
   DecodeEpi e;
-  e.gamma = da.gamma[0];
+  e.gamma = v.gamma[0];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = min(4 * g + r, da.M - 1);
@@ -151,14 +217,14 @@ __device__ __forceinline__ void decode_epi_fused(DecodeEpi& e, int g, int M,
 
 // Epilogue of one 16-row block: lane (j, g) holds C[4g + r][j] in sum.
 template <int OUT>
-__device__ __forceinline__ void decode_store(const DecodeArgs& da, int n, int g, const i32x4& sum,
-                                             const DecodeEpi& e) {
-  if (n >= da.N) return;
+__device__ __forceinline__ void decode_store(const DecodeView& v, int M, int n, int g,
+                                             const i32x4& sum, const DecodeEpi& e) {
+  if (n >= v.N) return;
   const int32_t vals[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * g + r;
-    if (m < da.M) store_out<OUT>(da.Y, (int64_t)m * da.N + n, vals[r] - e.sx[r], e.gamma, e.sc[r]);
+    if (m < M) store_out<OUT>(v.Y, (int64_t)m * v.N + n, vals[r] - e.sx[r], e.gamma, e.sc[r]);
   }
 }
 
@@ -177,7 +243,8 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_lds(DecodeArgs da) {
   uint32_t* s_wmax = reinterpret_cast<uint32_t*>(smem + lds_red_bytes(NW));        // [NW]
   int32_t* s_wsum = reinterpret_cast<int32_t*>(s_wmax + NW);                       // [NW]
   int8_t* xl = reinterpret_cast<int8_t*>(smem + lds_x_offset(NW));               // [M][K+16]
-  const int N = da.N, K = da.K, M = da.M;
+  const DecodeView view = decode_view(da, blockIdx.x);
+  const int N = view.N, K = da.K, M = da.M;
   const int KP = K + 16;
   int8_t* zero_slot = xl + (int64_t)M * KP;
 
@@ -189,9 +256,9 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_lds(DecodeArgs da) {
   const int nchunks = (K + 63) / 64;
   const int ncg = (nchunks + 3) / 4;
   const int n_it = wave < ncg ? (ncg - wave + NW - 1) / NW : 0;
-  const int n0 = 16 * (int)blockIdx.x;
+  const int n0 = 16 * view.unit;
   const uint32_t* wrow =
-      reinterpret_cast<const uint32_t*>(da.Wp + (int64_t)min(n0 + j, N - 1) * (K / 4));
+      reinterpret_cast<const uint32_t*>(view.Wp + (int64_t)min(n0 + j, N - 1) * (K / 4));
   const bool tok_ok = j < M;
 
   int mp = 1;
@@ -199,8 +266,8 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_lds(DecodeArgs da) {
   const int gw = NW / mp;                    // fused: waves per token (host ensures M <= NW)
 
   DecodeEpi epi;
-  if constexpr (AM == kAFuse) epi.gamma = da.gamma[0];
-  else epi = decode_epi_load(da, g);
+  if constexpr (AM == kAFuse) epi.gamma = view.gamma[0];
+  else epi = decode_epi_load(da, view, g);
 
   // Fused prologue, part 1: the fp32 activations are requested before the
   // weights so that they do not queue behind the weight stream.
@@ -312,19 +379,20 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_lds(DecodeArgs da) {
     sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
   }
   if constexpr (AM == kAFuse) decode_epi_fused(epi, g, M, s_wmax, s_wsum, gw);
-  decode_store<OUT>(da, n0 + j, g, sum, epi);
+  decode_store<OUT>(view, M, n0 + j, g, sum, epi);
 }
 
 template <bool kAligned64, int OUT, int RB, int NW, int P>
 __global__ __launch_bounds__(NW * kWave) void k_decode_reg(DecodeArgs da) {
   static_assert(RB <= NW, "one wave per row block in the epilogue");
   __shared__ i32x4 red[NW * RB * kWave];
-  const int N = da.N, K = da.K, M = da.M;
+  const DecodeView view = decode_view(da, blockIdx.x);
+  const int N = view.N, K = da.K, M = da.M;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int rb0 = blockIdx.x * RB;
+  const int rb0 = view.unit * RB;
   const int kw = K / 16;
   const int nchunks = (K + 63) / 64;
   const int ncg = (nchunks + 3) / 4;
@@ -333,10 +401,10 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_reg(DecodeArgs da) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
     wrow[rb] = reinterpret_cast<const uint32_t*>(
-        da.Wp + (int64_t)min(16 * (rb0 + rb) + j, N - 1) * (K / 4));
+        view.Wp + (int64_t)min(16 * (rb0 + rb) + j, N - 1) * (K / 4));
   const bool tok_ok = j < M;
   const int8_t* xrow = da.Xq + (int64_t)min(j, M - 1) * K;
-  const DecodeEpi epi = decode_epi_load(da, g);
+  const DecodeEpi epi = decode_epi_load(da, view, g);
 
   uint32_t wb[P][RB][4];
   i32x4 ab[P][4];
@@ -394,7 +462,7 @@ __global__ __launch_bounds__(NW * kWave) void k_decode_reg(DecodeArgs da) {
     const i32x4 o = red[(w2 * RB + rb) * kWave + lane];
     sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
   }
-  decode_store<OUT>(da, 16 * (rb0 + rb) + j, g, sum, epi);
+  decode_store<OUT>(view, M, 16 * (rb0 + rb) + j, g, sum, epi);
 }
 
 // Launch geometry of the decode kernels for one shape.
@@ -450,7 +518,9 @@ inline DecodeCfg decode_cfg(int M, int N, int K, bool fused) {
 }
 
 template <bool A64, int OUT, int NW, int P, int AM>
-hipError_t launch_decode_lds_t(const DecodeCfg& c, const DecodeArgs& da, hipStream_t stream) {
+hipError_t launch_decode_lds_t(const DecodeCfg& c, DecodeArgs da, hipStream_t stream) {
+  (void)c;
+  const int grid = set_units(da, 16);   // one 16-row block per workgroup
   const size_t lds = decode_lds_bytes(NW, da.M, da.K);
   auto kern = k_decode_lds<A64, OUT, NW, P, AM>;
   if (lds > 64 * 1024) {
@@ -458,13 +528,15 @@ hipError_t launch_decode_lds_t(const DecodeCfg& c, const DecodeArgs& da, hipStre
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  kern<<<dim3(c.grid), dim3(NW * kWave), lds, stream>>>(da);
+  kern<<<dim3(grid), dim3(NW * kWave), lds, stream>>>(da);
   return hipGetLastError();
 }
 
 template <bool A64, int OUT, int RB, int NW, int P>
-hipError_t launch_decode_reg_t(const DecodeCfg& c, const DecodeArgs& da, hipStream_t stream) {
-  k_decode_reg<A64, OUT, RB, NW, P><<<dim3(c.grid), dim3(NW * kWave), 0, stream>>>(da);
+hipError_t launch_decode_reg_t(const DecodeCfg& c, DecodeArgs da, hipStream_t stream) {
+  (void)c;
+  const int grid = set_units(da, 16 * RB);
+  k_decode_reg<A64, OUT, RB, NW, P><<<dim3(grid), dim3(NW * kWave), 0, stream>>>(da);
   return hipGetLastError();
 }
 
@@ -503,19 +575,21 @@ constexpr int kDotWaves = 4;   // waves per workgroup
 
 template <int OUT, int R, int Q>
 __global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da) {
-  const int N = da.N, K = da.K;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * kDotWaves + wave;   // the wave's index over all projections
+  if (unit >= da.first[da.G]) return;               // wave-uniform
+  const DecodeView view = decode_view(da, unit);
+  const int N = view.N, K = da.K;
   const int npieces = K / 64;
-  const int n0 = (blockIdx.x * kDotWaves + wave) * R;
-  if (n0 >= N) return;   // wave-uniform
+  const int n0 = view.unit * R;
 
   // Weights first (the long-latency stream), then activations and the
   // epilogue inputs.
   uint4 wq[R][Q];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint8_t* row = da.Wp + (int64_t)min(n0 + r, N - 1) * (K / 4);
+    const uint8_t* row = view.Wp + (int64_t)min(n0 + r, N - 1) * (K / 4);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int p = lane + kWave * q;
@@ -533,7 +607,7 @@ __global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da)
       xa[q][4 * v + 0] = a.x; xa[q][4 * v + 1] = a.y; xa[q][4 * v + 2] = a.z; xa[q][4 * v + 3] = a.w;
     }
   }
-  const float gamma = da.gamma[0];
+  const float gamma = view.gamma[0];
   const int32_t sx = da.xsum[0];
   const float sc = da.xs[0];
 #pragma unroll
@@ -563,12 +637,12 @@ __global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da)
     acc = wave_sum_i32(acc);
     if (lane == r) mine = acc;
   }
-  if (lane < R && n0 + lane < N) store_out<OUT>(da.Y, n0 + lane, mine - sx, gamma, sc);
+  if (lane < R && n0 + lane < N) store_out<OUT>(view.Y, n0 + lane, mine - sx, gamma, sc);
 }
 
 template <int OUT, int R, int Q>
-hipError_t launch_decode_dot_t(const DecodeArgs& da, hipStream_t stream) {
-  const int waves = (da.N + R - 1) / R;
+hipError_t launch_decode_dot_t(DecodeArgs da, hipStream_t stream) {
+  const int waves = set_units(da, R);
   const int grid = (waves + kDotWaves - 1) / kDotWaves;
   k_decode_dot<OUT, R, Q><<<dim3(grid), dim3(kDotWaves * kWave), 0, stream>>>(da);
   return hipGetLastError();
@@ -1065,18 +1139,20 @@ hipError_t launch_gemm(const GemmCfg& c, GemmArgs ga, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Decode (M <= 16) over every projection of `da` in one launch.
+template <bool A64, int OUT>
+hipError_t decode_grouped(const DecodeArgs& da, hipStream_t stream) {
+  // One token and rows of at most 64 pieces (one per lane): the vector-ALU
+  // kernel, 2 rows per wave (timed 5-7 % faster than the matrix kernel on
+  // the 3B and 7B single-token shapes).
+  if (da.M == 1 && A64 && da.K <= 64 * 64) return launch_decode_dot_t<OUT, 2, 1>(da, stream);
+  return launch_decode<A64, OUT>(decode_cfg(da.M, decode_rows(da), da.K, false), da, stream);
+}
+
 template <bool A64, int OUT>
 hipError_t dispatch(const uint8_t* Wp, const float* gamma, int N, int K, const int8_t* Xq,
                     const float* xs, const int32_t* xsum, int M, void* Y, void* workspace,
                     hipStream_t stream) {
-  if (M <= 16) {
-    DecodeArgs da{Wp, gamma, N, K, M, Xq, xs, xsum, nullptr, nullptr, nullptr, nullptr, Y};
-    // One token and rows of at most 64 pieces (one per lane): the vector-ALU
-    // kernel, 2 rows per wave (timed 5-7 % faster than the matrix kernel on
-    // the 3B and 7B single-token shapes).
-    if (M == 1 && A64 && K <= 64 * 64) return launch_decode_dot_t<OUT, 2, 1>(da, stream);
-    return launch_decode<A64, OUT>(decode_cfg(M, N, K, false), da, stream);
-  }
   // 2: bf16 rows through LDS with 16-byte stores; 1: 4-wide stores; 0: scalar.
   const uintptr_t ya = reinterpret_cast<uintptr_t>(Y);
   int vec_out = (N % 4 == 0) && (ya % (OUT == kOutBF16 ? 8 : 16) == 0);
@@ -1102,21 +1178,76 @@ size_t forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return gemm_workspace_bytes(gemm_cfg((int)M, (int)N, (int)K), M, N);
 }
 
+size_t forward_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K) {
+  size_t need = 0;
+  for (int g = 0; g < G; ++g) need = std::max(need, forward_workspace_bytes(M, N[g], K));
+  return need;
+}
+
+namespace {
+DecodeArgs decode_args_group(int G, const uint8_t* const* Wp, const float* const* gamma,
+                             const int64_t* N, int K, int M, void* const* Y) {
+  DecodeArgs da{};
+  for (int g = 0; g < G; ++g) {
+    da.Wp[g] = Wp[g];
+    da.gamma[g] = gamma[g];
+    da.Ng[g] = (int)N[g];
+    da.Y[g] = Y[g];
+  }
+  da.G = G;
+  da.K = K;
+  da.M = M;
+  return da;
+}
+
+template <int OUT>
+hipError_t forward_grouped_out(int G, const uint8_t* const* Wp, const float* const* gamma,
+                               const int64_t* N, int K, const int8_t* Xq, const float* xs,
+                               const int32_t* xsum, int M, void* const* Y, void* workspace,
+                               hipStream_t stream) {
+  if (M <= 16) {
+    DecodeArgs da = decode_args_group(G, Wp, gamma, N, K, M, Y);
+    da.Xq = Xq;
+    da.xs = xs;
+    da.xsum = xsum;
+    return K % 64 == 0 ? decode_grouped<true, OUT>(da, stream)
+                       : decode_grouped<false, OUT>(da, stream);
+  }
+  // GEMM shapes: one projection after another (the workspace is reused in
+  // stream order).
+  for (int g = 0; g < G; ++g) {
+    const hipError_t e = dispatch_out<OUT>(Wp[g], gamma[g], (int)N[g], K, Xq, xs, xsum, M, Y[g],
+                                           workspace, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_forward_grouped(int G, const uint8_t* const* W_packed,
+                                  const float* const* gamma, const int64_t* N, int64_t K,
+                                  const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
+                                  int64_t M, void* const* Y, int y_dtype, void* workspace,
+                                  hipStream_t stream) {
+  const int k = (int)K, m = (int)M;
+  switch (y_dtype) {
+    case kOutF32:
+      return forward_grouped_out<kOutF32>(G, W_packed, gamma, N, k, X_q, x_scale, x_sum, m, Y,
+                                          workspace, stream);
+    case kOutBF16:
+      return forward_grouped_out<kOutBF16>(G, W_packed, gamma, N, k, X_q, x_scale, x_sum, m, Y,
+                                           workspace, stream);
+    default:
+      return forward_grouped_out<kOutI32>(G, W_packed, gamma, N, k, X_q, x_scale, x_sum, m, Y,
+                                          workspace, stream);
+  }
+}
+
 hipError_t launch_forward(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
                           const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
                           int64_t M, void* Y, int y_dtype, void* workspace, hipStream_t stream) {
-  const int n = (int)N, k = (int)K, m = (int)M;
-  switch (y_dtype) {
-    case kOutF32:
-      return dispatch_out<kOutF32>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, workspace,
-                                   stream);
-    case kOutBF16:
-      return dispatch_out<kOutBF16>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, workspace,
-                                    stream);
-    default:
-      return dispatch_out<kOutI32>(W_packed, gamma, n, k, X_q, x_scale, x_sum, m, Y, workspace,
-                                   stream);
-  }
+  return launch_forward_grouped(1, &W_packed, &gamma, &N, K, X_q, x_scale, x_sum, M, &Y, y_dtype,
+                                workspace, stream);
 }
 
 }  // namespace bl
@@ -1129,9 +1260,23 @@ inline size_t quant_region_bytes(int64_t M, int64_t K) {
   return (size_t)(((M * K + 255) / 256) * 256 + ((8 * M + 255) / 256) * 256);
 }
 
+// The fused launch for a decode group, or none (kind < 0).
+inline DecodeCfg fused_cfg(int64_t M, int G, const int64_t* N, int64_t K) {
+  DecodeCfg c{};
+  c.am = -1;
+  if (M > 16) return c;
+  int rows = 0;
+  for (int g = 0; g < G; ++g) rows += 16 * (int)((N[g] + 15) / 16);
+  return decode_cfg((int)M, rows, (int)K, true);
+}
+
+size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K) {
+  if (fused_cfg(M, G, N, K).am == kAFuse) return 0;
+  return quant_region_bytes(M, K) + forward_grouped_workspace_bytes(M, G, N, K);
+}
+
 size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16 && decode_cfg((int)M, (int)N, (int)K, true).am == kAFuse) return 0;
-  return quant_region_bytes(M, K) + forward_workspace_bytes(M, N, K);
+  return forward_f32_grouped_workspace_bytes(M, 1, &N, K);
 }
 
 namespace {
@@ -1142,25 +1287,26 @@ hipError_t fused_out(const DecodeCfg& c, const DecodeArgs& da, hipStream_t strea
 }
 }  // namespace
 
-hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
-                              const float* X, int64_t M, void* Y, int y_dtype, int8_t* X_q_out,
-                              float* x_scale_out, int32_t* x_sum_out, void* workspace,
-                              hipStream_t stream) {
-  const int n = (int)N, k = (int)K, m = (int)M;
-  if (M <= 16) {
-    const DecodeCfg c = decode_cfg(m, n, k, true);
-    if (c.am == kAFuse) {
-      DecodeArgs da{W_packed, gamma, n, k, m, nullptr, nullptr, nullptr, X,
-                    X_q_out, x_scale_out, x_sum_out, Y};
-      switch (y_dtype) {
-        case kOutF32: return fused_out<kOutF32>(c, da, stream);
-        case kOutBF16: return fused_out<kOutBF16>(c, da, stream);
-        default: return fused_out<kOutI32>(c, da, stream);
-      }
+hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
+                                      const float* const* gamma, const int64_t* N, int64_t K,
+                                      const float* X, int64_t M, void* const* Y, int y_dtype,
+                                      int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
+                                      void* workspace, hipStream_t stream) {
+  const DecodeCfg c = fused_cfg(M, G, N, K);
+  if (c.am == kAFuse) {
+    DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);
+    da.X = X;
+    da.Xq_out = X_q_out;
+    da.xs_out = x_scale_out;
+    da.xsum_out = x_sum_out;
+    switch (y_dtype) {
+      case kOutF32: return fused_out<kOutF32>(c, da, stream);
+      case kOutBF16: return fused_out<kOutBF16>(c, da, stream);
+      default: return fused_out<kOutI32>(c, da, stream);
     }
   }
-  // Two launches: quantise into the caller's output buffers (or the
-  // workspace), then the projection.
+  // Two launches: quantise once into the caller's output buffers (or the
+  // workspace), then every projection.
   int8_t* xq = X_q_out;
   float* xs = x_scale_out;
   int32_t* xsum = x_sum_out;
@@ -1170,12 +1316,21 @@ hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64
     xs = reinterpret_cast<float*>(w + ((M * K + 255) / 256) * 256);
     xsum = reinterpret_cast<int32_t*>(xs + M);
   }
-  // The projection's workspace follows the quantiser region (present in the
+  // The projections' workspace follows the quantiser region (present in the
   // size query in both cases).
   void* fws = w ? w + quant_region_bytes(M, K) : nullptr;
   hipError_t e = launch_quant(X, M, K, xq, xs, xsum, stream);
   if (e != hipSuccess) return e;
-  return launch_forward(W_packed, gamma, N, K, xq, xs, xsum, M, Y, y_dtype, fws, stream);
+  return launch_forward_grouped(G, W_packed, gamma, N, K, xq, xs, xsum, M, Y, y_dtype, fws,
+                                stream);
+}
+
+hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
+                              const float* X, int64_t M, void* Y, int y_dtype, int8_t* X_q_out,
+                              float* x_scale_out, int32_t* x_sum_out, void* workspace,
+                              hipStream_t stream) {
+  return launch_forward_f32_grouped(1, &W_packed, &gamma, &N, K, X, M, &Y, y_dtype, X_q_out,
+                                    x_scale_out, x_sum_out, workspace, stream);
 }
 
 }  // namespace bl

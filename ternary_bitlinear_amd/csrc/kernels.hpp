@@ -27,6 +27,23 @@ hipError_t launch_forward(const uint8_t* W_packed, const float* gamma, int64_t N
                           const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
                           int64_t M, void* Y, int y_dtype, void* workspace, hipStream_t stream);
 
+// Several projections of one activation matrix (G <= 4; W_packed, gamma, N
+// and Y are host arrays of G entries): decode shapes run as one launch over
+// all of them, GEMM shapes one projection after another.
+size_t forward_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K);
+hipError_t launch_forward_grouped(int G, const uint8_t* const* W_packed,
+                                  const float* const* gamma, const int64_t* N, int64_t K,
+                                  const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
+                                  int64_t M, void* const* Y, int y_dtype, void* workspace,
+                                  hipStream_t stream);
+size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K);
+hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
+                                      const float* const* gamma, const int64_t* N, int64_t K,
+                                      const float* X, int64_t M, void* const* Y, int y_dtype,
+                                      int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
+                                      void* workspace, hipStream_t stream);
+constexpr int kMaxGroupProjections = 4;
+
 // Quantisation fused with the projection (fp32 activations in).  Optional
 // X_q_out / x_scale_out / x_sum_out receive the quantiser's outputs (all or
 // none).  Unfused shapes use `workspace`: the quantiser region (used only

@@ -126,3 +126,28 @@ def test_binding_raises_on_cpu_tensors():
     import ternary_bitlinear_amd as tb
     with pytest.raises(TypeError):
         tb.bitlinear_quant_acts(torch.zeros(2, 16))
+
+
+def test_grouped_validation_without_gpu_calls(lib):
+    import ctypes
+    ptrs = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    ns = (ctypes.c_int64 * 3)(4096, 1024, 1024)
+    def call(G=3, W=ptrs, g=ptrs, N=ns, K=4096, M=1, Y=ptrs, dt=1, ws=None, wsb=0):
+        return lib.bitlinear_forward_grouped(G, W, g, N, K, FAKE, FAKE, FAKE, M, Y, dt, ws, wsb, None)
+    assert call(G=0) == 2 and call(G=5) == 2
+    assert call(W=None) == 1 and call(Y=None) == 1
+    bad = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    assert call(W=bad) == 1
+    bad = (ctypes.c_void_p * 3)(FAKE, FAKE + 4, FAKE)
+    assert call(W=bad) == 3
+    assert call(N=(ctypes.c_int64 * 3)(4096, 0, 1024)) == 2
+    assert call(K=40) == 2 and call(dt=9) == 4
+    # decode shapes need no workspace; a split GEMM group needs the largest member's
+    assert lib.bitlinear_forward_grouped_workspace_bytes(1, 3, ns, 4096) == 0
+    big = lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 4096)
+    assert big == max(lib.bitlinear_forward_workspace_bytes(64, n, 4096) for n in (4096, 1024, 1024))
+    assert big > 0 and call(M=64) == 7
+    assert lib.bitlinear_forward_grouped_workspace_bytes(1, 5, ns, 4096) == 0
+    f32 = lib.bitlinear_forward_f32_grouped(3, ptrs, ptrs, ns, 4096, None, 1, ptrs, 1,
+                                            None, None, None, None, 0, None)
+    assert f32 == 1

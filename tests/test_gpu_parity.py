@@ -4,6 +4,8 @@ Bit-exact: gamma, packed bytes, X~, x_scale, x_sum and the int32 accumulators.
 Within tolerance: Y (1e-5 relative for fp32 out, 1e-2 for bf16), with outputs
 of a zero accumulator exactly zero.
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -353,3 +355,69 @@ def test_forward_f32_fused(gpu_lib, M, N, K, with_outputs):
     for out in ("f32", "bf16"):
         Y = gpu_lib.bitlinear_forward_f32(P, g, Xd, N=N, y_dtype=out, **outs)
         check_y(Y, r["y"], out)
+
+
+# --------------------------------------------------------------------------- grouped
+GROUP_CASES = [
+    # (M, K, Ns): one token on the vector ALU, LDS-staged decode, a K that is
+    # not a multiple of 64, register-fed decode (X~ beyond the LDS budget),
+    # and GEMM shapes run one projection after another (K split on some)
+    (1, 4096, (4096, 1024, 1024)),
+    (3, 4096, (4096, 1024, 1024)),
+    (16, 1040, (300, 17, 64, 129)),
+    (16, 8192, (2048, 1040)),
+    (40, 4096, (512, 200)),
+    (130, 1040, (300, 64)),
+]
+
+
+@pytest.mark.parametrize("M,K,Ns", GROUP_CASES, ids=[f"M{m}K{k}G{len(n)}" for m, k, n in GROUP_CASES])
+def test_forward_grouped(gpu_lib, M, K, Ns):
+    """Every projection of the group: exact accumulators (oracle), and the same
+    output bytes as its own bitlinear_forward call."""
+    import torch
+    X = make_acts(0, f"test/grp/X{M}x{K}", M, K, {})
+    rs = [O.bitlinear(make_weight(0, f"test/grp/W{i}_{n}x{K}", n, K, 0.02), X)
+          for i, n in enumerate(Ns)]
+    Wp = [dev(r["packed"]) for r in rs]
+    gm = [dev(np.array([r["gamma"]], np.float32)) for r in rs]
+    xq, xs, xsum = dev(rs[0]["Xq"]), dev(rs[0]["x_scale"]), dev(rs[0]["x_sum"].astype(np.int32))
+    acc = gpu_lib.bitlinear_forward_grouped(Wp, gm, xq, xs, xsum, K=K, y_dtype="i32")
+    Yb = gpu_lib.bitlinear_forward_grouped(Wp, gm, xq, xs, xsum, K=K, y_dtype="bf16")
+    torch.cuda.synchronize()
+    for g, r in enumerate(rs):
+        assert_equal(host(acc[g]).astype(np.int64), r["acc"], f"accumulators of projection {g}")
+        check_y(Yb[g], r["y"], "bf16")
+        single = gpu_lib.bitlinear_forward(Wp[g], gm[g], xq, xs, xsum, N=Ns[g], K=K, y_dtype="bf16")
+        torch.cuda.synchronize()
+        assert torch.equal(single, Yb[g]), f"projection {g} differs from its own call"
+
+
+@pytest.mark.parametrize("with_outputs", [True, False], ids=["outs", "noouts"])
+@pytest.mark.parametrize("M,K,Ns", [(1, 4096, (1024, 512, 512)), (2, 3200, (8640, 64)),
+                                    (5, 1040, (300, 17)), (48, 4096, (200, 64))],
+                         ids=["fusedM1", "twoM2", "smallM5", "gemmM48"])
+def test_forward_f32_grouped(gpu_lib, M, K, Ns, with_outputs):
+    """Quantise once, then every projection: the quantiser outputs and each
+    projection's accumulators as the oracle's."""
+    import torch
+    X = make_acts(0, f"test/grpf/X{M}x{K}", M, K, {"outlier_frac": Fraction(1, 100), "outlier_scale": 50.0})
+    rs = [O.bitlinear(make_weight(0, f"test/grpf/W{i}_{n}x{K}", n, K, 0.02), X)
+          for i, n in enumerate(Ns)]
+    Wp = [dev(r["packed"]) for r in rs]
+    gm = [dev(np.array([r["gamma"]], np.float32)) for r in rs]
+    kw = {}
+    if with_outputs:
+        kw = dict(X_q_out=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                  x_scale_out=torch.empty(M, dtype=torch.float32, device="cuda"),
+                  x_sum_out=torch.empty(M, dtype=torch.int32, device="cuda"))
+    acc = gpu_lib.bitlinear_forward_f32_grouped(Wp, gm, dev(X), y_dtype="i32", **kw)
+    Y = gpu_lib.bitlinear_forward_f32_grouped(Wp, gm, dev(X), y_dtype="f32")
+    torch.cuda.synchronize()
+    for g, r in enumerate(rs):
+        assert_equal(host(acc[g]).astype(np.int64), r["acc"], f"accumulators of projection {g}")
+        check_y(Y[g], r["y"], "f32")
+    if with_outputs:
+        assert_equal(host(kw["X_q_out"]), rs[0]["Xq"], "X~")
+        assert_equal(f32_bits(host(kw["x_scale_out"])), f32_bits(rs[0]["x_scale"]), "x_scale bits")
+        assert_equal(host(kw["x_sum_out"]).astype(np.int64), rs[0]["x_sum"], "x_sum")
