@@ -121,6 +121,12 @@ def main():
                           xs=torch.empty(M, dtype=torch.int32, device=dev),
                           Y=torch.empty((M, p.N), dtype=getattr(torch, {"f32": "float32", "bf16": "bfloat16"}[out]),
                                         device=dev)))
+    grouped = wl.shared_input
+    if grouped:
+        # every projection reads one X (and, after quantisation, one X~)
+        for q in projs[1:]:
+            for key in ("X", "Xq", "s", "xs"):
+                q[key] = projs[0][key]
     wbytes_step = sum(q["p"].N * q["p"].K // 4 for q in projs)
     # every projection alone cycles through >= ROTATE_BYTES of copies
     copies = max(1, math.ceil(ROTATE_BYTES / min(q["p"].N * q["p"].K // 4 for q in projs)))
@@ -132,16 +138,28 @@ def main():
         need = tb.forward_f32_workspace_bytes(M, q["p"].N, q["p"].K)
         q["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         q["fused"] = need == 0
+    Ns = [q["p"].N for q in projs]
+    g_need = tb.forward_f32_grouped_workspace_bytes(M, Ns, projs[0]["p"].K) if grouped else 0
+    ws_group = torch.empty(max(g_need, 16), dtype=torch.uint8, device=dev)
 
     if args.traffic_probe:
-        traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl)
+        traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped)
         return
 
-    def step(r):
+    def step_separate(r):
         # quantise + project; one launch when the shape fuses, else two
         for q in projs:
             tb.bitlinear_forward_f32(q["Wc"][r % copies], q["g"], q["X"], N=q["p"].N,
                                      y_dtype=out, Y=q["Y"], workspace=q["ws"], stream=stream)
+
+    def step_grouped(r):
+        # quantise once, then every projection in one launch (decode shapes)
+        tb.bitlinear_forward_f32_grouped([q["Wc"][r % copies] for q in projs],
+                                         [q["g"] for q in projs], projs[0]["X"], Ns=Ns,
+                                         y_dtype=out, Y=[q["Y"] for q in projs],
+                                         workspace=ws_group, stream=stream)
+
+    step = step_grouped if grouped else step_separate
 
     def graph_of(fn_list):
         g = torch.cuda.CUDAGraph()
@@ -207,7 +225,7 @@ def main():
     with torch.cuda.stream(stream):
         for q in projs:
             tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
-    roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream)
+    roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream, grouped)
     dom = max(projs, key=lambda q: q["p"].N * q["p"].K)
     P = dom["p"]
 
@@ -252,6 +270,16 @@ def main():
                                (2 * M * P.N * P.K / t_fwd / 1e12) if prefill
                                else f32_bytes / t_fwd / 1e9, 2 if prefill else 1)}
 
+    if grouped:
+        # the same step as one call per projection, for comparison
+        g_sep = graph_of([lambda r=r: step_separate(r) for r in range(cycle)])
+        g_sep.replay()
+        t_sep = timer(g_sep.replay, max(1, 2000 // cycle)) / (max(1, 2000 // cycle) * cycle)
+        rows["step_separate_calls"] = {"us": round(t_sep * 1e6, 3),
+                                       "note": "one bitlinear_forward_f32 per projection"}
+        rows["step_grouped"] = {"us": round(ms_per_step * 1e3, 3),
+                                "note": "one bitlinear_forward_f32_grouped"}
+
     # ---------------- CPU oracle on a bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
@@ -281,23 +309,39 @@ def kernel_family(M):
     return "k_decode" if M <= 16 else "k_gemm"
 
 
-def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream):
-    """Average launch of bitlinear_forward over the workload's projections,
-    timed with HIP events on the launch stream around a graph of back-to-back
-    launches over the rotated weight copies."""
+def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream, grouped=False):
+    """Average launch of bitlinear_forward over the workload's projections (or
+    of one bitlinear_forward_grouped over all of them, when they share their
+    input), timed with HIP events on the launch stream around a graph of
+    back-to-back launches over the rotated weight copies."""
     def fwd_all(r):
+        if grouped:
+            tb.bitlinear_forward_grouped([q["Wc"][r % copies] for q in projs],
+                                         [q["g"] for q in projs], projs[0]["Xq"], projs[0]["s"],
+                                         projs[0]["xs"], Ns=[q["p"].N for q in projs],
+                                         K=projs[0]["p"].K, y_dtype=out, Y=[q["Y"] for q in projs],
+                                         stream=stream)
+            return
         for q in projs:
             tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
                                  N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
     g = graph_of([lambda r=r: fwd_all(r) for r in range(copies)])
     g.replay()
-    launches_per_replay = copies * len(projs)
+    per_replay = 1 if grouped else len(projs)
+    launches_per_replay = copies * per_replay
     reps = max(1, (4000 if not prefill else 200) // launches_per_replay)
     t_all = timer(g.replay, reps)
     n_launch = reps * launches_per_replay
     t_launch = t_all / n_launch
-    bytes_launch = sum(alg_bytes(q["p"], M, out) for q in projs) / len(projs)
-    ops_launch = sum(2 * M * q["p"].N * q["p"].K for q in projs) / len(projs)
+    if grouped:
+        # one launch: every matrix and output, the shared X~ once
+        K = projs[0]["p"].K
+        bytes_launch = (sum(alg_bytes(q["p"], M, out) for q in projs)
+                        - (len(projs) - 1) * (M * K + 8 * M))
+        ops_launch = sum(2 * M * q["p"].N * q["p"].K for q in projs)
+    else:
+        bytes_launch = sum(alg_bytes(q["p"], M, out) for q in projs) / len(projs)
+        ops_launch = sum(2 * M * q["p"].N * q["p"].K for q in projs) / len(projs)
     if prefill:
         achieved = ops_launch / t_launch / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
@@ -313,16 +357,20 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream)
         "us_per_launch": round(t_launch * 1e6, 3), "launches_timed": n_launch,
         "algorithmic_bytes_per_launch": int(bytes_launch),
         "ops_per_launch": int(ops_launch),
+        "grouped": grouped,
         "timing": "HIP events on the launch stream around a graph of back-to-back "
-                  "bitlinear_forward launches (every projection, rotated weight copies)"})
+                  + ("bitlinear_forward_grouped launches (all projections in one, "
+                     if grouped else "bitlinear_forward launches (every projection, ")
+                  + "rotated weight copies)"})
     return roof, t_launch
 
 CAL_BYTES = 256 << 20        # the calibration copy reads and writes this many bytes
 
 
-def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl):
+def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=False):
     """One elementwise copy of CAL_BYTES (torch.neg on int32: reads and writes
-    CAL_BYTES), then bitlinear_forward once per projection and weight copy."""
+    CAL_BYTES), then bitlinear_forward once per projection and weight copy (or
+    bitlinear_forward_grouped once per weight copy)."""
     src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -333,6 +381,14 @@ def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl):
         for q in projs:
             tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
         for r in range(copies):
+            if grouped:
+                tb.bitlinear_forward_grouped([q["Wc"][r % copies] for q in projs],
+                                             [q["g"] for q in projs], projs[0]["Xq"],
+                                             projs[0]["s"], projs[0]["xs"],
+                                             Ns=[q["p"].N for q in projs], K=projs[0]["p"].K,
+                                             y_dtype=out, Y=[q["Y"] for q in projs],
+                                             stream=stream)
+                continue
             for q in projs:
                 tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
                                      N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
@@ -388,7 +444,11 @@ def traffic_from(args):
                      "kernel_kib_per_dispatch": round(kib, 2), "dispatches": len(ker),
                      "reduce_dispatches": len(red),
                      "bytes_per_launch": kib * 1024.0 * factor}
-    alg = sum(alg_bytes(P, M, wl.out_dtype) for P in shapes) / len(shapes)
+    if wl.shared_input:   # one grouped launch: every matrix and output, X~ once
+        alg = (sum(alg_bytes(P, M, wl.out_dtype) for P in shapes)
+               - (len(shapes) - 1) * (M * shapes[0].K + 8 * M))
+    else:
+        alg = sum(alg_bytes(P, M, wl.out_dtype) for P in shapes) / len(shapes)
     total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
     ent = {"bytes_per_launch": int(total), "algorithmic_bytes_per_launch": int(alg),
            "ratio_to_algorithmic": round(total / alg, 4),

@@ -31,14 +31,15 @@ class Workload:
     x_recipe: dict = field(default_factory=dict)
     out_dtype: str = "bf16"  # "f32" or "bf16"
     seed: int = 0
+    shared_input: bool = False   # every projection reads the same X (q/k/v, gate/up)
 
     def weight(self, proj: Projection) -> np.ndarray:
         return make_weight(self.seed, f"{self.name}/{proj.name}/W", proj.N, proj.K,
                            self.w_sigma)
 
     def acts(self, proj: Projection, M: int) -> np.ndarray:
-        return make_acts(self.seed, f"{self.name}/{proj.name}/X/M{M}", M, proj.K,
-                         self.x_recipe)
+        tag = "shared" if self.shared_input else proj.name
+        return make_acts(self.seed, f"{self.name}/{tag}/X/M{M}", M, proj.K, self.x_recipe)
 
 
 WORKLOADS = {
@@ -69,6 +70,18 @@ WORKLOADS = {
             tokens=(1, 8, 32, 64),
             w_sigma=0.02,
             x_recipe={"outlier_frac": Fraction(1, 200), "outlier_scale": 100.0},
+        ),
+        Workload(
+            name="attn-qkv-7b",
+            description="query, key and value projections of one 7B attention block, 3 x "
+                        "(4096->4096) reading the same X; M in {1,8,16}; 0.5% channels x100; "
+                        "bf16 out",
+            projections=(Projection("q", 4096, 4096), Projection("k", 4096, 4096),
+                         Projection("v", 4096, 4096)),
+            tokens=(1, 8, 16),
+            w_sigma=0.02,
+            x_recipe={"outlier_frac": Fraction(1, 200), "outlier_scale": 100.0},
+            shared_input=True,
         ),
         Workload(
             name="prefill-7b",

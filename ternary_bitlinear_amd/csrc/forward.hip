@@ -160,17 +160,22 @@ struct DecodeView {
   int unit;
 };
 
+// Branch-free: every entry is read at once and picked by selects, so the
+// (scalar) argument loads issue together instead of as a chain of
+// load-wait-branch steps ahead of the first weight load.
 __device__ __forceinline__ DecodeView decode_view(const DecodeArgs& da, int unit) {
-  DecodeView v{da.Wp[0], da.gamma[0], da.Ng[0], da.Y[0], unit};
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) g += (i < da.G && unit >= da.first[i]) ? 1 : 0;
+  DecodeView v{da.Wp[0], da.gamma[0], da.Ng[0], da.Y[0], unit - da.first[0]};
 #pragma unroll
   for (int i = 1; i < kMaxGroup; ++i) {
-    if (i < da.G && unit >= da.first[i]) {
-      v.Wp = da.Wp[i];
-      v.gamma = da.gamma[i];
-      v.N = da.Ng[i];
-      v.Y = da.Y[i];
-      v.unit = unit - da.first[i];
-    }
+    const bool pick = g == i;
+    v.Wp = pick ? da.Wp[i] : v.Wp;
+    v.gamma = pick ? da.gamma[i] : v.gamma;
+    v.N = pick ? da.Ng[i] : v.N;
+    v.Y = pick ? da.Y[i] : v.Y;
+    v.unit = pick ? unit - da.first[i] : v.unit;
   }
   return v;
 }
@@ -578,10 +583,12 @@ __global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * kDotWaves + wave;   // the wave's index over all projections
-  if (unit >= da.first[da.G]) return;               // wave-uniform
   const DecodeView view = decode_view(da, unit);
   const int N = view.N, K = da.K;
   const int npieces = K / 64;
+  // A wave past the last projection's rows (at most kDotWaves - 1 of them)
+  // reads that projection's last row and stores nothing; no early exit, so
+  // the argument loads issue as one batch.
   const int n0 = view.unit * R;
 
   // Weights first (the long-latency stream), then activations and the
@@ -610,6 +617,11 @@ __global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da)
   const float gamma = view.gamma[0];
   const int32_t sx = da.xsum[0];
   const float sc = da.xs[0];
+  void* const yout = view.Y;
+  // Keep the epilogue's scalar inputs here, under the weight stream's
+  // latency, instead of letting them sink behind the reduction into the
+  // store branch as a chain of dependent scalar loads.
+  asm volatile("" ::"s"(gamma), "s"(sx), "s"(sc), "s"(yout));
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     if (lane + kWave * q >= npieces) {
@@ -637,7 +649,7 @@ __global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da)
     acc = wave_sum_i32(acc);
     if (lane == r) mine = acc;
   }
-  if (lane < R && n0 + lane < N) store_out<OUT>(view.Y, n0 + lane, mine - sx, gamma, sc);
+  if (lane < R && n0 + lane < N) store_out<OUT>(yout, n0 + lane, mine - sx, gamma, sc);
 }
 
 template <int OUT, int R, int Q>
