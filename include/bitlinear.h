@@ -178,9 +178,10 @@ size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Computes exactly bitlinear_quant_acts followed by bitlinear_forward (same
  * X~, same x_scale, same x_sum, same accumulators; page section 2, absmax
  * activation quantiser and the linear transformation), as one launch for
- * decode shapes (M <= 8 tokens whose int8 rows fit the on-chip staging;
- * every workgroup quantises the activations it needs), else as those two
- * launches.  This is the quantiser folded into the projection's prologue.
+ * decode shapes (one token with K a multiple of 64 up to 12288, or M <= 8
+ * tokens whose int8 rows fit the on-chip staging; every workgroup quantises
+ * the activations it needs), else as those two launches.  This is the
+ * quantiser folded into the projection's prologue.
  *
  * X        [M][K] fp32, device, 16-byte aligned (read only).
  * Y        [M][N], device, as in bitlinear_forward.

@@ -572,61 +572,193 @@ hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t s
 // activations per piece are loaded once into registers and serve all R
 // rows.  Codes expand to int8 in registers as in the matrix kernels and
 // multiply with v_dot4_i32_i8 (four products per instruction); a wave
-// shuffle sums each row.  No LDS and no barrier: at one token the matrix
-// instruction would compute 16 columns to keep one.  Lanes past a row's end
-// re-read its first piece and multiply it by zeroed activations.
+// shuffle sums each row.  At one token the matrix instruction would compute
+// 16 columns to keep one.  Lanes past a row's end re-read its first piece and
+// multiply it by zeroed activations.
+//
+// FUSE (fp32 input) quantises the token inside the kernel,
+// with the same per-element arithmetic as the standalone quantiser (absmax on
+// bit patterns, one correctly rounded divide, one multiply and the exact
+// round-half-up per element):
+//   kDotFuseWave  (Q = 1) every wave quantises the whole row itself: lane l
+//                 holds the 64 fp32 activations of piece l; wave reductions
+//                 only, no LDS and no barrier, but the row's conversion is
+//                 repeated per wave (measured slower than the next mode).
+//   kDotFuseBlock the WV waves of a workgroup convert the row once: each thread
+//                 takes every (64 WV)-th group of four, the absmax and the code
+//                 sum go through LDS (two barriers), and each lane then reads
+//                 its piece's codes from LDS.
+// In both, the weight loads are issued before the quantiser's chain starts,
+// and wave 0 of workgroup 0 may also write X~, x_scale and x_sum out.
 // ---------------------------------------------------------------------------
-constexpr int kDotWaves = 4;   // waves per workgroup
+constexpr int kDotFuseNone = 0, kDotFuseWave = 1, kDotFuseBlock = 2;
+constexpr int kDotWaves = 4;   // waves per workgroup without block fusion
 
-template <int OUT, int R, int Q>
-__global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da) {
+template <int OUT, int R, int Q, int FUSE, int WV>
+__global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
+  static_assert(FUSE != kDotFuseWave || Q == 1, "the per-wave prologue holds one piece per lane");
+  constexpr int kFuseK4 = 64 * 64 / 4 * Q;                   // groups of four at K = 4096 Q
+  constexpr int kJ = FUSE == kDotFuseBlock ? kFuseK4 / (WV * kWave) : 1;   // groups per thread
+  __shared__ uint32_t s_codes[FUSE == kDotFuseBlock ? kFuseK4 : 1];
+  __shared__ uint32_t s_red[2][WV];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kDotWaves + wave;   // the wave's index over all projections
+  const int unit = blockIdx.x * WV + wave;   // the wave's index over all projections
   const DecodeView view = decode_view(da, unit);
   const int N = view.N, K = da.K;
   const int npieces = K / 64;
-  // A wave past the last projection's rows (at most kDotWaves - 1 of them)
-  // reads that projection's last row and stores nothing; no early exit, so
-  // the argument loads issue as one batch.
+  // A wave past the last projection's rows (fewer than WV of them) reads
+  // that projection's last row and stores nothing; no early exit, so the
+  // argument loads issue as one batch (and every wave reaches the barriers).
   const int n0 = view.unit * R;
 
-  // Weights first (the long-latency stream), then activations and the
-  // epilogue inputs.
   uint4 wq[R][Q];
+  auto load_weights = [&]() {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint8_t* row = view.Wp + (int64_t)min(n0 + r, N - 1) * (K / 4);
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* row = view.Wp + (int64_t)min(n0 + r, N - 1) * (K / 4);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int p = lane + kWave * q;
+        wq[r][q] = *reinterpret_cast<const uint4*>(row + 16 * (p < npieces ? p : 0));
+      }
+    }
+  };
+  // Unfused: weights first (the long-latency stream), then the activations.
+  // Fused: the fp32 activations first, then the weights, then the
+  // quantiser's chain (reduce, convert, reduce).  Loads complete in issue
+  // order, so activations requested after the weights could not be used
+  // before the weights had arrived; the scheduling barriers keep the
+  // compiler from sinking the weight loads below the chain.
+  if constexpr (FUSE == kDotFuseNone) load_weights();
+  int32_t xa[Q][16];
+  const float gamma = view.gamma[0];
+  void* const yout = view.Y;
+  int32_t sx;
+  float sc;
+  if constexpr (FUSE == kDotFuseWave) {
+    const bool live = lane < npieces;
+    const float4* src = reinterpret_cast<const float4*>(da.X) + 16 * (live ? lane : 0);
+    float4 xv[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) xv[d] = src[d];
+    __builtin_amdgcn_sched_barrier(0);
+    load_weights();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(gamma), "s"(yout));
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) lmax = max(lmax, absmax4(xv[d]));
+    lmax = wave_max_u32(live ? lmax : 0u);
+    const float beta = __uint_as_float(lmax);
+    const float inv = 127.0f / (beta + 1e-5f);
+    int32_t lsum = 0;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) xa[0][d] = (int32_t)quant4(xv[d], inv, lsum);
+    if (!live) {
+      lsum = 0;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) xa[0][d] = 0;
+    }
+    sx = wave_sum_i32(lsum);
+    sc = beta / 127.0f;
+    if (unit == 0 && da.Xq_out != nullptr) {
+      if (live) {
+        i32x4* dst = reinterpret_cast<i32x4*>(da.Xq_out + 64 * lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          dst[v] = i32x4{xa[0][4 * v + 0], xa[0][4 * v + 1], xa[0][4 * v + 2], xa[0][4 * v + 3]};
+      }
+      if (lane == 0) {
+        da.xs_out[0] = sc;
+        da.xsum_out[0] = sx;
+      }
+    }
+  } else if constexpr (FUSE == kDotFuseBlock) {
+    const int K4 = K / 4;
+    const float4* src = reinterpret_cast<const float4*>(da.X);
+    float4 xv[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int i = threadIdx.x + WV * kWave * j;
+      xv[j] = src[i < K4 ? i : 0];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_weights();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(gamma), "s"(yout));
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (threadIdx.x + WV * kWave * j < K4) lmax = max(lmax, absmax4(xv[j]));
+    lmax = wave_max_u32(lmax);
+    if (lane == 0) s_red[0][wave] = lmax;
+    __syncthreads();
+    uint32_t bmax = s_red[0][0];
+#pragma unroll
+    for (int w = 1; w < WV; ++w) bmax = max(bmax, s_red[0][w]);
+    const float beta = __uint_as_float(bmax);
+    const float inv = 127.0f / (beta + 1e-5f);
+    const bool write_out = blockIdx.x == 0 && da.Xq_out != nullptr;
+    int32_t lsum = 0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int i = threadIdx.x + WV * kWave * j;
+      if (i < K4) {
+        const uint32_t c = quant4(xv[j], inv, lsum);
+        s_codes[i] = c;
+        if (write_out) reinterpret_cast<uint32_t*>(da.Xq_out)[i] = c;
+      }
+    }
+    lsum = wave_sum_i32(lsum);
+    if (lane == 0) s_red[1][wave] = (uint32_t)lsum;
+    __syncthreads();
+    int32_t tsum = 0;
+#pragma unroll
+    for (int w = 0; w < WV; ++w) tsum += (int32_t)s_red[1][w];
+    sx = tsum;
+    sc = beta / 127.0f;
+    if (write_out && threadIdx.x == 0) {
+      da.xs_out[0] = sc;
+      da.xsum_out[0] = sx;
+    }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int p = lane + kWave * q;
-      wq[r][q] = *reinterpret_cast<const uint4*>(row + 16 * (p < npieces ? p : 0));
+      const i32x4* lp = reinterpret_cast<const i32x4*>(s_codes) + 4 * (p < npieces ? p : 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const i32x4 a = lp[v];
+        xa[q][4 * v + 0] = a.x; xa[q][4 * v + 1] = a.y; xa[q][4 * v + 2] = a.z; xa[q][4 * v + 3] = a.w;
+      }
+      if (p >= npieces) {
+#pragma unroll
+        for (int d = 0; d < 16; ++d) xa[q][d] = 0;
+      }
     }
-  }
-  int32_t xa[Q][16];
+  } else {
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int p = lane + kWave * q;
-    const i32x4* src = reinterpret_cast<const i32x4*>(da.Xq + 64 * (p < npieces ? p : 0));
+    for (int q = 0; q < Q; ++q) {
+      const int p = lane + kWave * q;
+      const i32x4* src = reinterpret_cast<const i32x4*>(da.Xq + 64 * (p < npieces ? p : 0));
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const i32x4 a = src[v];
-      xa[q][4 * v + 0] = a.x; xa[q][4 * v + 1] = a.y; xa[q][4 * v + 2] = a.z; xa[q][4 * v + 3] = a.w;
+      for (int v = 0; v < 4; ++v) {
+        const i32x4 a = src[v];
+        xa[q][4 * v + 0] = a.x; xa[q][4 * v + 1] = a.y; xa[q][4 * v + 2] = a.z; xa[q][4 * v + 3] = a.w;
+      }
     }
-  }
-  const float gamma = view.gamma[0];
-  const int32_t sx = da.xsum[0];
-  const float sc = da.xs[0];
-  void* const yout = view.Y;
-  // Keep the epilogue's scalar inputs here, under the weight stream's
-  // latency, instead of letting them sink behind the reduction into the
-  // store branch as a chain of dependent scalar loads.
-  asm volatile("" ::"s"(gamma), "s"(sx), "s"(sc), "s"(yout));
+    sx = da.xsum[0];
+    sc = da.xs[0];
+    // Keep the epilogue's scalar inputs here, under the weight stream's
+    // latency, instead of letting them sink behind the reduction into the
+    // store branch as a chain of dependent scalar loads.
+    asm volatile("" ::"s"(gamma), "s"(sx), "s"(sc), "s"(yout));
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    if (lane + kWave * q >= npieces) {
+    for (int q = 0; q < Q; ++q) {
+      if (lane + kWave * q >= npieces) {
 #pragma unroll
-      for (int d = 0; d < 16; ++d) xa[q][d] = 0;
+        for (int d = 0; d < 16; ++d) xa[q][d] = 0;
+      }
     }
   }
 
@@ -652,11 +784,11 @@ __global__ __launch_bounds__(kDotWaves * kWave) void k_decode_dot(DecodeArgs da)
   if (lane < R && n0 + lane < N) store_out<OUT>(yout, n0 + lane, mine - sx, gamma, sc);
 }
 
-template <int OUT, int R, int Q>
+template <int OUT, int R, int Q, int FUSE = kDotFuseNone, int WV = kDotWaves>
 hipError_t launch_decode_dot_t(DecodeArgs da, hipStream_t stream) {
   const int waves = set_units(da, R);
-  const int grid = (waves + kDotWaves - 1) / kDotWaves;
-  k_decode_dot<OUT, R, Q><<<dim3(grid), dim3(kDotWaves * kWave), 0, stream>>>(da);
+  const int grid = (waves + WV - 1) / WV;
+  k_decode_dot<OUT, R, Q, FUSE, WV><<<dim3(grid), dim3(WV * kWave), 0, stream>>>(da);
   return hipGetLastError();
 }
 
@@ -1282,8 +1414,28 @@ inline DecodeCfg fused_cfg(int64_t M, int G, const int64_t* N, int64_t K) {
   return decode_cfg((int)M, rows, (int)K, true);
 }
 
+// One token with K <= 12288 (a multiple of 64): the vector-ALU decode
+// quantises in place (the workgroup converts the row once into LDS), one
+// launch and no workspace; Q = ceil(K / 4096) pieces per lane.
+constexpr int kDotFuseRows = 4;   // rows per wave in that mode
+constexpr int kDotFuseWaves = 4;  // waves per workgroup in that mode
+constexpr int kDotFuseMaxQ = 3;
+inline bool fused_dot(int64_t M, int64_t K) {
+  return M == 1 && K % 64 == 0 && K <= 64 * 64 * kDotFuseMaxQ;
+}
+
+namespace {
+template <int OUT>
+hipError_t fused_dot_out(const DecodeArgs& da, hipStream_t stream) {
+  const int q = (da.K + 64 * 64 - 1) / (64 * 64);
+  if (q <= 1) return launch_decode_dot_t<OUT, kDotFuseRows, 1, kDotFuseBlock, kDotFuseWaves>(da, stream);
+  if (q == 2) return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, kDotFuseWaves>(da, stream);
+  return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves>(da, stream);
+}
+}  // namespace
+
 size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K) {
-  if (fused_cfg(M, G, N, K).am == kAFuse) return 0;
+  if (fused_dot(M, K) || fused_cfg(M, G, N, K).am == kAFuse) return 0;
   return quant_region_bytes(M, K) + forward_grouped_workspace_bytes(M, G, N, K);
 }
 
@@ -1304,6 +1456,18 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
                                       const float* X, int64_t M, void* const* Y, int y_dtype,
                                       int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
                                       void* workspace, hipStream_t stream) {
+  if (fused_dot(M, K)) {
+    DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);
+    da.X = X;
+    da.Xq_out = X_q_out;
+    da.xs_out = x_scale_out;
+    da.xsum_out = x_sum_out;
+    switch (y_dtype) {
+      case kOutF32: return fused_dot_out<kOutF32>(da, stream);
+      case kOutBF16: return fused_dot_out<kOutBF16>(da, stream);
+      default: return fused_dot_out<kOutI32>(da, stream);
+    }
+  }
   const DecodeCfg c = fused_cfg(M, G, N, K);
   if (c.am == kAFuse) {
     DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);

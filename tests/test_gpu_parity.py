@@ -319,6 +319,10 @@ def test_workload_full_size(gpu_lib, wname, pname):
 FUSED_SHAPES = [
     (1, 1, 16), (1, 40, 80), (2, 33, 1040), (3, 300, 4096), (5, 129, 512), (8, 64, 2048),
     (1, 8640, 3200), (1, 3200, 8640), (1, 64, 28672), (4, 100, 8192),
+    # one token, K <= 4096 in steps of 64: quantised inside the vector-ALU decode
+    # (row counts that leave a workgroup, and a wave, partly past the end)
+    (1, 1, 64), (1, 3, 128), (1, 1001, 192), (1, 4096, 4096), (1, 11008, 4096),
+    (1, 5, 4160), (1, 77, 8192), (1, 4096, 11008), (1, 33, 12288), (1, 9, 12352),
     # outside the fused kernel's reach: two launches
     (9, 77, 1040), (16, 300, 4096), (8, 64, 8640), (40, 130, 1024), (2, 50, 40960),
     # two launches with K split across workgroups (workspace needed either way)
@@ -363,6 +367,8 @@ GROUP_CASES = [
     # not a multiple of 64, register-fed decode (X~ beyond the LDS budget),
     # and GEMM shapes run one projection after another (K split on some)
     (1, 4096, (4096, 1024, 1024)),
+    (1, 8640, (3200, 3200)),
+    (1, 192, (5, 17, 1, 64)),
     (3, 4096, (4096, 1024, 1024)),
     (16, 1040, (300, 17, 64, 129)),
     (16, 8192, (2048, 1040)),
