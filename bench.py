@@ -18,7 +18,10 @@ overhead does not hide the device time.
 
 Prints one JSON line: the whole-step throughput ("value"), the roofline of the
 dominant kernel, the CPU oracle timed on a bounded sample, and one entry per
-step of the path.
+step of the path.  The dominant kernel is the step's own launch where the step
+is nothing but fused launches (decode shapes), else the projection on
+pre-quantised activations (bitlinear_forward), which is also reported as a row
+in both cases.
 """
 from __future__ import annotations
 
@@ -142,10 +145,6 @@ def main():
     g_need = tb.forward_f32_grouped_workspace_bytes(M, Ns, projs[0]["p"].K) if grouped else 0
     ws_group = torch.empty(max(g_need, 16), dtype=torch.uint8, device=dev)
 
-    if args.traffic_probe:
-        traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped)
-        return
-
     def step_separate(r):
         # quantise + project; one launch when the shape fuses, else two
         for q in projs:
@@ -160,6 +159,12 @@ def main():
                                          workspace=ws_group, stream=stream)
 
     step = step_grouped if grouped else step_separate
+    fused_step = step_is_fused(tb, [q["p"] for q in projs], M, grouped)
+
+    if args.traffic_probe:
+        traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped,
+                      step if fused_step else None)
+        return
 
     def graph_of(fn_list):
         g = torch.cuda.CUDAGraph()
@@ -219,13 +224,20 @@ def main():
     else:
         value, unit = wbytes_step / (elapsed / args.steps) / 1e9, "GB/s"
 
-    # ---------------- the dominant kernel: the projection (bitlinear_forward on
-    # pre-quantised activations) on every projection of the workload, back to
-    # back over the rotated weight copies
+    # ---------------- the dominant kernel.  The projection on pre-quantised
+    # activations (bitlinear_forward) over every projection of the workload,
+    # back to back over the rotated weight copies; when the step is nothing but
+    # fused launches (decode shapes), the step's own launch is the dominant
+    # kernel and is timed the same way.
     with torch.cuda.stream(stream):
         for q in projs:
             tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
-    roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream, grouped)
+    proj_roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
+                            grouped)
+    roof = proj_roof
+    if fused_step:
+        roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
+                           grouped, fused_step=step)
     dom = max(projs, key=lambda q: q["p"].N * q["p"].K)
     P = dom["p"]
 
@@ -260,8 +272,9 @@ def main():
     rows["quant_acts"] = {"shape": f"M{M} K{q0['p'].K}", "us": round(t_q * 1e6, 3),
                           "GB/s": round(q_bytes / t_q / 1e9, 1)}
     rows["forward" + ("_gemm" if M > 16 else "_decode")] = {
-        "shape": roof["shape"], "us": roof["us_per_launch"],
-        ("TOP/s" if prefill else "GB/s"): roof["achieved"],
+        "shape": proj_roof["shape"], "us": proj_roof["us_per_launch"],
+        ("TOP/s" if prefill else "GB/s"): proj_roof["achieved"],
+        "entry_point": proj_roof["entry_point"],
         "epilogue": f"gamma*beta rescale fused, {out} out"}
     f32_bytes = P.N * P.K // 4 + 4 * M * P.K + OUT_BYTES[out] * M * P.N + 4
     rows["forward_f32"] = {"shape": f"M{M} {P.K}->{P.N}", "us": round(t_fwd * 1e6, 3),
@@ -305,16 +318,51 @@ def alg_bytes(P, M, out):
     return P.N * P.K // 4 + M * P.K + 8 * M + OUT_BYTES[out] * M * P.N + 4
 
 
+def alg_bytes_f32(P, M, out):
+    """Algorithmic bytes of one fused launch (quantiser in the prologue):
+    packed W, fp32 X, Y, gamma."""
+    return P.N * P.K // 4 + 4 * M * P.K + OUT_BYTES[out] * M * P.N + 4
+
+
+def launch_alg_bytes(shapes, M, out, fused, grouped):
+    """Algorithmic bytes per launch of the dominant kernel: one grouped launch
+    reads the shared activations once; separate launches are averaged."""
+    f = alg_bytes_f32 if fused else alg_bytes
+    shared = 4 * M * shapes[0].K if fused else M * shapes[0].K + 8 * M
+    if grouped:
+        return sum(f(P, M, out) for P in shapes) - (len(shapes) - 1) * shared
+    return sum(f(P, M, out) for P in shapes) / len(shapes)
+
+
+def step_is_fused(tb, shapes, M, grouped):
+    """True when every launch of the step is the fused projection (no
+    separate quantiser launch): its workspace query is then 0."""
+    if M > 16:
+        return False
+    if grouped:
+        return tb.forward_f32_grouped_workspace_bytes(M, [P.N for P in shapes], shapes[0].K) == 0
+    return all(tb.forward_f32_workspace_bytes(M, P.N, P.K) == 0 for P in shapes)
+
+
 def kernel_family(M):
     return "k_decode" if M <= 16 else "k_gemm"
 
 
-def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream, grouped=False):
-    """Average launch of bitlinear_forward over the workload's projections (or
-    of one bitlinear_forward_grouped over all of them, when they share their
-    input), timed with HIP events on the launch stream around a graph of
-    back-to-back launches over the rotated weight copies."""
+def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream, grouped=False,
+             fused_step=None):
+    """Average launch of the dominant kernel, timed with HIP events on the
+    launch stream around a graph of back-to-back launches over the rotated
+    weight copies.  With fused_step (the step's own function, every launch of
+    which is one fused bitlinear_forward_f32[_grouped]) that kernel is the
+    step's; otherwise it is bitlinear_forward (or one bitlinear_forward_grouped
+    over all projections, when they share their input) on pre-quantised
+    activations."""
+    fused = fused_step is not None
+
     def fwd_all(r):
+        if fused:
+            fused_step(r)
+            return
         if grouped:
             tb.bitlinear_forward_grouped([q["Wc"][r % copies] for q in projs],
                                          [q["g"] for q in projs], projs[0]["Xq"], projs[0]["s"],
@@ -333,15 +381,9 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
     t_all = timer(g.replay, reps)
     n_launch = reps * launches_per_replay
     t_launch = t_all / n_launch
-    if grouped:
-        # one launch: every matrix and output, the shared X~ once
-        K = projs[0]["p"].K
-        bytes_launch = (sum(alg_bytes(q["p"], M, out) for q in projs)
-                        - (len(projs) - 1) * (M * K + 8 * M))
-        ops_launch = sum(2 * M * q["p"].N * q["p"].K for q in projs)
-    else:
-        bytes_launch = sum(alg_bytes(q["p"], M, out) for q in projs) / len(projs)
-        ops_launch = sum(2 * M * q["p"].N * q["p"].K for q in projs) / len(projs)
+    shapes = [q["p"] for q in projs]
+    bytes_launch = launch_alg_bytes(shapes, M, out, fused, grouped)
+    ops_launch = sum(2 * M * P.N * P.K for P in shapes) / (1 if grouped else len(shapes))
     if prefill:
         achieved = ops_launch / t_launch / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
@@ -350,27 +392,31 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
         achieved = bytes_launch / t_launch / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    shapes = ", ".join(f"{q['p'].K}->{q['p'].N}" for q in projs)
+    api = ("bitlinear_forward_f32" if fused else "bitlinear_forward") + ("_grouped" if grouped else "")
     roof.update({
-        "traffic": load_traffic(kernel_family(M), projs, M, out, bytes_launch),
-        "kernel": kernel_family(M), "shape": f"M{M} {shapes}",
+        "traffic": load_traffic(kernel_family(M), projs, M, out, fused),
+        "kernel": kernel_family(M), "entry_point": api,
+        "shape": f"M{M} " + ", ".join(f"{P.K}->{P.N}" for P in shapes),
         "us_per_launch": round(t_launch * 1e6, 3), "launches_timed": n_launch,
         "algorithmic_bytes_per_launch": int(bytes_launch),
         "ops_per_launch": int(ops_launch),
-        "grouped": grouped,
-        "timing": "HIP events on the launch stream around a graph of back-to-back "
-                  + ("bitlinear_forward_grouped launches (all projections in one, "
-                     if grouped else "bitlinear_forward launches (every projection, ")
+        "grouped": grouped, "fused_quantiser": fused,
+        "timing": f"HIP events on the launch stream around a graph of back-to-back {api} "
+                  + ("launches (all projections in one, " if grouped
+                     else "launches (every projection, ")
                   + "rotated weight copies)"})
     return roof, t_launch
+
 
 CAL_BYTES = 256 << 20        # the calibration copy reads and writes this many bytes
 
 
-def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=False):
+def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=False,
+                  fused_step=None):
     """One elementwise copy of CAL_BYTES (torch.neg on int32: reads and writes
-    CAL_BYTES), then bitlinear_forward once per projection and weight copy (or
-    bitlinear_forward_grouped once per weight copy)."""
+    CAL_BYTES), then the dominant kernel once per weight copy: the step's own
+    fused launches when it has nothing else (fused_step), else bitlinear_forward
+    once per projection (or bitlinear_forward_grouped once)."""
     src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -378,9 +424,13 @@ def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=Fal
     torch.cuda.synchronize()
     del src, dst
     with torch.cuda.stream(stream):
-        for q in projs:
-            tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
+        if fused_step is None:
+            for q in projs:
+                tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
         for r in range(copies):
+            if fused_step is not None:
+                fused_step(r)
+                continue
             if grouped:
                 tb.bitlinear_forward_grouped([q["Wc"][r % copies] for q in projs],
                                              [q["g"] for q in projs], projs[0]["Xq"],
@@ -393,9 +443,10 @@ def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=Fal
                 tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
                                      N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": traffic_key(kernel_family(M), [q["p"] for q in projs], M, out),
+    print(json.dumps({"traffic_probe": traffic_key(kernel_family(M), [q["p"] for q in projs], M,
+                                                   out, fused_step is not None),
                       "workload": wl.name, "calibration_bytes": CAL_BYTES,
-                      "launches": copies * len(projs)}), flush=True)
+                      "launches": copies * (1 if grouped else len(projs))}), flush=True)
 
 
 def _counters(d, name):
@@ -426,7 +477,10 @@ def traffic_from(args):
     M = args.tokens or wl.tokens[0]
     fam = kernel_family(M)
     shapes = list(wl.projections)
-    key = traffic_key(fam, shapes, M, wl.out_dtype)
+    import ternary_bitlinear_amd as tb   # size queries only: no GPU
+    tb.load()
+    fused = step_is_fused(tb, shapes, M, wl.shared_input)
+    key = traffic_key(fam, shapes, M, wl.out_dtype, fused)
     out = {}
     for what, d, cname in (("fetch", args.traffic_from[0], "FETCH_SIZE"),
                            ("write", args.traffic_from[1], "WRITE_SIZE")):
@@ -444,11 +498,7 @@ def traffic_from(args):
                      "kernel_kib_per_dispatch": round(kib, 2), "dispatches": len(ker),
                      "reduce_dispatches": len(red),
                      "bytes_per_launch": kib * 1024.0 * factor}
-    if wl.shared_input:   # one grouped launch: every matrix and output, X~ once
-        alg = (sum(alg_bytes(P, M, wl.out_dtype) for P in shapes)
-               - (len(shapes) - 1) * (M * shapes[0].K + 8 * M))
-    else:
-        alg = sum(alg_bytes(P, M, wl.out_dtype) for P in shapes) / len(shapes)
+    alg = launch_alg_bytes(shapes, M, wl.out_dtype, fused, wl.shared_input)
     total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
     ent = {"bytes_per_launch": int(total), "algorithmic_bytes_per_launch": int(alg),
            "ratio_to_algorithmic": round(total / alg, 4),
@@ -463,18 +513,21 @@ def traffic_from(args):
         with open(path) as f:
             data = json.load(f)
     data.setdefault("entries", {})[key] = ent
-    data["note"] = ("HBM bytes per launch of bitlinear_forward's kernel: rocprofv3 FETCH_SIZE "
-                    "and WRITE_SIZE (KiB per dispatch), each scaled by CAL_BYTES / the same "
-                    "counter on one torch.neg copy of CAL_BYTES int32 bytes in the same run.")
+    data["note"] = ("HBM bytes per launch of the dominant kernel (bitlinear_forward's, or the "
+                    "fused bitlinear_forward_f32's where the key says f32-fused): rocprofv3 "
+                    "FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by CAL_BYTES / "
+                    "the same counter on one torch.neg copy of CAL_BYTES int32 bytes in the "
+                    "same run.")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
     print(json.dumps({key: ent}))
 
 
-def traffic_key(kernel, shapes, M, out):
+def traffic_key(kernel, shapes, M, out, fused=False):
     """shapes: the workload's projections (objects with K and N)."""
-    return f"{kernel} M{M} " + ",".join(f"{P.K}->{P.N}" for P in shapes) + f" {out}"
+    return (f"{kernel}{' f32-fused' if fused else ''} M{M} "
+            + ",".join(f"{P.K}->{P.N}" for P in shapes) + f" {out}")
 
 
 def forward_source_digest():
@@ -483,7 +536,7 @@ def forward_source_digest():
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(kernel, projs, M, out, bytes_launch):
+def load_traffic(kernel, projs, M, out, fused=False):
     """HBM bytes per launch (read + written) from profiles/traffic.json, when the
     counters there were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -491,7 +544,7 @@ def load_traffic(kernel, projs, M, out, bytes_launch):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get("entries", {}).get(traffic_key(kernel, [q["p"] for q in projs], M, out))
+    ent = data.get("entries", {}).get(traffic_key(kernel, [q["p"] for q in projs], M, out, fused))
     if not ent or ent.get("source_sha256_16") != forward_source_digest():
         return None
     return ent.get("bytes_per_launch")
