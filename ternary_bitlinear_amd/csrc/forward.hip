@@ -871,19 +871,99 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until this wave's LDS reads are done (lgkmcnt 0; other counters free).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+// One stage's fragments in registers: the lane's code words and its
+// activation rows for the four 32-wide k sub-steps.
+template <int MB, int NB>
+struct GemmFrag {
+  i32x4 bw[NB];
+  i32x4 af[kGBK / 32][MB];
+};
+
+template <int BN, int MB, int NB>
+__device__ __forceinline__ void gemm_read(const int8_t* __restrict__ Ac,
+                                          const uint8_t* __restrict__ Bc, int a_row0, int b_row0,
+                                          int lane_sw, int g2, GemmFrag<MB, NB>& f) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    f.bw[nb] = *reinterpret_cast<const i32x4*>(Bc + g2 * BN * 16 + (b_row0 + nb * 32) * 16);
+#pragma unroll
+  for (int ks = 0; ks < kGBK / 32; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      f.af[ks][mb] = *reinterpret_cast<const i32x4*>(Ac + (a_row0 + mb * 32) * 128 +
+                                                     16 * ((4 * g2 + ks) ^ lane_sw));
+}
+
+template <int MB, int NB, int NA>
+__device__ __forceinline__ void gemm_mma(const GemmFrag<MB, NB>& f, i32x16 (&acc)[NA][MB][NB]);
+
+// One step with fragments read one stage ahead: issue the direct loads of a
+// later stage into (An, Bn), read the next stage's fragments from (Ar, Br)
+// into nxt, and run the matrix instructions on cur.  As in gemm_step, the
+// __restrict__ qualifiers let the compiler see that the stage being read is
+// not the one being filled, so it waits for no load in flight.
+template <int BN, int MB, int NB, int A_INS, int B_INS, int NA>
+__device__ __forceinline__ void gemm_step_pf(const int8_t* __restrict__ Ar,
+                                             const uint8_t* __restrict__ Br,
+                                             int8_t* __restrict__ An, uint8_t* __restrict__ Bn,
+                                             const int8_t* const (&asrc)[A_INS],
+                                             const uint8_t* const (&bsrc)[B_INS],
+                                             const int (&bblk)[B_INS], int k0n, int wave,
+                                             int a_row0, int b_row0, int lane_sw, int g2,
+                                             const GemmFrag<MB, NB>& cur, GemmFrag<MB, NB>& nxt,
+                                             i32x16 (&acc)[NA][MB][NB]) {
+#pragma unroll
+  for (int qi = 0; qi < A_INS; ++qi)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(asrc[qi] + k0n),
+                                     static_cast<void*>(An + (qi * 4 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int qi = 0; qi < B_INS; ++qi)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(bsrc[qi] + k0n / 4),
+                                     static_cast<void*>(Bn + bblk[qi] * 1024), 16, 0, 0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    nxt.bw[nb] = *reinterpret_cast<const i32x4*>(Br + g2 * BN * 16 + (b_row0 + nb * 32) * 16);
+#pragma unroll
+  for (int ks = 0; ks < kGBK / 32; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      nxt.af[ks][mb] = *reinterpret_cast<const i32x4*>(Ar + (a_row0 + mb * 32) * 128 +
+                                                       16 * ((4 * g2 + ks) ^ lane_sw));
+  gemm_mma<MB, NB, NA>(cur, acc);
+}
+
+template <int MB, int NB, int NA>
+__device__ __forceinline__ void gemm_mma(const GemmFrag<MB, NB>& f, i32x16 (&acc)[NA][MB][NB]) {
+#pragma unroll
+  for (int ks = 0; ks < kGBK / 32; ++ks) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const i32x4 bf = expand_codes((uint32_t)f.bw[nb][ks]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[ks % NA][mb][nb] = mfma_i8_32x32x32(bf, f.af[ks][mb], acc[ks % NA][mb][nb]);
+    }
+  }
+}
+
 // One pipeline step: issue the direct loads of a later stage into (An, Bn)
 // and run the matrix instructions on the current stage (Ac, Bc).  The
 // __restrict__ qualifiers tell the compiler the two stages are disjoint, so it
 // need not wait for the loads in flight before reading the current stage, and
 // it schedules the fragment reads itself.
-template <int BN, int MB, int NB, int A_INS, int B_INS>
+template <int BN, int MB, int NB, int A_INS, int B_INS, int NA>
 __device__ __forceinline__ void gemm_step(const int8_t* __restrict__ Ac, const uint8_t* __restrict__ Bc,
                                           int8_t* __restrict__ An, uint8_t* __restrict__ Bn,
                                           bool do_issue, const int8_t* const (&asrc)[A_INS],
                                           const uint8_t* const (&bsrc)[B_INS],
                                           const int (&bblk)[B_INS], int k0n, int wave,
                                           int a_row0, int b_row0, int lane_sw, int g2,
-                                          i32x16 (&acc)[MB][NB]) {
+                                          i32x16 (&acc)[NA][MB][NB]) {
   if (do_issue) {
 #pragma unroll
     for (int qi = 0; qi < A_INS; ++qi)
@@ -906,23 +986,29 @@ __device__ __forceinline__ void gemm_step(const int8_t* __restrict__ Ac, const u
     for (int mb = 0; mb < MB; ++mb)
       af[ks][mb] = *reinterpret_cast<const i32x4*>(Ac + (a_row0 + mb * 32) * 128 +
                                                     16 * ((4 * g2 + ks) ^ lane_sw));
+  // Sub-step ks accumulates into set ks % NA: with few blocks per wave the
+  // matrix instructions of a step would otherwise form one dependent chain.
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const i32x4 bf = expand_codes((uint32_t)bw[nb][ks]);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma_i8_32x32x32(bf, af[ks][mb], acc[mb][nb]);
+      for (int mb = 0; mb < MB; ++mb)
+        acc[ks % NA][mb][nb] = mfma_i8_32x32x32(bf, af[ks][mb], acc[ks % NA][mb][nb]);
     }
   }
 }
 
-template <bool kAligned64, int OUT, int BM, int BN, int WM, int WN, int NS>
+template <bool kAligned64, int OUT, int BM, int BN, int WM, int WN, int NS, bool PF>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   static_assert(WM * WN == kGemmThreads / kWave, "4 waves");
   static_assert(NS >= 2 && NS <= 8, "ring depth");
   constexpr int MB = BM / WM / 32, NB = BN / WN / 32;   // 32x32 blocks per wave
   static_assert(MB >= 1 && NB >= 1 && BN % 64 == 0, "tile");
+  // Independent accumulator sets (added exactly at the end): at least four
+  // independent matrix-instruction chains per wave.
+  constexpr int NA = MB * NB >= 4 ? 1 : 4 / (MB * NB);
   constexpr int A_INS = BM / 8 / 4;            // 1 KB direct loads per wave per stage (8 rows each)
   constexpr int B_BLK = BN / 32;               // 1 KB blocks of codes per stage (64 chunks each)
   constexpr int B_INS = (B_BLK + 3) / 4;       // per wave
@@ -1009,13 +1095,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
                                        static_cast<void*>(B + bblk[qi] * 1024), 16, 0, 0);
   };
 
-  i32x16 acc[MB][NB];
+  i32x16 acc_sets[NA][MB][NB];
 #pragma unroll
-  for (int a = 0; a < MB; ++a)
+  for (int h = 0; h < NA; ++h)
 #pragma unroll
-    for (int c = 0; c < NB; ++c)
+    for (int a = 0; a < MB; ++a)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][c][e] = 0;
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc_sets[h][a][c][e] = 0;
 
   // This lane's token rows in the epilogue; their sums and scales are read
   // now so the loads are long done by then.
@@ -1043,6 +1131,41 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   // its own.
   constexpr int NLD = A_INS + B_INS;
   const int nkf = min(per_split, nk_all - kb);   // full steps of this item
+  if constexpr (PF) {
+    // Fragments one step ahead in registers.  At step st the fragments of
+    // stage st are already in registers (read during step st - 1), so the
+    // matrix instructions of step st run while the LDS reads of stage
+    // st + 1 are in flight; with one workgroup per CU nothing else would
+    // hide that latency.  The ring is issued NS stages deep: before step st,
+    // stages up to st + NS - 1 are issued, stage st's buffer is released at
+    // the barrier of step st (after every wave's reads of it), and refilled
+    // with stage st + NS.
+    constexpr int U = NS % 2 == 0 ? NS : 2 * NS;   // stage and fragment indices static
+    GemmFrag<MB, NB> fr[2];
+    if (nkf > 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) issue(min(s, nkf - 1), sA[s], sB[s]);
+      wait_vmcnt<(NS - 1) * NLD>();
+      stage_barrier();
+      gemm_read<BN, MB, NB>(sA[0], sB[0], a_row0, b_row0, lane_sw, g2, fr[0]);
+    }
+    for (int kt = 0; kt < nkf; kt += U) {
+#pragma unroll
+      for (int s = 0; s < U; ++s) {
+        if (kt + s >= nkf) break;
+        // This wave's reads of stage st are done and its loads of stage
+        // st + 1 have landed; after the barrier the same holds for every
+        // wave, so stage st + 1 is complete and stage st's buffer is free.
+        wait_lgkm0();
+        wait_vmcnt<(NS - 2) * NLD>();
+        stage_barrier();
+        gemm_step_pf<BN, MB, NB, A_INS, B_INS, NA>(
+            sA[(s + 1) % NS], sB[(s + 1) % NS], sA[s % NS], sB[s % NS], asrc, bsrc, bblk,
+            min(kt + s + NS, nkf - 1) * kGBK, wave, a_row0, b_row0, lane_sw, g2, fr[s & 1],
+            fr[(s + 1) & 1], acc_sets);
+      }
+    }
+  } else {
   if (nkf > 0) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(min(s, nkf - 1), sA[s], sB[s]);
@@ -1058,11 +1181,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
       // refilled below) before the other waves' refills: every wave has
       // finished that step when it reaches this barrier.
       stage_barrier();
-      gemm_step<BN, MB, NB, A_INS, B_INS>(sA[s], sB[s], sA[(s + NS - 1) % NS],
-                                          sB[(s + NS - 1) % NS], true, asrc, bsrc, bblk,
-                                          min(kt + s + NS - 1, nkf - 1) * kGBK, wave, a_row0,
-                                          b_row0, lane_sw, g2, acc);
+      gemm_step<BN, MB, NB, A_INS, B_INS, NA>(sA[s], sB[s], sA[(s + NS - 1) % NS],
+                                              sB[(s + NS - 1) % NS], true, asrc, bsrc, bblk,
+                                              min(kt + s + NS - 1, nkf - 1) * kGBK, wave, a_row0,
+                                              b_row0, lane_sw, g2, acc_sets);
     }
+  }
   }
   // No direct load may still be writing LDS when the tail refills a stage or
   // the workgroup ends.
@@ -1088,9 +1212,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
       *reinterpret_cast<uint32_t*>(B + b_off<BN>(r, word)) = load_word(row, k0 / 16 + word, kw);
     }
     __syncthreads();
-    gemm_step<BN, MB, NB, A_INS, B_INS>(A, B, nullptr, nullptr, false, asrc, bsrc, bblk, 0, wave,
-                                        a_row0, b_row0, lane_sw, g2, acc);
+    gemm_step<BN, MB, NB, A_INS, B_INS, NA>(A, B, nullptr, nullptr, false, asrc, bsrc, bblk, 0,
+                                            wave, a_row0, b_row0, lane_sw, g2, acc_sets);
   }
+  i32x16 (&acc)[MB][NB] = acc_sets[0];
+#pragma unroll
+  for (int h = 1; h < NA; ++h)
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[a][c][e] += acc_sets[h][a][c][e];
 
   // Epilogue: lane (r32, g2), register 4 i + j of block (mb, nb) holds the
   // output of token m0 + (row block) + r32 and weight row
@@ -1198,6 +1331,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs ga) {
   }
 }
 
+constexpr int kMaxSplits = 4;   // K splits of one projection (gemm_cfg's maximum)
+
 // Sum of the K splits of every output, then the epilogue: thread i handles
 // outputs 4i .. 4i + 3 of the flattened [M][N] tile set when N % 4 == 0 (one
 // vector load per split), else one output.
@@ -1211,10 +1346,16 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs ga) {
     const int64_t e = 4 * i;
     if (e >= MN) return;
     const int m = (int)(e / N);
-    i32x4 v = *reinterpret_cast<const i32x4*>(ga.part + e);
-    for (int sp = 1; sp < S; ++sp) {
-      const i32x4 w = *reinterpret_cast<const i32x4*>(ga.part + sp * MN + e);
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    // Every split's partials are requested before any is added (S <= 4),
+    // so the loads overlap instead of following one another.
+    i32x4 w[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+      w[sp] = sp < S ? *reinterpret_cast<const i32x4*>(ga.part + sp * MN + e) : i32x4{0, 0, 0, 0};
+    i32x4 v = w[0];
+#pragma unroll
+    for (int sp = 1; sp < kMaxSplits; ++sp) {
+      v.x += w[sp].x; v.y += w[sp].y; v.z += w[sp].z; v.w += w[sp].w;
     }
     const int32_t sx = ga.xsum[m];
     v.x -= sx; v.y -= sx; v.z -= sx; v.w -= sx;
@@ -1227,8 +1368,12 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs ga) {
   } else {
     if (i >= MN) return;
     const int m = (int)(i / N);
+    int32_t w[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) w[sp] = sp < S ? ga.part[sp * MN + i] : 0;
     int32_t a = 0;
-    for (int sp = 0; sp < S; ++sp) a += ga.part[sp * MN + i];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) a += w[sp];
     store_out<OUT>(ga.Y, i, a - ga.xsum[m], gamma, ga.xs[m]);
   }
 }
@@ -1238,14 +1383,15 @@ struct GemmCfg {
   int splits;   // K splits (1: none)
 };
 
-template <bool A64, int OUT, int BM, int BN, int WM, int WN, int NS = 3>
+template <bool A64, int OUT, int BM, int BN, int WM, int WN, int NS = 3, bool PF = false>
 hipError_t launch_gemm_t(GemmArgs ga, hipStream_t stream) {
   ga.tiles_m = (ga.M + BM - 1) / BM;
   ga.tiles_n = (ga.N + BN - 1) / BN;
   if (ga.band <= 0 || ga.band > ga.tiles_n) ga.band = ga.tiles_n;
   if (ga.splits < 1) ga.splits = 1;
+  if (ga.splits > kMaxSplits) return hipErrorInvalidValue;   // the reduction adds at most that many
   const int items = ga.tiles_m * ga.tiles_n * ga.splits;
-  k_gemm<A64, OUT, BM, BN, WM, WN, NS><<<dim3(items), dim3(kGemmThreads), 0, stream>>>(ga);
+  k_gemm<A64, OUT, BM, BN, WM, WN, NS, PF><<<dim3(items), dim3(kGemmThreads), 0, stream>>>(ga);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ga.splits == 1) return e;
   const int64_t MN = (int64_t)ga.M * ga.N;
@@ -1265,7 +1411,7 @@ inline GemmCfg gemm_cfg(int M, int N, int K) {
   if (M <= 128) c = {64, 64, 1};
   const int tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
   const int nk = K / kGBK;
-  if (tiles <= 128) c.splits = max(1, min(4, min(nk / 4, K / (16 * M))));
+  if (tiles <= 128) c.splits = max(1, min(kMaxSplits, min(nk / 4, K / (16 * M))));
   return c;
 }
 
@@ -1279,7 +1425,10 @@ template <bool A64, int OUT>
 hipError_t launch_gemm(const GemmCfg& c, GemmArgs ga, hipStream_t stream) {
   ga.splits = c.splits;
   if (c.bm == 128 && c.bn == 128) return launch_gemm_t<A64, OUT, 128, 128, 2, 2, 3>(ga, stream);
-  if (c.bm == 64 && c.bn == 64) return launch_gemm_t<A64, OUT, 64, 64, 2, 2, 4>(ga, stream);
+  // 64 x 64 tiles run one workgroup per CU (a single wave per SIMD), so the
+  // fragment reads are pipelined a step ahead there (timed 5-7 % faster);
+  // at 128 x 128 two workgroups per CU already hide them.
+  if (c.bm == 64 && c.bn == 64) return launch_gemm_t<A64, OUT, 64, 64, 2, 2, 4, true>(ga, stream);
   return hipErrorInvalidValue;
 }
 
