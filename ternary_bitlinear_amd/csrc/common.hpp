@@ -45,17 +45,31 @@ __device__ __forceinline__ uint32_t absmax4(const float4& f) {
   return max(max(abs_bits(f.x), abs_bits(f.y)), max(abs_bits(f.z), abs_bits(f.w)));
 }
 
-// ---- wave reductions (all lanes receive the result) -------------------------
+// ---- wave reductions (all 64 lanes active; every lane receives the result) --
+// In the vector ALU with DPP, no round trip through the LDS crossbar: an
+// inclusive prefix within each row of 16 lanes (row_shr 1, 2, 4, 8), then the
+// last lane of a row carried into the next rows (row_bcast15 into rows 1 and
+// 3, row_bcast31 into rows 2 and 3), so lane 63 ends with the whole wave's
+// value and readlane makes it uniform.  Lanes shifted in from outside a row,
+// and rows outside a step's row mask, contribute 0: the identity of both
+// wrapping addition and unsigned max.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));   // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));   // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));   // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));   // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, true));   // row_bcast15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, true));   // row_bcast31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-  return v;
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
 __device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return (int32_t)wave_reduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
