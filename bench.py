@@ -263,14 +263,17 @@ def main():
     pk_bytes = q0["p"].N * q0["p"].K * 4 + q0["p"].N * q0["p"].K // 4
     rows["pack_weights"] = {"shape": f"{q0['p'].K}->{q0['p'].N}", "us": round(t_pack * 1e6, 2),
                             "GB/s": round(pk_bytes / t_pack / 1e9, 1),
-                            "note": "3 launches; reads W twice (exact sum, then codes)"}
+                            "frac_of_hbm": round(pk_bytes / t_pack / 1e9 / HBM_PEAK_GBS, 4),
+                            "note": "3 launches; reads W twice (exact sum, then codes); bytes "
+                                    "counted once: 4NK read + NK/4 written"}
     g_q = graph_of([lambda: tb.bitlinear_quant_acts(q0["X"], q0["Xq"], q0["s"], q0["xs"],
                                                      stream=stream)] * 50)
     g_q.replay()
     t_q = timer(g_q.replay, 10) / 500
     q_bytes = M * q0["p"].K * 5 + 8 * M
     rows["quant_acts"] = {"shape": f"M{M} K{q0['p'].K}", "us": round(t_q * 1e6, 3),
-                          "GB/s": round(q_bytes / t_q / 1e9, 1)}
+                          "GB/s": round(q_bytes / t_q / 1e9, 1),
+                          "frac_of_hbm": round(q_bytes / t_q / 1e9 / HBM_PEAK_GBS, 4)}
     rows["forward" + ("_gemm" if M > 16 else "_decode")] = {
         "shape": proj_roof["shape"], "us": proj_roof["us_per_launch"],
         ("TOP/s" if prefill else "GB/s"): proj_roof["achieved"],

@@ -27,6 +27,12 @@ reason in the design notes):
     per-tensor) and the symmetric range [-127, 127] (Q_b - 1 = 127).
   * The per-token reciprocal 127 / (absmax + eps) is formed in fp32 first and
     each element is multiplied by it (one fp32 multiply per element).
+  * RMS normalisation before the quantiser ([B158] section 2 names it and
+    cites Zhang and Sennrich's "Root Mean Square Layer Normalization"):
+    y_k = x_k / sqrt(mean_k x_k^2 + eps) * g_k with a gain vector g, no
+    centring, eps the quantisers' 1e-5 inside the root; the mean of squares is
+    exact and rounded once to fp32, then an fp32 add, a correctly rounded fp32
+    square root and reciprocal r, and per element fl32(fl32(x_k r) g_k).
 
 Every function here is pinned by the CPU tests (closed forms, brute force,
 invariants, a hand-derived worked example); none is "parity unpinned".
@@ -176,6 +182,47 @@ def unpack_codes(P: np.ndarray, K: int) -> np.ndarray:
     if (c == 3).any():
         raise ValueError("code 3 is not part of the format")
     return (c.reshape(N, K) - 1).astype(np.int8)
+
+
+# --------------------------------------------------------------------------
+# RMS normalisation of the activations (before the quantiser)
+# --------------------------------------------------------------------------
+def exact_sum_squares(X: np.ndarray) -> list:
+    """Per row, the exact sum of x_k^2 as a Fraction.
+
+    Every fp32 value is an integer multiple of 2^-149, so x = n 2^-149 with an
+    integer n and sum x^2 = (sum n^2) 2^-298: a Python-integer sum, exact.
+    """
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    out = []
+    for row in X:
+        m, e = np.frexp(row.astype(np.float64))          # row = m 2^e, 0.5 <= |m| < 1
+        ints = (m * 2.0 ** 24).astype(np.int64)          # exact: 24 significant bits
+        total = 0
+        for n, ee in zip(ints.tolist(), e.tolist()):
+            if n:
+                sh = ee - 24 + 149                       # x = n 2^(e-24) = v 2^-149
+                v = n << sh if sh >= 0 else n >> -sh     # exact: x is a multiple of 2^-149
+                total += v * v
+        out.append(Fraction(total, 1 << 298))
+    return out
+
+
+def rmsnorm(X: np.ndarray, g: np.ndarray):
+    """RMS-normalised activations ([B158] section 2; the normalisation of the
+    reference it cites), fp32 [M][K], and the per-token reciprocal r [M].
+
+    ms = fl32(exact mean of x^2);  d = fl32(sqrt(fl32(ms + eps)));  r = fl32(1 / d);
+    y_k = fl32(fl32(x_k r) g_k).
+    """
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    M, K = X.shape
+    ms = np.array([f32_nearest(s / K) for s in exact_sum_squares(X)], dtype=np.float32)
+    d = np.sqrt(ms + EPS)                                # fp32 add, correctly rounded fp32 sqrt
+    r = np.float32(1.0) / d                              # correctly rounded fp32 division
+    Y = (X * r[:, None]) * g[None, :]                    # two fp32 multiplies per element
+    return Y.astype(np.float32), r.astype(np.float32)
 
 
 # --------------------------------------------------------------------------

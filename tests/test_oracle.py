@@ -359,3 +359,74 @@ def test_worked_example_end_to_end():
     # codes route: sum c x~ - sum x~ with c = W~ + 1
     c = r["Wt"].astype(int) + 1
     assert (c @ r["Xq"][0].astype(int) - g["x_sum"][0]).tolist() == acc0
+
+
+# ---------------------------------------------------------------- RMS normalisation
+def test_sum_squares_bruteforce_fraction_tiny():
+    # Fraction(float) is the exact value of each element; squares and sums of
+    # Fractions are exact.  Includes subnormals and values near the fp32 max.
+    rng = np.random.default_rng(7)
+    rows = [np.array([1e-30, 3e38, -1.5e-45, 0.0, 2.8e-45, -1e-40], np.float32),
+            rng.standard_normal(37).astype(np.float32),
+            (rng.standard_normal(19) * 1e-20).astype(np.float32)]
+    for row in rows:
+        want = sum(Fraction(float(v)) ** 2 for v in row)
+        assert O.exact_sum_squares(row[None, :])[0] == want
+
+
+@pytest.mark.parametrize("c_exp", [4, 10, 20])
+def test_rmsnorm_power_of_two_rows_are_exact(c_exp):
+    # x = 2^c u with u_k = +-1: mean of squares 2^(2c) exactly; for 2^(2c) far
+    # above eps the fp32 add returns 2^(2c), the root is 2^c, r = 2^-c, so
+    # y = u g exactly (g a few powers of two).
+    rng = np.random.default_rng(c_exp)
+    K = 96
+    u = np.where(rng.random(K) < 0.5, -1.0, 1.0).astype(np.float32)
+    g = np.ldexp(np.ones(K), rng.integers(-3, 4, size=K)).astype(np.float32)
+    X = (np.float32(2.0 ** c_exp) * u)[None, :]
+    Y, r = O.rmsnorm(X, g)
+    assert r[0] == np.float32(2.0 ** -c_exp)
+    assert np.array_equal(Y[0], u * g)
+
+
+def test_rmsnorm_scale_invariance_by_powers_of_two():
+    # Multiplying a row by 2^j multiplies the mean of squares by 4^j exactly
+    # and, while eps stays below half an ulp of it, the root by 2^j: the
+    # output does not change.
+    rng = np.random.default_rng(3)
+    X = (rng.standard_normal((3, 200)) * 64).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(200)).astype(np.float32)
+    Y0, _ = O.rmsnorm(X, g)
+    for j in (1, 3, 7):
+        Yj, _ = O.rmsnorm(X * np.float32(2.0 ** j), g)
+        assert np.array_equal(Y0, Yj)
+
+
+def test_rmsnorm_matches_float64_formula():
+    # Textbook formula in float64: a dropped 1/K, a missing square root, a
+    # missing gain or eps outside the root would miss by far more than the few
+    # fp32 roundings allowed here.
+    rng = np.random.default_rng(5)
+    for K, scale in ((64, 1.0), (4096, 0.05), (1000, 3e-3)):
+        X = (rng.standard_normal((4, K)) * scale).astype(np.float32)
+        g = (1 + 0.2 * rng.standard_normal(K)).astype(np.float32)
+        Y, r = O.rmsnorm(X, g)
+        x64 = X.astype(np.float64)
+        d64 = np.sqrt((x64 * x64).mean(axis=1) + float(O.EPS))
+        y64 = x64 / d64[:, None] * g.astype(np.float64)[None, :]
+        assert np.allclose(Y, y64, rtol=4 * 2.0 ** -23, atol=0)
+        assert np.allclose(r, 1 / d64, rtol=2 * 2.0 ** -23, atol=0)
+
+
+def test_rmsnorm_zero_row_and_quantiser_after_it():
+    K = 128
+    g = np.ones(K, np.float32)
+    Y, r = O.rmsnorm(np.zeros((1, K), np.float32), g)
+    assert not Y.any() and np.isfinite(r).all()                # 0 / sqrt(eps) = 0
+    # after the norm, the element of largest |x g| maps to +-127
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((3, K)).astype(np.float32)
+    Yn, _ = O.rmsnorm(X, g)
+    Xq, _, _, _ = O.quantize_activations(Yn)
+    idx = np.abs(X).argmax(axis=1)
+    assert (np.abs(Xq[np.arange(3), idx]) == 127).all()
