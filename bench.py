@@ -286,6 +286,38 @@ def main():
                                (2 * M * P.N * P.K / t_fwd / 1e12) if prefill
                                else f32_bytes / t_fwd / 1e9, 2 if prefill else 1)}
 
+    # RMS normalisation in front of the quantiser (the step before the
+    # projection): the normalising quantiser alone, and fused into the
+    # projection as the dominant projection would run it
+    from synth import make_weight
+    norm_g = torch.from_numpy((1.0 + make_weight(wl.seed, "bench/norm_g", 1, q0["p"].K, 0.1)[0])
+                              .astype(np.float32)).to(dev)
+    g_rq = graph_of([lambda: tb.bitlinear_rmsnorm_quant(q0["X"], norm_g, q0["Xq"], q0["s"],
+                                                         q0["xs"], stream=stream)] * 50)
+    g_rq.replay()
+    t_rq = timer(g_rq.replay, 10) / 500
+    rq_bytes = M * q0["p"].K * 5 + 4 * q0["p"].K + 8 * M
+    rows["rmsnorm_quant"] = {"shape": f"M{M} K{q0['p'].K}", "us": round(t_rq * 1e6, 3),
+                             "GB/s": round(rq_bytes / t_rq / 1e9, 1),
+                             "frac_of_hbm": round(rq_bytes / t_rq / 1e9 / HBM_PEAK_GBS, 4)}
+    gd = dom["p"].K
+    dom_norm_g = norm_g if gd == q0["p"].K else torch.from_numpy(
+        (1.0 + make_weight(wl.seed, "bench/norm_g", 1, gd, 0.1)[0]).astype(np.float32)).to(dev)
+    rn_need = tb.forward_rmsnorm_workspace_bytes(M, P.N, P.K)
+    rn_ws = torch.empty(max(rn_need, 16), dtype=torch.uint8, device=dev)
+
+    def fwd_rms(r):
+        tb.bitlinear_forward_rmsnorm(dom["Wc"][r % copies], dom["g"], dom["X"], dom_norm_g, N=P.N,
+                                     y_dtype=out, Y=dom["Y"], workspace=rn_ws, stream=stream)
+    g_fr = graph_of([lambda r=r: fwd_rms(r) for r in range(copies)])
+    g_fr.replay()
+    t_fr = timer(g_fr.replay, reps) / (reps * copies)
+    rows["forward_rmsnorm"] = {"shape": f"M{M} {P.K}->{P.N}", "us": round(t_fr * 1e6, 3),
+                               "fused": rn_need == 0,
+                               ("TOP/s" if prefill else "GB/s"): round(
+                                   (2 * M * P.N * P.K / t_fr / 1e12) if prefill
+                                   else (f32_bytes + 4 * P.K) / t_fr / 1e9, 2 if prefill else 1)}
+
     if grouped:
         # the same step as one call per projection, for comparison
         g_sep = graph_of([lambda r=r: step_separate(r) for r in range(cycle)])
@@ -295,6 +327,20 @@ def main():
                                        "note": "one bitlinear_forward_f32 per projection"}
         rows["step_grouped"] = {"us": round(ms_per_step * 1e3, 3),
                                 "note": "one bitlinear_forward_f32_grouped"}
+        gn_need = tb.forward_rmsnorm_grouped_workspace_bytes(M, Ns, projs[0]["p"].K)
+        gn_ws = torch.empty(max(gn_need, 16), dtype=torch.uint8, device=dev)
+
+        def step_grouped_rms(r):
+            tb.bitlinear_forward_rmsnorm_grouped([q["Wc"][r % copies] for q in projs],
+                                                 [q["g"] for q in projs], projs[0]["X"], norm_g,
+                                                 Ns=Ns, y_dtype=out, Y=[q["Y"] for q in projs],
+                                                 workspace=gn_ws, stream=stream)
+        g_gr = graph_of([lambda r=r: step_grouped_rms(r) for r in range(cycle)])
+        g_gr.replay()
+        t_gr = timer(g_gr.replay, max(1, 2000 // cycle)) / (max(1, 2000 // cycle) * cycle)
+        rows["step_grouped_rmsnorm"] = {"us": round(t_gr * 1e6, 3), "fused": gn_need == 0,
+                                        "note": "one bitlinear_forward_rmsnorm_grouped: RMS "
+                                                "normalisation, quantiser and every projection"}
 
     # ---------------- CPU oracle on a bounded sample of the same step
     cpu = None

@@ -249,6 +249,64 @@ bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_pa
                                                int32_t* x_sum_out, void* workspace,
                                                size_t workspace_bytes, void* stream);
 
+/*
+ * RMS normalisation before the quantiser.  Page section 2 (activations are
+ * normalised with RMSNorm before they are quantised to int8; the page cites
+ * Zhang and Sennrich, "Root Mean Square Layer Normalization"):
+ *   y_k = x_k / sqrt(mean_k x_k^2 + eps) * g_k,   eps = 1e-5,
+ * per token, with a gain vector g and no centring.  The mean of squares is
+ * accumulated in fp64 and rounded once to fp32; then one fp32 add, a correctly
+ * rounded fp32 square root and reciprocal r, and y_k = fl32(fl32(x_k r) g_k).
+ * The fp64 sum equals the exact sum to within K 2^-53 (relative), so the fp32
+ * mean is the correctly rounded one except when the exact mean lies that close
+ * to a rounding boundary between two fp32 values.  Then y goes through exactly
+ * bitlinear_quant_acts.
+ *
+ * X       [M][K] fp32, device, 16-byte aligned (read only).
+ * norm_g  [K] fp32 gain, device, 16-byte aligned (read only).
+ * X_q, x_scale, x_sum   as in bitlinear_quant_acts.
+ * Errors as in bitlinear_quant_acts (a NULL gain is BITLINEAR_ERR_NULL).
+ */
+bitlinear_status bitlinear_rmsnorm_quant(const float* X, const float* norm_g, int64_t M,
+                                         int64_t K, int8_t* X_q, float* x_scale, int32_t* x_sum,
+                                         void* stream);
+
+/* Bytes of workspace bitlinear_forward_rmsnorm needs (the rules of
+ * bitlinear_forward_f32_workspace_bytes; normalisation is fused only into the
+ * single-token launch, so some multi-token shapes that fuse in
+ * bitlinear_forward_f32 take two launches here).  0 if the shape is invalid. */
+size_t bitlinear_forward_rmsnorm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * RMS normalisation, quantiser and projection: bitlinear_rmsnorm_quant
+ * followed by bitlinear_forward (same X~, x_scale, x_sum and accumulators).
+ * One launch for one token with K a multiple of 64 up to 12288, else those
+ * two launches.  Arguments as in bitlinear_forward_f32, plus the gain norm_g
+ * ([K] fp32, device, 16-byte aligned); workspace from
+ * bitlinear_forward_rmsnorm_workspace_bytes, with the same exception when the
+ * quantiser outputs are given.
+ */
+bitlinear_status bitlinear_forward_rmsnorm(const uint8_t* W_packed, const float* gamma, int64_t N,
+                                           int64_t K, const float* X, const float* norm_g,
+                                           int64_t M, void* Y, bitlinear_dtype y_dtype,
+                                           int8_t* X_q_out, float* x_scale_out,
+                                           int32_t* x_sum_out, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/* The grouped form (up to BITLINEAR_MAX_GROUP projections of one normalised
+ * activation matrix, arrays as in bitlinear_forward_grouped): the usual place
+ * of the normalisation, in front of the q/k/v or up/gate projections. */
+size_t bitlinear_forward_rmsnorm_grouped_workspace_bytes(int64_t M, int G, const int64_t* N,
+                                                         int64_t K);
+bitlinear_status bitlinear_forward_rmsnorm_grouped(int G, const uint8_t* const* W_packed,
+                                                   const float* const* gamma, const int64_t* N,
+                                                   int64_t K, const float* X,
+                                                   const float* norm_g, int64_t M,
+                                                   void* const* Y, bitlinear_dtype y_dtype,
+                                                   int8_t* X_q_out, float* x_scale_out,
+                                                   int32_t* x_sum_out, void* workspace,
+                                                   size_t workspace_bytes, void* stream);
+
 /* Static English name of a status. */
 const char* bitlinear_status_string(bitlinear_status s);
 

@@ -14,11 +14,16 @@ from .binding import (  # noqa: F401
     bitlinear_forward_f32,
     bitlinear_forward_f32_grouped,
     bitlinear_forward_grouped,
+    bitlinear_forward_rmsnorm,
+    bitlinear_forward_rmsnorm_grouped,
     bitlinear_pack_weights,
     bitlinear_quant_acts,
+    bitlinear_rmsnorm_quant,
     forward_f32_grouped_workspace_bytes,
     forward_f32_workspace_bytes,
     forward_grouped_workspace_bytes,
+    forward_rmsnorm_grouped_workspace_bytes,
+    forward_rmsnorm_workspace_bytes,
     forward_workspace_bytes,
     load,
     pack_workspace_bytes,

@@ -40,6 +40,15 @@ SIGNATURES = {
     "bitlinear_forward_f32_grouped": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i64, _vp, _c_i64,
                                                      _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_size,
                                                      _vp]),
+    "bitlinear_rmsnorm_quant": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "bitlinear_forward_rmsnorm_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "bitlinear_forward_rmsnorm": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp,
+                                                 ctypes.c_int, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bitlinear_forward_rmsnorm_grouped_workspace_bytes": (_c_size, [_c_i64, ctypes.c_int, _vp,
+                                                                    _c_i64]),
+    "bitlinear_forward_rmsnorm_grouped": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i64, _vp,
+                                                         _vp, _c_i64, _vp, ctypes.c_int, _vp, _vp,
+                                                         _vp, _vp, _c_size, _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -180,10 +189,26 @@ def forward_f32_workspace_bytes(M: int, N: int, K: int) -> int:
 def bitlinear_forward_f32(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None, X_q_out=None,
                           x_scale_out=None, x_sum_out=None, workspace=None, stream=None):
     """Quantise fp32 X [M][K] and project in one call -> Y [M][N]."""
+    return _forward_f32(W_packed, gamma, X, None, N, y_dtype, Y, X_q_out, x_scale_out,
+                        x_sum_out, workspace, stream)
+
+
+def bitlinear_forward_rmsnorm(W_packed, gamma, X, norm_g, N=None, y_dtype="bf16", Y=None,
+                              X_q_out=None, x_scale_out=None, x_sum_out=None, workspace=None,
+                              stream=None):
+    """RMS-normalise fp32 X [M][K] with gain norm_g [K], quantise and project -> Y [M][N]."""
+    return _forward_f32(W_packed, gamma, X, norm_g, N, y_dtype, Y, X_q_out, x_scale_out,
+                        x_sum_out, workspace, stream)
+
+
+def _forward_f32(W_packed, gamma, X, norm_g, N, y_dtype, Y, X_q_out, x_scale_out, x_sum_out,
+                 workspace, stream):
     import torch
     lib = load()
     _dev(W_packed, torch.uint8, "W_packed")
     _dev(X, torch.float32, "X")
+    if norm_g is not None:
+        _dev(norm_g, torch.float32, "norm_g")
     M, K = X.shape
     N = W_packed.shape[0] if N is None else N
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[y_dtype]
@@ -195,7 +220,8 @@ def bitlinear_forward_f32(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None, X_
         _dev(X_q_out, torch.int8, "X_q_out")
         _dev(x_scale_out, torch.float32, "x_scale_out")
         _dev(x_sum_out, torch.int32, "x_sum_out")
-    need = lib.bitlinear_forward_f32_workspace_bytes(M, N, K)
+    need = (lib.bitlinear_forward_f32_workspace_bytes(M, N, K) if norm_g is None
+            else lib.bitlinear_forward_rmsnorm_workspace_bytes(M, N, K))
     if X_q_out is not None and (M <= 16 or lib.bitlinear_forward_workspace_bytes(M, N, K) == 0):
         need = 0   # outputs given and the projection needs no workspace of its own
     if workspace is None and need:
@@ -203,10 +229,39 @@ def bitlinear_forward_f32(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None, X_
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ptr = [o.data_ptr() if o is not None else None for o in outs]
-    _check(lib.bitlinear_forward_f32(W_packed.data_ptr(), gamma.data_ptr(), N, K, X.data_ptr(), M,
-                                     Y.data_ptr(), DTYPES[y_dtype], ptr[0], ptr[1], ptr[2],
-                                     ws_ptr, ws_bytes, _stream(stream)))
+    if norm_g is None:
+        _check(lib.bitlinear_forward_f32(W_packed.data_ptr(), gamma.data_ptr(), N, K,
+                                         X.data_ptr(), M, Y.data_ptr(), DTYPES[y_dtype], ptr[0],
+                                         ptr[1], ptr[2], ws_ptr, ws_bytes, _stream(stream)))
+    else:
+        _check(lib.bitlinear_forward_rmsnorm(W_packed.data_ptr(), gamma.data_ptr(), N, K,
+                                             X.data_ptr(), norm_g.data_ptr(), M, Y.data_ptr(),
+                                             DTYPES[y_dtype], ptr[0], ptr[1], ptr[2], ws_ptr,
+                                             ws_bytes, _stream(stream)))
     return Y
+
+
+def forward_rmsnorm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return load().bitlinear_forward_rmsnorm_workspace_bytes(M, N, K)
+
+
+def bitlinear_rmsnorm_quant(X, norm_g, X_q=None, x_scale=None, x_sum=None, stream=None):
+    """RMS-normalise fp32 X [M][K] with gain norm_g [K], then quantise:
+    -> (X_q int8 [M][K], x_scale fp32 [M], x_sum int32 [M])."""
+    import torch
+    lib = load()
+    _dev(X, torch.float32, "X")
+    _dev(norm_g, torch.float32, "norm_g")
+    M, K = X.shape
+    if X_q is None:
+        X_q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    if x_sum is None:
+        x_sum = torch.empty(M, dtype=torch.int32, device=X.device)
+    _check(lib.bitlinear_rmsnorm_quant(X.data_ptr(), norm_g.data_ptr(), M, K, X_q.data_ptr(),
+                                       x_scale.data_ptr(), x_sum.data_ptr(), _stream(stream)))
+    return X_q, x_scale, x_sum
 
 
 MAX_GROUP = 4
@@ -271,8 +326,29 @@ def bitlinear_forward_f32_grouped(W_packed, gamma, X, Ns=None, y_dtype="bf16", Y
                                   X_q_out=None, x_scale_out=None, x_sum_out=None, workspace=None,
                                   stream=None):
     """Quantise fp32 X [M][K] once and run every packed projection -> list of Y."""
+    return _forward_f32_grouped(W_packed, gamma, X, None, Ns, y_dtype, Y, X_q_out, x_scale_out,
+                                x_sum_out, workspace, stream)
+
+
+def bitlinear_forward_rmsnorm_grouped(W_packed, gamma, X, norm_g, Ns=None, y_dtype="bf16",
+                                      Y=None, X_q_out=None, x_scale_out=None, x_sum_out=None,
+                                      workspace=None, stream=None):
+    """RMS-normalise fp32 X [M][K] with gain norm_g [K], quantise once and run every packed
+    projection -> list of Y."""
+    return _forward_f32_grouped(W_packed, gamma, X, norm_g, Ns, y_dtype, Y, X_q_out,
+                                x_scale_out, x_sum_out, workspace, stream)
+
+
+def forward_rmsnorm_grouped_workspace_bytes(M: int, Ns, K: int) -> int:
+    return load().bitlinear_forward_rmsnorm_grouped_workspace_bytes(M, len(Ns), _i64_array(Ns), K)
+
+
+def _forward_f32_grouped(W_packed, gamma, X, norm_g, Ns, y_dtype, Y, X_q_out, x_scale_out,
+                         x_sum_out, workspace, stream):
     import torch
     lib = load()
+    if norm_g is not None:
+        _dev(norm_g, torch.float32, "norm_g")
     G = len(W_packed)
     if len(gamma) != G:
         raise ValueError("one gamma per projection")
@@ -288,7 +364,8 @@ def bitlinear_forward_f32_grouped(W_packed, gamma, X, Ns=None, y_dtype="bf16", Y
         _dev(x_scale_out, torch.float32, "x_scale_out")
         _dev(x_sum_out, torch.int32, "x_sum_out")
     n_arr = _i64_array(Ns)
-    need = lib.bitlinear_forward_f32_grouped_workspace_bytes(M, G, n_arr, K)
+    need = (lib.bitlinear_forward_f32_grouped_workspace_bytes(M, G, n_arr, K) if norm_g is None
+            else lib.bitlinear_forward_rmsnorm_grouped_workspace_bytes(M, G, n_arr, K))
     if X_q_out is not None and (M <= 16 or lib.bitlinear_forward_grouped_workspace_bytes(
             M, G, n_arr, K) == 0):
         need = 0   # outputs given and the projections need no workspace of their own
@@ -297,8 +374,15 @@ def bitlinear_forward_f32_grouped(W_packed, gamma, X, Ns=None, y_dtype="bf16", Y
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ptr = [o.data_ptr() if o is not None else None for o in outs]
-    _check(lib.bitlinear_forward_f32_grouped(G, _ptr_array(W_packed), _ptr_array(gamma), n_arr, K,
-                                             X.data_ptr(), M, _ptr_array(Y), DTYPES[y_dtype],
-                                             ptr[0], ptr[1], ptr[2], ws_ptr, ws_bytes,
-                                             _stream(stream)))
+    if norm_g is None:
+        _check(lib.bitlinear_forward_f32_grouped(G, _ptr_array(W_packed), _ptr_array(gamma), n_arr,
+                                                 K, X.data_ptr(), M, _ptr_array(Y),
+                                                 DTYPES[y_dtype], ptr[0], ptr[1], ptr[2], ws_ptr,
+                                                 ws_bytes, _stream(stream)))
+    else:
+        _check(lib.bitlinear_forward_rmsnorm_grouped(G, _ptr_array(W_packed), _ptr_array(gamma),
+                                                     n_arr, K, X.data_ptr(), norm_g.data_ptr(), M,
+                                                     _ptr_array(Y), DTYPES[y_dtype], ptr[0],
+                                                     ptr[1], ptr[2], ws_ptr, ws_bytes,
+                                                     _stream(stream)))
     return Y

@@ -154,9 +154,55 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma, 
                   "forward launch");
 }
 
-size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+namespace {
+// fp32 activations in: the quantiser (after an RMS normalisation with gain
+// norm_g when that is not null) and the projection.
+bitlinear_status forward_f32_impl(const char* who, const uint8_t* W_packed, const float* gamma,
+                                  int64_t N, int64_t K, const float* X, const float* norm_g,
+                                  int64_t M, void* Y, bitlinear_dtype y_dtype, int8_t* X_q_out,
+                                  float* x_scale_out, int32_t* x_sum_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!W_packed || !gamma || !X || !Y) return fail(BITLINEAR_ERR_NULL, "%s: NULL buffer", who);
+  const int given = (X_q_out != nullptr) + (x_scale_out != nullptr) + (x_sum_out != nullptr);
+  if (given != 0 && given != 3)
+    return fail(BITLINEAR_ERR_NULL, "%s: X_q_out, x_scale_out and x_sum_out go together", who);
+  if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "%s: invalid shape M=%lld N=%lld K=%lld", who,
+                (long long)M, (long long)N, (long long)K);
+  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+    return fail(BITLINEAR_ERR_DTYPE, "%s: unknown y_dtype %d", who, (int)y_dtype);
+  const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
+  if (!aligned(W_packed, 16) || !aligned(X, 16) || !aligned(gamma, 4) || !aligned(Y, ya) ||
+      (norm_g && !aligned(norm_g, 16)) ||
+      (X_q_out && (!aligned(X_q_out, 16) || !aligned(x_scale_out, 4) || !aligned(x_sum_out, 4))))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: W_packed, X, the gain and X_q_out need 16-byte "
+                "alignment, Y its element size", who);
+  // With the quantiser outputs given, the workspace is needed only for the
+  // projection's own part (same layout: it follows the quantiser region).
+  const bool norm = norm_g != nullptr;
+  const bool proj_ws = M > 16 && bl::forward_workspace_bytes(M, N, K) > 0;
+  const size_t need = (given && !proj_ws) ? 0 : bl::forward_f32_workspace_bytes(M, N, K, norm);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu", who,
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned(workspace, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: workspace alignment", who);
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward_f32(W_packed, gamma, N, K, X, norm_g, M, Y, (int)y_dtype,
+                                         X_q_out, x_scale_out, x_sum_out, workspace,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                  "forward launch");
+}
+
+size_t forward_f32_ws(int64_t M, int64_t N, int64_t K, bool norm) {
   if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K)) return 0;
-  return bl::forward_f32_workspace_bytes(M, N, K);
+  return bl::forward_f32_workspace_bytes(M, N, K, norm);
+}
+}  // namespace
+
+size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return forward_f32_ws(M, N, K, false);
 }
 
 bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N,
@@ -164,35 +210,43 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
                                        bitlinear_dtype y_dtype, int8_t* X_q_out,
                                        float* x_scale_out, int32_t* x_sum_out, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  if (!W_packed || !gamma || !X || !Y) return fail(BITLINEAR_ERR_NULL, "forward_f32: NULL buffer");
-  const int given = (X_q_out != nullptr) + (x_scale_out != nullptr) + (x_sum_out != nullptr);
-  if (given != 0 && given != 3)
-    return fail(BITLINEAR_ERR_NULL, "forward_f32: X_q_out, x_scale_out and x_sum_out go together");
-  if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K))
-    return fail(BITLINEAR_ERR_SHAPE, "forward_f32: invalid shape M=%lld N=%lld K=%lld",
-                (long long)M, (long long)N, (long long)K);
-  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
-    return fail(BITLINEAR_ERR_DTYPE, "forward_f32: unknown y_dtype %d", (int)y_dtype);
-  const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
-  if (!aligned(W_packed, 16) || !aligned(X, 16) || !aligned(gamma, 4) || !aligned(Y, ya) ||
-      (X_q_out && (!aligned(X_q_out, 16) || !aligned(x_scale_out, 4) || !aligned(x_sum_out, 4))))
-    return fail(BITLINEAR_ERR_ALIGN, "forward_f32: W_packed, X and X_q_out need 16-byte "
-                "alignment, Y its element size");
-  // With the quantiser outputs given, the workspace is needed only for the
-  // projection's own part (same layout: it follows the quantiser region).
-  const bool proj_ws = M > 16 && bl::forward_workspace_bytes(M, N, K) > 0;
-  const size_t need = (given && !proj_ws) ? 0 : bl::forward_f32_workspace_bytes(M, N, K);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(BITLINEAR_ERR_WORKSPACE, "forward_f32: workspace of %zu bytes needed, got %zu",
-                need, workspace ? workspace_bytes : (size_t)0);
-  if (need && !aligned(workspace, 16))
-    return fail(BITLINEAR_ERR_ALIGN, "forward_f32: workspace alignment");
+  return forward_f32_impl("forward_f32", W_packed, gamma, N, K, X, nullptr, M, Y, y_dtype,
+                          X_q_out, x_scale_out, x_sum_out, workspace, workspace_bytes, stream);
+}
+
+// ---- RMS normalisation before the quantiser -------------------------------------
+
+bitlinear_status bitlinear_rmsnorm_quant(const float* X, const float* norm_g, int64_t M,
+                                         int64_t K, int8_t* X_q, float* x_scale, int32_t* x_sum,
+                                         void* stream) {
+  if (!X || !norm_g || !X_q || !x_scale || !x_sum)
+    return fail(BITLINEAR_ERR_NULL, "rmsnorm_quant: NULL buffer");
+  if (M < 1 || M > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "rmsnorm_quant: invalid shape M=%lld K=%lld", (long long)M,
+                (long long)K);
+  if (!aligned(X, 16) || !aligned(norm_g, 16) || !aligned(X_q, 16) || !aligned(x_scale, 4) ||
+      !aligned(x_sum, 4))
+    return fail(BITLINEAR_ERR_ALIGN, "rmsnorm_quant: X, the gain and X_q need 16-byte alignment");
   bitlinear_status s = check_device();
   if (s != BITLINEAR_OK) return s;
-  return launched(bl::launch_forward_f32(W_packed, gamma, N, K, X, M, Y, (int)y_dtype, X_q_out,
-                                         x_scale_out, x_sum_out, workspace,
-                                         reinterpret_cast<hipStream_t>(stream)),
-                  "forward_f32 launch");
+  return launched(bl::launch_rmsnorm_quant(X, norm_g, M, K, X_q, x_scale, x_sum,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                  "rmsnorm_quant launch");
+}
+
+size_t bitlinear_forward_rmsnorm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return forward_f32_ws(M, N, K, true);
+}
+
+bitlinear_status bitlinear_forward_rmsnorm(const uint8_t* W_packed, const float* gamma, int64_t N,
+                                           int64_t K, const float* X, const float* norm_g,
+                                           int64_t M, void* Y, bitlinear_dtype y_dtype,
+                                           int8_t* X_q_out, float* x_scale_out,
+                                           int32_t* x_sum_out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (!norm_g) return fail(BITLINEAR_ERR_NULL, "forward_rmsnorm: NULL gain");
+  return forward_f32_impl("forward_rmsnorm", W_packed, gamma, N, K, X, norm_g, M, Y, y_dtype,
+                          X_q_out, x_scale_out, x_sum_out, workspace, workspace_bytes, stream);
 }
 
 // ---- several projections of one activation matrix -----------------------------
@@ -256,12 +310,53 @@ bitlinear_status bitlinear_forward_grouped(int G, const uint8_t* const* W_packed
                   "forward_grouped launch");
 }
 
-size_t bitlinear_forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N,
-                                                     int64_t K) {
+namespace {
+size_t forward_f32_grouped_ws(int64_t M, int G, const int64_t* N, int64_t K, bool norm) {
   if (G < 1 || G > BITLINEAR_MAX_GROUP || !N || M < 1 || M > kMaxDim || !shape_ok_k(K)) return 0;
   for (int g = 0; g < G; ++g)
     if (N[g] < 1 || N[g] > kMaxDim) return 0;
-  return bl::forward_f32_grouped_workspace_bytes(M, G, N, K);
+  return bl::forward_f32_grouped_workspace_bytes(M, G, N, K, norm);
+}
+
+bitlinear_status forward_f32_grouped_impl(const char* who, int G, const uint8_t* const* W_packed,
+                                          const float* const* gamma, const int64_t* N, int64_t K,
+                                          const float* X, const float* norm_g, int64_t M,
+                                          void* const* Y, bitlinear_dtype y_dtype,
+                                          int8_t* X_q_out, float* x_scale_out,
+                                          int32_t* x_sum_out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  bitlinear_status s = check_group(who, G, W_packed, gamma, N, K, M, Y, y_dtype);
+  if (s != BITLINEAR_OK) return s;
+  if (!X) return fail(BITLINEAR_ERR_NULL, "%s: NULL X", who);
+  const int given = (X_q_out != nullptr) + (x_scale_out != nullptr) + (x_sum_out != nullptr);
+  if (given != 0 && given != 3)
+    return fail(BITLINEAR_ERR_NULL, "%s: X_q_out, x_scale_out and x_sum_out go together", who);
+  if (!aligned(X, 16) || (norm_g && !aligned(norm_g, 16)) ||
+      (X_q_out && (!aligned(X_q_out, 16) || !aligned(x_scale_out, 4) || !aligned(x_sum_out, 4))))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: X, the gain and X_q_out need 16-byte alignment", who);
+  // With the quantiser outputs given, the workspace is needed only for the
+  // projections' own part (same layout: it follows the quantiser region).
+  const bool norm = norm_g != nullptr;
+  const bool proj_ws = M > 16 && bl::forward_grouped_workspace_bytes(M, G, N, K) > 0;
+  const size_t need =
+      (given && !proj_ws) ? 0 : bl::forward_f32_grouped_workspace_bytes(M, G, N, K, norm);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu", who,
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned(workspace, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: workspace alignment", who);
+  s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward_f32_grouped(G, W_packed, gamma, N, K, X, norm_g, M, Y,
+                                                 (int)y_dtype, X_q_out, x_scale_out, x_sum_out,
+                                                 workspace, reinterpret_cast<hipStream_t>(stream)),
+                  "grouped forward launch");
+}
+}  // namespace
+
+size_t bitlinear_forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N,
+                                                     int64_t K) {
+  return forward_f32_grouped_ws(M, G, N, K, false);
 }
 
 bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_packed,
@@ -271,33 +366,28 @@ bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_pa
                                                int8_t* X_q_out, float* x_scale_out,
                                                int32_t* x_sum_out, void* workspace,
                                                size_t workspace_bytes, void* stream) {
-  bitlinear_status s = check_group("forward_f32_grouped", G, W_packed, gamma, N, K, M, Y, y_dtype);
-  if (s != BITLINEAR_OK) return s;
-  if (!X) return fail(BITLINEAR_ERR_NULL, "forward_f32_grouped: NULL X");
-  const int given = (X_q_out != nullptr) + (x_scale_out != nullptr) + (x_sum_out != nullptr);
-  if (given != 0 && given != 3)
-    return fail(BITLINEAR_ERR_NULL,
-                "forward_f32_grouped: X_q_out, x_scale_out and x_sum_out go together");
-  if (!aligned(X, 16) ||
-      (X_q_out && (!aligned(X_q_out, 16) || !aligned(x_scale_out, 4) || !aligned(x_sum_out, 4))))
-    return fail(BITLINEAR_ERR_ALIGN, "forward_f32_grouped: X and X_q_out need 16-byte alignment");
-  // With the quantiser outputs given, the workspace is needed only for the
-  // projections' own part (same layout: it follows the quantiser region).
-  const bool proj_ws = M > 16 && bl::forward_grouped_workspace_bytes(M, G, N, K) > 0;
-  const size_t need =
-      (given && !proj_ws) ? 0 : bl::forward_f32_grouped_workspace_bytes(M, G, N, K);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(BITLINEAR_ERR_WORKSPACE,
-                "forward_f32_grouped: workspace of %zu bytes needed, got %zu", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (need && !aligned(workspace, 16))
-    return fail(BITLINEAR_ERR_ALIGN, "forward_f32_grouped: workspace alignment");
-  s = check_device();
-  if (s != BITLINEAR_OK) return s;
-  return launched(bl::launch_forward_f32_grouped(G, W_packed, gamma, N, K, X, M, Y, (int)y_dtype,
-                                                 X_q_out, x_scale_out, x_sum_out, workspace,
-                                                 reinterpret_cast<hipStream_t>(stream)),
-                  "forward_f32_grouped launch");
+  return forward_f32_grouped_impl("forward_f32_grouped", G, W_packed, gamma, N, K, X, nullptr, M,
+                                  Y, y_dtype, X_q_out, x_scale_out, x_sum_out, workspace,
+                                  workspace_bytes, stream);
+}
+
+size_t bitlinear_forward_rmsnorm_grouped_workspace_bytes(int64_t M, int G, const int64_t* N,
+                                                         int64_t K) {
+  return forward_f32_grouped_ws(M, G, N, K, true);
+}
+
+bitlinear_status bitlinear_forward_rmsnorm_grouped(int G, const uint8_t* const* W_packed,
+                                                   const float* const* gamma, const int64_t* N,
+                                                   int64_t K, const float* X,
+                                                   const float* norm_g, int64_t M,
+                                                   void* const* Y, bitlinear_dtype y_dtype,
+                                                   int8_t* X_q_out, float* x_scale_out,
+                                                   int32_t* x_sum_out, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  if (!norm_g) return fail(BITLINEAR_ERR_NULL, "forward_rmsnorm_grouped: NULL gain");
+  return forward_f32_grouped_impl("forward_rmsnorm_grouped", G, W_packed, gamma, N, K, X, norm_g,
+                                  M, Y, y_dtype, X_q_out, x_scale_out, x_sum_out, workspace,
+                                  workspace_bytes, stream);
 }
 
 const char* bitlinear_status_string(bitlinear_status s) {

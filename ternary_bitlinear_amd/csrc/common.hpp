@@ -72,6 +72,50 @@ __device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
   return (int32_t)wave_reduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
+// fp64 sum over the wave by the same DPP steps, each moving both 32-bit halves
+// of a value; every lane receives the result.  The addition order is fixed,
+// so the result is reproducible.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, true);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_f64<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_f64<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_f64<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_f64<0x142, 0xA>(v);   // row_bcast15
+  v += dpp_f64<0x143, 0xC>(v);   // row_bcast31
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// RMS normalisation of a token (page section 2: activations are RMS-normalised
+// before the quantiser; the normalisation of the reference it cites):
+// y_k = x_k / sqrt(mean x^2 + eps) * g_k.  sq is the token's sum of squares in
+// fp64 (each square exact); ms = fl32(sq / K), then an fp32 add, a correctly
+// rounded fp32 square root and reciprocal.  Returns r; each element is then
+// fl32(fl32(x_k r) g_k) (rms_apply).
+__device__ __forceinline__ float rms_reciprocal(double sq, int64_t K) {
+  const float ms = (float)(sq / (double)K);
+  return 1.0f / sqrtf(ms + 1e-5f);
+}
+
+__device__ __forceinline__ float4 rms_apply(const float4& x, float r, const float4& g) {
+  return make_float4((x.x * r) * g.x, (x.y * r) * g.y, (x.z * r) * g.z, (x.w * r) * g.w);
+}
+
+__device__ __forceinline__ double sum_sq4(const float4& x) {
+  const double a = x.x, b = x.y, c = x.z, d = x.w;
+  return ((a * a + b * b) + c * c) + d * d;
+}
+
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += (uint64_t)__shfl_xor((unsigned long long)v, o, kWave);

@@ -115,6 +115,7 @@ struct DecodeArgs {
   const float* xs;         //                x_scale [M]
   const int32_t* xsum;     //                x_sum [M]
   const float* X;          // kAFuse: fp32 activations [M][K]
+  const float* norm_g;     // fused single-token decode with RMS normalisation: gain [K]
   int8_t* Xq_out;          // kAFuse: optional copies of the quantiser outputs
   float* xs_out;
   int32_t* xsum_out;
@@ -594,13 +595,15 @@ hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t s
 constexpr int kDotFuseNone = 0, kDotFuseWave = 1, kDotFuseBlock = 2;
 constexpr int kDotWaves = 4;   // waves per workgroup without block fusion
 
-template <int OUT, int R, int Q, int FUSE, int WV>
+template <int OUT, int R, int Q, int FUSE, int WV, bool NORM = false>
 __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
   static_assert(FUSE != kDotFuseWave || Q == 1, "the per-wave prologue holds one piece per lane");
+  static_assert(!NORM || FUSE == kDotFuseBlock, "normalisation only in the block-fused prologue");
   constexpr int kFuseK4 = 64 * 64 / 4 * Q;                   // groups of four at K = 4096 Q
   constexpr int kJ = FUSE == kDotFuseBlock ? kFuseK4 / (WV * kWave) : 1;   // groups per thread
   __shared__ uint32_t s_codes[FUSE == kDotFuseBlock ? kFuseK4 : 1];
   __shared__ uint32_t s_red[2][WV];
+  __shared__ double s_sq[NORM ? WV : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * WV + wave;   // the wave's index over all projections
@@ -678,15 +681,34 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
     const int K4 = K / 4;
     const float4* src = reinterpret_cast<const float4*>(da.X);
     float4 xv[kJ];
+    float4 gv[NORM ? kJ : 1];
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int i = threadIdx.x + WV * kWave * j;
       xv[j] = src[i < K4 ? i : 0];
+      if constexpr (NORM) gv[j] = reinterpret_cast<const float4*>(da.norm_g)[i < K4 ? i : 0];
     }
     __builtin_amdgcn_sched_barrier(0);
     load_weights();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::"s"(gamma), "s"(yout));
+    if constexpr (NORM) {
+      // RMS normalisation first (the standalone normalising quantiser's
+      // arithmetic and, with four waves, its exact fp64 summation order).
+      double sq = 0.0;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+        if (threadIdx.x + WV * kWave * j < K4) sq += sum_sq4(xv[j]);
+      sq = wave_sum_f64(sq);
+      if (lane == 0) s_sq[wave] = sq;
+      __syncthreads();
+      double tot = s_sq[0];
+#pragma unroll
+      for (int w = 1; w < WV; ++w) tot += s_sq[w];
+      const float rr = rms_reciprocal(tot, K);
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) xv[j] = rms_apply(xv[j], rr, gv[j]);
+    }
     uint32_t lmax = 0;
 #pragma unroll
     for (int j = 0; j < kJ; ++j)
@@ -784,11 +806,11 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
   if (lane < R && n0 + lane < N) store_out<OUT>(yout, n0 + lane, mine - sx, gamma, sc);
 }
 
-template <int OUT, int R, int Q, int FUSE = kDotFuseNone, int WV = kDotWaves>
+template <int OUT, int R, int Q, int FUSE = kDotFuseNone, int WV = kDotWaves, bool NORM = false>
 hipError_t launch_decode_dot_t(DecodeArgs da, hipStream_t stream) {
   const int waves = set_units(da, R);
   const int grid = (waves + WV - 1) / WV;
-  k_decode_dot<OUT, R, Q, FUSE, WV><<<dim3(grid), dim3(WV * kWave), 0, stream>>>(da);
+  k_decode_dot<OUT, R, Q, FUSE, WV, NORM><<<dim3(grid), dim3(WV * kWave), 0, stream>>>(da);
   return hipGetLastError();
 }
 
@@ -1574,22 +1596,29 @@ inline bool fused_dot(int64_t M, int64_t K) {
 }
 
 namespace {
-template <int OUT>
+template <int OUT, bool NORM>
 hipError_t fused_dot_out(const DecodeArgs& da, hipStream_t stream) {
   const int q = (da.K + 64 * 64 - 1) / (64 * 64);
-  if (q <= 1) return launch_decode_dot_t<OUT, kDotFuseRows, 1, kDotFuseBlock, kDotFuseWaves>(da, stream);
-  if (q == 2) return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, kDotFuseWaves>(da, stream);
-  return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves>(da, stream);
+  if (q <= 1) return launch_decode_dot_t<OUT, kDotFuseRows, 1, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
+  if (q == 2) return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
+  return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
+}
+template <int OUT>
+hipError_t fused_dot_norm(const DecodeArgs& da, hipStream_t stream) {
+  return da.norm_g ? fused_dot_out<OUT, true>(da, stream) : fused_dot_out<OUT, false>(da, stream);
 }
 }  // namespace
 
-size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K) {
-  if (fused_dot(M, K) || fused_cfg(M, G, N, K).am == kAFuse) return 0;
+// norm: RMS normalisation first; the single-token vector-ALU prologue fuses
+// it, the multi-token matrix prologue does not (two launches there).
+size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K,
+                                           bool norm) {
+  if (fused_dot(M, K) || (!norm && fused_cfg(M, G, N, K).am == kAFuse)) return 0;
   return quant_region_bytes(M, K) + forward_grouped_workspace_bytes(M, G, N, K);
 }
 
-size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  return forward_f32_grouped_workspace_bytes(M, 1, &N, K);
+size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K, bool norm) {
+  return forward_f32_grouped_workspace_bytes(M, 1, &N, K, norm);
 }
 
 namespace {
@@ -1602,23 +1631,25 @@ hipError_t fused_out(const DecodeCfg& c, const DecodeArgs& da, hipStream_t strea
 
 hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
                                       const float* const* gamma, const int64_t* N, int64_t K,
-                                      const float* X, int64_t M, void* const* Y, int y_dtype,
-                                      int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
-                                      void* workspace, hipStream_t stream) {
+                                      const float* X, const float* norm_g, int64_t M,
+                                      void* const* Y, int y_dtype, int8_t* X_q_out,
+                                      float* x_scale_out, int32_t* x_sum_out, void* workspace,
+                                      hipStream_t stream) {
   if (fused_dot(M, K)) {
     DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);
     da.X = X;
     da.Xq_out = X_q_out;
     da.xs_out = x_scale_out;
     da.xsum_out = x_sum_out;
+    da.norm_g = norm_g;
     switch (y_dtype) {
-      case kOutF32: return fused_dot_out<kOutF32>(da, stream);
-      case kOutBF16: return fused_dot_out<kOutBF16>(da, stream);
-      default: return fused_dot_out<kOutI32>(da, stream);
+      case kOutF32: return fused_dot_norm<kOutF32>(da, stream);
+      case kOutBF16: return fused_dot_norm<kOutBF16>(da, stream);
+      default: return fused_dot_norm<kOutI32>(da, stream);
     }
   }
   const DecodeCfg c = fused_cfg(M, G, N, K);
-  if (c.am == kAFuse) {
+  if (c.am == kAFuse && norm_g == nullptr) {
     DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);
     da.X = X;
     da.Xq_out = X_q_out;
@@ -1644,18 +1675,19 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
   // The projections' workspace follows the quantiser region (present in the
   // size query in both cases).
   void* fws = w ? w + quant_region_bytes(M, K) : nullptr;
-  hipError_t e = launch_quant(X, M, K, xq, xs, xsum, stream);
+  hipError_t e = norm_g ? launch_rmsnorm_quant(X, norm_g, M, K, xq, xs, xsum, stream)
+                        : launch_quant(X, M, K, xq, xs, xsum, stream);
   if (e != hipSuccess) return e;
   return launch_forward_grouped(G, W_packed, gamma, N, K, xq, xs, xsum, M, Y, y_dtype, fws,
                                 stream);
 }
 
 hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
-                              const float* X, int64_t M, void* Y, int y_dtype, int8_t* X_q_out,
-                              float* x_scale_out, int32_t* x_sum_out, void* workspace,
-                              hipStream_t stream) {
-  return launch_forward_f32_grouped(1, &W_packed, &gamma, &N, K, X, M, &Y, y_dtype, X_q_out,
-                                    x_scale_out, x_sum_out, workspace, stream);
+                              const float* X, const float* norm_g, int64_t M, void* Y,
+                              int y_dtype, int8_t* X_q_out, float* x_scale_out,
+                              int32_t* x_sum_out, void* workspace, hipStream_t stream) {
+  return launch_forward_f32_grouped(1, &W_packed, &gamma, &N, K, X, norm_g, M, &Y, y_dtype,
+                                    X_q_out, x_scale_out, x_sum_out, workspace, stream);
 }
 
 }  // namespace bl

@@ -16,6 +16,10 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* W_packed, 
 hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float* x_scale,
                         int32_t* x_sum, hipStream_t stream);
 
+// RMS normalisation with gain G [K], then the same quantiser.
+hipError_t launch_rmsnorm_quant(const float* X, const float* G, int64_t M, int64_t K,
+                                int8_t* X_q, float* x_scale, int32_t* x_sum, hipStream_t stream);
+
 // Workspace of the projection: split-K partial accumulators for shapes with
 // few output tiles and long K, else 0.
 size_t forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -36,22 +40,25 @@ hipError_t launch_forward_grouped(int G, const uint8_t* const* W_packed,
                                   const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
                                   int64_t M, void* const* Y, int y_dtype, void* workspace,
                                   hipStream_t stream);
-size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K);
+size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K,
+                                           bool norm);
 hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
                                       const float* const* gamma, const int64_t* N, int64_t K,
-                                      const float* X, int64_t M, void* const* Y, int y_dtype,
-                                      int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
-                                      void* workspace, hipStream_t stream);
+                                      const float* X, const float* norm_g, int64_t M,
+                                      void* const* Y, int y_dtype, int8_t* X_q_out,
+                                      float* x_scale_out, int32_t* x_sum_out, void* workspace,
+                                      hipStream_t stream);
 constexpr int kMaxGroupProjections = 4;
 
-// Quantisation fused with the projection (fp32 activations in).  Optional
+// Quantisation fused with the projection (fp32 activations in; norm_g, when
+// not null, the gain of an RMS normalisation applied first).  Optional
 // X_q_out / x_scale_out / x_sum_out receive the quantiser's outputs (all or
 // none).  Unfused shapes use `workspace`: the quantiser region (used only
 // when no outputs are given), then the projection's workspace.
-size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K, bool norm);
 hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,
-                              const float* X, int64_t M, void* Y, int y_dtype, int8_t* X_q_out,
-                              float* x_scale_out, int32_t* x_sum_out, void* workspace,
-                              hipStream_t stream);
+                              const float* X, const float* norm_g, int64_t M, void* Y,
+                              int y_dtype, int8_t* X_q_out, float* x_scale_out,
+                              int32_t* x_sum_out, void* workspace, hipStream_t stream);
 
 }  // namespace bl

@@ -1,4 +1,5 @@
-// Per-token absmax int8 quantisation of activations.
+// Per-token absmax int8 quantisation of activations, optionally after RMS
+// normalisation.
 //
 // Page "BitNet b1.58: Mathematical Foundations ..." (llms.blog), section 2,
 // "Activation Quantization: Absmax Scaling", per-token variant with the
@@ -95,7 +96,102 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_acts(const float* __res
   }
 }
 
+// Block-wide fp64 sum: waves added in wave order after the DPP tree, so the
+// order is the same in every launch (and the same as in the single-token
+// decode's fused prologue, which partitions a row the same way).
+__device__ __forceinline__ double block_sum_f64(double v, double* sh) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  v = wave_sum_f64(v);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  double t = sh[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / kWave; ++w) t += sh[w];
+  return t;
+}
+
+// RMS normalisation, then the absmax quantiser, per token (page section 2:
+// the activations are RMS-normalised, then quantised to int8).  One
+// workgroup per token; thread t holds groups of four t, t + 256, ... of the
+// row and of the gain (R of them in registers; R = 0: three passes over the
+// row for rows beyond the register-resident maximum).  Sum of squares in
+// fp64, then r = 1 / sqrt(fl32(sum / K) + eps); the normalised values
+// fl32(fl32(x r) g) go through the same absmax, factor and per-element
+// rounding as k_quant_acts.
+template <int R>
+__global__ __launch_bounds__(kQuantThreads) void k_rmsnorm_quant(
+    const float* __restrict__ X, const float* __restrict__ G, int64_t K, int8_t* __restrict__ Xq,
+    float* __restrict__ x_scale, int32_t* __restrict__ x_sum) {
+  __shared__ double s_sq[kQuantThreads / kWave];
+  __shared__ uint32_t s_max[kQuantThreads / kWave];
+  __shared__ int32_t s_sum[kQuantThreads / kWave];
+  const int64_t m = blockIdx.x;
+  const float4* row = reinterpret_cast<const float4*>(X + m * K);
+  const float4* grow = reinterpret_cast<const float4*>(G);
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(Xq + m * K);
+  const int64_t K4 = K / 4;
+
+  uint32_t amax = 0;
+  int32_t sum = 0;
+  float inv;
+  if constexpr (R > 0) {
+    float4 v[R], gv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = threadIdx.x + (int64_t)r * kQuantThreads;
+      v[r] = i < K4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      gv[r] = i < K4 ? grow[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    double sq = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) sq += sum_sq4(v[r]);
+    const float rr = rms_reciprocal(block_sum_f64(sq, s_sq), K);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      v[r] = rms_apply(v[r], rr, gv[r]);
+      amax = max(amax, absmax4(v[r]));
+    }
+    amax = block_max(amax, s_max);
+    inv = 127.0f / (__uint_as_float(amax) + 1e-5f);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = threadIdx.x + (int64_t)r * kQuantThreads;
+      if (i < K4) qrow[i] = quant4(v[r], inv, sum);
+    }
+  } else {
+    double sq = 0.0;
+    for (int64_t i = threadIdx.x; i < K4; i += kQuantThreads) sq += sum_sq4(row[i]);
+    const float rr = rms_reciprocal(block_sum_f64(sq, s_sq), K);
+    for (int64_t i = threadIdx.x; i < K4; i += kQuantThreads)
+      amax = max(amax, absmax4(rms_apply(row[i], rr, grow[i])));
+    amax = block_max(amax, s_max);
+    inv = 127.0f / (__uint_as_float(amax) + 1e-5f);
+    for (int64_t i = threadIdx.x; i < K4; i += kQuantThreads)
+      qrow[i] = quant4(rms_apply(row[i], rr, grow[i]), inv, sum);
+  }
+  sum = block_sum(sum, s_sum);
+  if (threadIdx.x == 0) {
+    x_sum[m] = sum;
+    x_scale[m] = __uint_as_float(amax) / 127.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm_quant(const float* X, const float* G, int64_t M, int64_t K,
+                                int8_t* X_q, float* x_scale, int32_t* x_sum, hipStream_t stream) {
+  const dim3 grid((unsigned)M), block(kQuantThreads);
+  const int64_t per = (K / 4 + kQuantThreads - 1) / kQuantThreads;   // float4 per thread
+#define BL_RQ(RR) k_rmsnorm_quant<RR><<<grid, block, 0, stream>>>(X, G, K, X_q, x_scale, x_sum)
+  if (per <= 1) BL_RQ(1);
+  else if (per <= 2) BL_RQ(2);
+  else if (per <= 4) BL_RQ(4);
+  else if (per <= 8) BL_RQ(8);
+  else if (per <= 16) BL_RQ(16);
+  else BL_RQ(0);   // row and gain would not fit the registers together
+#undef BL_RQ
+  return hipGetLastError();
+}
 
 hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float* x_scale,
                         int32_t* x_sum, hipStream_t stream) {

@@ -151,3 +151,39 @@ def test_grouped_validation_without_gpu_calls(lib):
     f32 = lib.bitlinear_forward_f32_grouped(3, ptrs, ptrs, ns, 4096, None, 1, ptrs, 1,
                                             None, None, None, None, 0, None)
     assert f32 == 1
+
+
+def test_rmsnorm_validation_without_gpu_calls(lib):
+    import ctypes
+    # the normalising quantiser: NULL gain, bad K, misaligned gain
+    assert lib.bitlinear_rmsnorm_quant(FAKE, None, 2, 16, FAKE, FAKE, FAKE, None) == 1
+    assert lib.bitlinear_rmsnorm_quant(FAKE, FAKE, 2, 8, FAKE, FAKE, FAKE, None) == 2
+    assert lib.bitlinear_rmsnorm_quant(FAKE, FAKE + 4, 2, 16, FAKE, FAKE, FAKE, None) == 3
+    assert lib.bitlinear_rmsnorm_quant(FAKE, FAKE, 0, 16, FAKE, FAKE, FAKE, None) == 2
+    # the fused projection: NULL gain, misaligned gain, then the shared checks
+    args = [FAKE, FAKE, 4096, 4096, FAKE, FAKE, 1, FAKE, 1, None, None, None, None, 0, None]
+    bad = list(args); bad[5] = None
+    assert lib.bitlinear_forward_rmsnorm(*bad) == 1 and "gain" in _last(lib)
+    bad = list(args); bad[5] = FAKE + 4
+    assert lib.bitlinear_forward_rmsnorm(*bad) == 3
+    bad = list(args); bad[3] = 40
+    assert lib.bitlinear_forward_rmsnorm(*bad) == 2
+    # one token, K <= 12288 in steps of 64: fused, no workspace either way
+    assert lib.bitlinear_forward_rmsnorm_workspace_bytes(1, 4096, 4096) == 0
+    assert lib.bitlinear_forward_f32_workspace_bytes(1, 4096, 4096) == 0
+    # a few tokens: the quantiser alone fuses into the matrix decode, the
+    # normalising one takes two launches and needs the quantiser region
+    assert lib.bitlinear_forward_f32_workspace_bytes(4, 4096, 4096) == 0
+    need = lib.bitlinear_forward_rmsnorm_workspace_bytes(4, 4096, 4096)
+    assert need >= 4 * 4096 + 8 * 4
+    bad = list(args); bad[6] = 4
+    assert lib.bitlinear_forward_rmsnorm(*bad) == 7 and "workspace" in _last(lib)
+    # grouped form
+    ptrs = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    ns = (ctypes.c_int64 * 3)(4096, 1024, 1024)
+    st = lib.bitlinear_forward_rmsnorm_grouped(3, ptrs, ptrs, ns, 4096, FAKE, None, 1, ptrs, 1,
+                                               None, None, None, None, 0, None)
+    assert st == 1
+    assert lib.bitlinear_forward_rmsnorm_grouped_workspace_bytes(1, 3, ns, 4096) == 0
+    assert lib.bitlinear_forward_rmsnorm_grouped_workspace_bytes(4, 3, ns, 4096) > 0
+    assert lib.bitlinear_forward_rmsnorm_grouped_workspace_bytes(4, 5, ns, 4096) == 0

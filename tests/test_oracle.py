@@ -430,3 +430,18 @@ def test_rmsnorm_zero_row_and_quantiser_after_it():
     Xq, _, _, _ = O.quantize_activations(Yn)
     idx = np.abs(X).argmax(axis=1)
     assert (np.abs(Xq[np.arange(3), idx]) == 127).all()
+
+
+def test_mean_square_candidates():
+    # A mean far from any rounding boundary has one candidate.  A row whose
+    # exact mean of squares is a midpoint between two fp32 values has both:
+    # (1 + 2^-12)^2 = 1 + 2^-11 + 2^-24, half way between 1 + 2^-11 and the
+    # next fp32 value up.
+    X = np.array([[1.0, -1.0, 1.0, 1.0]], np.float32)
+    assert O.mean_square_candidates(X, 2.0 ** -40) == [[np.float32(1.0)]]
+    row = np.array([[np.float32(1.0) + np.float32(2.0 ** -12)]], np.float32)
+    c = O.mean_square_candidates(row, 2.0 ** -40)
+    assert c == [[np.float32(1 + 2.0 ** -11), np.float32(1 + 2.0 ** -11 + 2.0 ** -23)]]
+    # a hair above the midpoint (mean of two squares), only the upper one
+    # survives a tolerance smaller than the distance
+    assert O.f32_nearest((1 + Fraction(1, 2 ** 12)) ** 2) == np.float32(1 + 2.0 ** -11)   # tie: even
