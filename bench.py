@@ -580,9 +580,12 @@ def traffic_key(kernel, shapes, M, out, fused=False):
 
 
 def forward_source_digest():
+    """Digest of the sources the projection kernels are compiled from."""
     import hashlib
-    src = os.path.join(ROOT, "ternary_bitlinear_amd", "csrc", "forward.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("forward.hip", "common.hpp"):
+        h.update(open(os.path.join(ROOT, "ternary_bitlinear_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel, projs, M, out, fused=False):
