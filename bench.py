@@ -274,8 +274,9 @@ def main():
     rows["quant_acts"] = {"shape": f"M{M} K{q0['p'].K}", "us": round(t_q * 1e6, 3),
                           "GB/s": round(q_bytes / t_q / 1e9, 1),
                           "frac_of_hbm": round(q_bytes / t_q / 1e9 / HBM_PEAK_GBS, 4)}
-    rows["forward" + ("_gemm" if M > 16 else "_decode")] = {
-        "shape": proj_roof["shape"], "us": proj_roof["us_per_launch"],
+    rows["forward"] = {
+        "shape": proj_roof["shape"], "kernel": proj_roof["kernel"],
+        "us": proj_roof["us_per_launch"],
         ("TOP/s" if prefill else "GB/s"): proj_roof["achieved"],
         "entry_point": proj_roof["entry_point"],
         "epilogue": f"gamma*beta rescale fused, {out} out"}
@@ -393,8 +394,26 @@ def step_is_fused(tb, shapes, M, grouped):
     return all(tb.forward_f32_workspace_bytes(M, P.N, P.K) == 0 for P in shapes)
 
 
-def kernel_family(M):
-    return "k_decode" if M <= 16 else "k_gemm"
+# Kernel names as the library reports them (bitlinear_forward_kernel), and the
+# symbols they appear under in a profile.
+KERNEL_SYMBOLS = {"k_decode_dot": ("k_decode_dot",), "k_decode": ("k_decode_lds", "k_decode_reg"),
+                  "k_skinny": ("k_skinny",), "k_gemm": ("k_gemm",)}
+
+
+def step_kernels(tb, shapes, M, grouped, fused):
+    """The kernel(s) the step's projection launches run, '+'-joined when the
+    projections of a step differ."""
+    entry = "f32" if fused else "forward"
+    if grouped:
+        names = {tb.forward_kernel(entry, M, [P.N for P in shapes], shapes[0].K)[0]}
+    else:
+        names = {tb.forward_kernel(entry, M, [P.N], P.K)[0] for P in shapes}
+    return "+".join(sorted(names))
+
+
+def kernel_matches(kernels, name):
+    """True when a profiled kernel name is one of `kernels` ('+'-joined)."""
+    return any(sym + "<" in name for k in kernels.split("+") for sym in KERNEL_SYMBOLS[k])
 
 
 def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream, grouped=False,
@@ -442,9 +461,10 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     api = ("bitlinear_forward_f32" if fused else "bitlinear_forward") + ("_grouped" if grouped else "")
+    kern = step_kernels(tb, shapes, M, grouped, fused)
     roof.update({
-        "traffic": load_traffic(kernel_family(M), projs, M, out, fused),
-        "kernel": kernel_family(M), "entry_point": api,
+        "traffic": load_traffic(kern, projs, M, out, fused),
+        "kernel": kern, "entry_point": api,
         "shape": f"M{M} " + ", ".join(f"{P.K}->{P.N}" for P in shapes),
         "us_per_launch": round(t_launch * 1e6, 3), "launches_timed": n_launch,
         "algorithmic_bytes_per_launch": int(bytes_launch),
@@ -492,8 +512,9 @@ def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=Fal
                 tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
                                      N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": traffic_key(kernel_family(M), [q["p"] for q in projs], M,
-                                                   out, fused_step is not None),
+    shapes = [q["p"] for q in projs]
+    kern = step_kernels(tb, shapes, M, grouped, fused_step is not None)
+    print(json.dumps({"traffic_probe": traffic_key(kern, shapes, M, out, fused_step is not None),
                       "workload": wl.name, "calibration_bytes": CAL_BYTES,
                       "launches": copies * (1 if grouped else len(projs))}), flush=True)
 
@@ -524,18 +545,18 @@ def traffic_from(args):
     from synth import WORKLOADS
     wl = WORKLOADS[args.workload]
     M = args.tokens or wl.tokens[0]
-    fam = kernel_family(M)
     shapes = list(wl.projections)
     import ternary_bitlinear_amd as tb   # size queries only: no GPU
     tb.load()
     fused = step_is_fused(tb, shapes, M, wl.shared_input)
+    fam = step_kernels(tb, shapes, M, wl.shared_input, fused)
     key = traffic_key(fam, shapes, M, wl.out_dtype, fused)
     out = {}
     for what, d, cname in (("fetch", args.traffic_from[0], "FETCH_SIZE"),
                            ("write", args.traffic_from[1], "WRITE_SIZE")):
         c = _counters(d, cname)
         cal = [v for kn, v in c.values() if "neg" in kn.lower()]
-        ker = [v for kn, v in c.values() if fam in kn]
+        ker = [v for kn, v in c.values() if kernel_matches(fam, kn)]
         # a projection with K split across workgroups is two dispatches
         red = [v for kn, v in c.values() if "k_splitk_reduce" in kn]
         if len(cal) != 1 or not ker:

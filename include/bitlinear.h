@@ -307,6 +307,30 @@ bitlinear_status bitlinear_forward_rmsnorm_grouped(int G, const uint8_t* const* 
                                                    int32_t* x_sum_out, void* workspace,
                                                    size_t workspace_bytes, void* stream);
 
+/* Kernels a forward call may launch (values of bitlinear_forward_kernel). */
+typedef enum bitlinear_kernel {
+  BITLINEAR_KERNEL_DECODE_DOT = 1, /* one token: dot products on the vector ALU */
+  BITLINEAR_KERNEL_DECODE = 2,     /* up to 16 tokens: matrix instructions, weights streamed once */
+  BITLINEAR_KERNEL_SKINNY = 3,     /* 2-64 tokens: activations and codes through an LDS ring */
+  BITLINEAR_KERNEL_GEMM = 4,       /* tiled matrix product (K split over workgroups when tiles are few) */
+  BITLINEAR_KERNEL_FUSED_QUANT = 16 /* or'ed in: the activation quantiser runs in the same launch */
+} bitlinear_kernel;
+
+/*
+ * Which kernel a forward call launches for these sizes, for profiling and
+ * for callers that budget per kernel.  Host only: no GPU call, no state.
+ * entry   0: bitlinear_forward / bitlinear_forward_grouped;
+ *         1: bitlinear_forward_f32 / _f32_grouped;
+ *         2: bitlinear_forward_rmsnorm / _rmsnorm_grouped.
+ * M, K    as in those calls; G, N the group (G = 1, N = &n for one projection).
+ * Returns a bitlinear_kernel value, with BITLINEAR_KERNEL_FUSED_QUANT or'ed
+ * in when the quantiser (and normalisation) runs inside that launch; when it
+ * is absent for entry 1 or 2 a quantiser launch comes first.  Returns
+ * -BITLINEAR_ERR_SHAPE for sizes the call would reject (or an entry other
+ * than 0, 1, 2).
+ */
+int bitlinear_forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K);
+
 /* Static English name of a status. */
 const char* bitlinear_status_string(bitlinear_status s);
 

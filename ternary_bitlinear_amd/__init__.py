@@ -5,6 +5,7 @@ include/bitlinear.h; this package is its Python binding.
 """
 from .binding import (  # noqa: F401
     DTYPES,
+    KERNELS,
     LIB_PATH,
     SIGNATURES,
     STATUS,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     forward_f32_grouped_workspace_bytes,
     forward_f32_workspace_bytes,
     forward_grouped_workspace_bytes,
+    forward_kernel,
     forward_rmsnorm_grouped_workspace_bytes,
     forward_rmsnorm_workspace_bytes,
     forward_workspace_bytes,

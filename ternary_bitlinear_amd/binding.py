@@ -49,6 +49,7 @@ SIGNATURES = {
     "bitlinear_forward_rmsnorm_grouped": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i64, _vp,
                                                          _vp, _c_i64, _vp, ctypes.c_int, _vp, _vp,
                                                          _vp, _vp, _c_size, _vp]),
+    "bitlinear_forward_kernel": (ctypes.c_int, [ctypes.c_int, _c_i64, ctypes.c_int, _vp, _c_i64]),
     "bitlinear_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -341,6 +342,19 @@ def bitlinear_forward_rmsnorm_grouped(W_packed, gamma, X, norm_g, Ns=None, y_dty
 
 def forward_rmsnorm_grouped_workspace_bytes(M: int, Ns, K: int) -> int:
     return load().bitlinear_forward_rmsnorm_grouped_workspace_bytes(M, len(Ns), _i64_array(Ns), K)
+
+
+KERNELS = {1: "k_decode_dot", 2: "k_decode", 3: "k_skinny", 4: "k_gemm"}
+ENTRIES = {"forward": 0, "f32": 1, "rmsnorm": 2}
+
+
+def forward_kernel(entry: str, M: int, Ns, K: int):
+    """(kernel name, quantiser fused) that the forward entry point ("forward",
+    "f32" or "rmsnorm", single or grouped over Ns) launches for these sizes."""
+    r = load().bitlinear_forward_kernel(ENTRIES[entry], M, len(Ns), _i64_array(Ns), K)
+    if r < 0:
+        raise BitLinearError(-r, f"forward_kernel: invalid sizes M={M} Ns={list(Ns)} K={K}")
+    return KERNELS[r & 15], bool(r & 16)
 
 
 def _forward_f32_grouped(W_packed, gamma, X, norm_g, Ns, y_dtype, Y, X_q_out, x_scale_out,

@@ -390,6 +390,20 @@ bitlinear_status bitlinear_forward_rmsnorm_grouped(int G, const uint8_t* const* 
                                   workspace_bytes, stream);
 }
 
+int bitlinear_forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K) {
+  if (entry < 0 || entry > 2 || G < 1 || G > BITLINEAR_MAX_GROUP || !N || M < 1 ||
+      M > kMaxDim || !shape_ok_k(K))
+    return -BITLINEAR_ERR_SHAPE;
+  for (int g = 0; g < G; ++g)
+    if (N[g] < 1 || N[g] > kMaxDim) return -BITLINEAR_ERR_SHAPE;
+  static_assert(BITLINEAR_KERNEL_DECODE_DOT == bl::kKernelDecodeDot &&
+                    BITLINEAR_KERNEL_DECODE == bl::kKernelDecode &&
+                    BITLINEAR_KERNEL_SKINNY == bl::kKernelSkinny &&
+                    BITLINEAR_KERNEL_GEMM == bl::kKernelGemm,
+                "kernel ids");
+  return bl::forward_kernel(entry, M, G, N, K);
+}
+
 const char* bitlinear_status_string(bitlinear_status s) {
   switch (s) {
     case BITLINEAR_OK: return "ok";

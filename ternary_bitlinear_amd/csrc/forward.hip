@@ -1400,6 +1400,256 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs ga) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny projections: a few dozen tokens (M <= 16 TG), K % 64 == 0.
+//
+// Between the single-token decode and the GEMM.  A workgroup owns RB blocks
+// of 16 weight rows and runs NWK waves per block; K advances in chunks of
+// CK = 256 NWK, and wave kw of a block takes chunk group kw (256 k) of every
+// chunk.  Per chunk group a lane takes one 16-byte piece of its row (64
+// codes) and issues 4 TG matrix instructions (16x16x64), one per token group.
+// Activations and codes both stream through an LDS ring of NS = SP + 1
+// stages, SP chunks ahead, filled with direct loads of the same count per
+// wave and step, so one vmcnt wait per step retires exactly the stage about
+// to be read (a ring of registers carried across the loop would make the
+// compiler drain every load at the loop head).  With about one workgroup per
+// CU (RB ~ row blocks / 256), the activations are read from L2 about once per
+// CU rather than once per output tile, and every SIMD runs RB NWK / 4 waves.
+//
+// Stage layouts (16-byte pieces XOR-swizzled by row, so that the lanes of a
+// fragment read, 16 rows and one piece, fall in different bank groups):
+//   activations [16 TG token rows][CK bytes], piece q of row r at q ^ (r & 15);
+//   codes       [RB][16 rows][64 NWK bytes], piece q of row r at q ^ (r & (4 NWK - 1)).
+// Rows past M or N and pieces past K are loaded from clamped addresses
+// (garbage): past M or N the outputs are not stored; past K the codes are
+// masked to 0, which contributes nothing.
+// ---------------------------------------------------------------------------
+// One step of k_skinny: issue the direct loads of a later chunk into (An, Bn)
+// and run the current chunk from (Ac, Bc).  The __restrict__ qualifiers tell
+// the compiler the two stages are disjoint (as in gemm_step).
+template <int TG, int NWK, typename Issue>
+__device__ __forceinline__ void skinny_step(const int8_t* __restrict__ Ac,
+                                            const uint8_t* __restrict__ Bc,
+                                            int8_t* __restrict__ An, uint8_t* __restrict__ Bn,
+                                            Issue issue, int wr, int qw, int j, uint32_t wmask,
+                                            i32x4 (&acc)[TG]) {
+  constexpr int CK = 256 * NWK, WROW = 64 * NWK, WSW = 4 * NWK - 1;
+  issue(An, Bn);
+  const uint4 wv = *reinterpret_cast<const uint4*>(Bc + wr * WROW + 16 * (qw ^ (wr & WSW)));
+  const uint32_t w4[4] = {wv.x & wmask, wv.y & wmask, wv.z & wmask, wv.w & wmask};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const i32x4 b = expand_codes(w4[t]);
+    const int q = 4 * qw + t;                   // 16-byte piece of the chunk (k = 16 q ..)
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      const int r = 16 * tg + j;
+      const i32x4 a = *reinterpret_cast<const i32x4*>(Ac + r * CK + 16 * (q ^ (r & 15)));
+      acc[tg] = mfma_i8_16x16x64(a, b, acc[tg]);
+    }
+  }
+}
+
+// Work unit: one workgroup (RB row blocks of one projection).
+template <int TG, int RB, int NWK, int SP, int OUT>
+__global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
+  constexpr int NWV = RB * NWK;               // waves
+  constexpr int CK = 256 * NWK;               // k per chunk
+  constexpr int NS = SP + 1;                  // ring stages
+  constexpr int ROWS = 16 * TG;
+  constexpr int XSTAGE = ROWS * CK;           // activation bytes per stage
+  constexpr int XBLOCKS = XSTAGE / 1024;      // 1 KB direct loads per stage
+  constexpr int XL = (XBLOCKS + NWV - 1) / NWV;   // per wave (the last one repeated)
+  constexpr int WROW = 64 * NWK;              // code bytes of one row per chunk
+  constexpr int WSTAGE = RB * 16 * WROW;      // = NWV KB: one direct load per wave
+  constexpr int NLD = XL + 1;                 // loads per wave per step
+  constexpr int WSW = 4 * NWK - 1;            // code piece swizzle mask
+  static_assert(XSTAGE % 1024 == 0 && WSTAGE == NWV * 1024, "stage");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(RB * (NWK - 1) * TG * kWave * 16 <= XSTAGE, "partial tiles fit stage 0");
+  // One array per stage, so that every access names its stage at compile
+  // time and the compiler can tell the stage being read from the one being
+  // filled (one array of stages would make it wait for every load in flight).
+#define BL_SX(i) sX##i[NS > i ? XSTAGE : 16]
+#define BL_SW(i) sW##i[NS > i ? WSTAGE : 16]
+  __shared__ __attribute__((aligned(1024))) int8_t BL_SX(0), BL_SX(1), BL_SX(2), BL_SX(3);
+  __shared__ __attribute__((aligned(1024))) uint8_t BL_SW(0), BL_SW(1), BL_SW(2), BL_SW(3);
+#undef BL_SX
+#undef BL_SW
+  int8_t* const sX[4] = {sX0, sX1, sX2, sX3};
+  uint8_t* const sW[4] = {sW0, sW1, sW2, sW3};
+
+  const DecodeView view = decode_view(da, blockIdx.x);
+  const int N = view.N, K = da.K, M = da.M;
+  const uint8_t* const Wp = view.Wp;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = wave / NWK, kw = wave - rb * NWK;
+  const int j = lane & 15, g = lane >> 4;
+  const int nb0 = view.unit * RB;             // first row block of the workgroup
+  const int npieces = K / 64;
+  const int kbytes = K / 4;
+  const int nch = (K + CK - 1) / CK;
+
+  // Epilogue inputs now, so no memory round trip follows the reduction.
+  const float gamma = view.gamma[0];
+  int32_t sxv[TG][4];
+  float scv[TG][4];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = min(16 * tg + 4 * g + r, M - 1);
+      sxv[tg][r] = da.xsum[m];
+      scv[tg][r] = da.xs[m];
+    }
+
+  // Direct loads of chunk c: activation blocks wave, wave + NWV, ... and the
+  // code block `wave`.  Lane l fills the 16-byte slot at 1024 b + 16 l of its
+  // block: activation row r = slot / CK, position q' within the row, source
+  // piece q' ^ (r & 15); code row block b / NWK, row r = slot / WROW within
+  // the workgroup's stage, position q', source piece q' ^ (r & WSW).
+  auto issue = [&](int c, int8_t* A, uint8_t* B) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int b = min(wave + NWV * i, XBLOCKS - 1);
+      const int off = 1024 * b + 16 * lane;
+      const int r = off / CK;
+      const int q = ((off % CK) / 16) ^ (r & 15);
+      const int m = min(r, M - 1);
+      const int k = min(c * CK + 16 * q, K - 16);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(da.Xq + (int64_t)m * K + k),
+                                       static_cast<void*>(A + 1024 * b), 16, 0, 0);
+    }
+    {
+      const int off = 1024 * wave + 16 * lane;
+      const int r = off / WROW;                 // row within the workgroup's 16 RB rows
+      const int q = ((off % WROW) / 16) ^ (r & WSW);
+      const int n = min(16 * nb0 + r, N - 1);
+      const int kb = min(c * (CK / 4) + 16 * q, kbytes - 16);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Wp + (int64_t)n * kbytes + kb),
+                                       static_cast<void*>(B + 1024 * wave), 16, 0, 0);
+    }
+  };
+
+  i32x4 acc[TG];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) acc[tg] = i32x4{0, 0, 0, 0};
+
+  const int wr = 16 * rb + j;                   // this lane's code row in the stage
+  const int qw = 4 * kw + g;                    // and its piece of the chunk
+#pragma unroll
+  for (int s = 0; s < SP; ++s) issue(min(s, nch - 1), sX[s], sW[s]);
+  for (int c0 = 0; c0 < nch; c0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = c0 + s;
+      if (c >= nch) break;
+      // This wave's loads of chunk c have landed (the SP - 1 younger chunks
+      // may still be in flight); after the barrier every wave's have, and
+      // every wave has finished chunk c - 1, whose stage is refilled below.
+      wait_vmcnt<(SP - 1) * NLD>();
+      stage_barrier();
+      // pieces past K: code 0 (the mask does not depend on the loaded value)
+      const uint32_t wmask = c * (CK / 64) + qw < npieces ? 0xffffffffu : 0u;
+      skinny_step<TG, NWK>(sX[s], sW[s], sX[(s + SP) % NS], sW[(s + SP) % NS],
+                           [&](int8_t* An, uint8_t* Bn) { issue(min(c + SP, nch - 1), An, Bn); },
+                           wr, qw, j, wmask, acc);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // Waves kw > 0 hand their partial tiles to wave kw = 0 of their row block.
+  if constexpr (NWK > 1) {
+    __syncthreads();   // every wave is done with the stages
+    i32x4* red = reinterpret_cast<i32x4*>(sX0);   // [RB][NWK - 1][TG][64]
+    if (kw > 0) {
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+        red[((rb * (NWK - 1) + kw - 1) * TG + tg) * kWave + lane] = acc[tg];
+    }
+    __syncthreads();
+    if (kw > 0) return;
+#pragma unroll
+    for (int w2 = 0; w2 < NWK - 1; ++w2)
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        const i32x4 o = red[((rb * (NWK - 1) + w2) * TG + tg) * kWave + lane];
+        acc[tg].x += o.x; acc[tg].y += o.y; acc[tg].z += o.z; acc[tg].w += o.w;
+      }
+  }
+  // Lane (j, g) register r of token group tg: token 16 tg + 4 g + r, row n.
+  const int n = 16 * (nb0 + rb) + j;
+  if (n >= N) return;
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    const int32_t v[4] = {acc[tg].x, acc[tg].y, acc[tg].z, acc[tg].w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * tg + 4 * g + r;
+      if (m < M) store_out<OUT>(view.Y, (int64_t)m * N + n, v[r] - sxv[tg][r], gamma, scv[tg][r]);
+    }
+  }
+}
+
+template <int TG, int RB, int NWK, int SP, int OUT>
+hipError_t launch_skinny_t(DecodeArgs da, hipStream_t stream) {
+  const int grid = set_units(da, 16 * RB);
+  k_skinny<TG, RB, NWK, SP, OUT><<<dim3(grid), dim3(RB * NWK * kWave), 0, stream>>>(da);
+  return hipGetLastError();
+}
+
+// Where the skinny kernel takes a projection (or a group of them sharing the
+// activations), `rows` being all output rows, each projection's rounded up
+// to 16.  Timed on MI355X against the matrix decode and the GEMM on the 3B,
+// 7B and 70B projections:
+//   2-7 tokens: the matrix decode keeps more weight loads in flight on
+//     narrow outputs (< 384 row blocks), and at 2 tokens on matrices of
+//     less than 2^27 weights;
+//   33-64 tokens: the GEMM's K split wins once a workgroup's activations
+//     outgrow its codes (M K > 256 Ki, e.g. 4096 <- 11008 at 64 tokens).
+inline int64_t group_rows(int G, const int64_t* N) {
+  int64_t rows = 0;
+  for (int g = 0; g < G; ++g) rows += 16 * ((N[g] + 15) / 16);
+  return rows;
+}
+
+inline bool skinny_ok(int64_t M, int64_t rows, int64_t K) {
+  if (K % 64 != 0 || M < 2 || M > 64) return false;
+  if (M > 32) return M * K <= 256 * 1024;
+  if (M >= 8) return true;
+  if (rows < 16 * 384) return false;
+  return M > 2 || rows * K >= (int64_t(1) << 27);
+}
+
+// About 256 workgroups of 8 waves: 4 row blocks of 2 waves on wide outputs
+// (>= 640 row blocks), 2 of 4 waves on mid ones, 1 of 4 waves on narrow
+// ones (each wave of a row block takes a quarter or half of every chunk).
+// Rings of 3 stages, 2 above 16 tokens (LDS).
+template <int TG, int OUT>
+hipError_t launch_skinny_tg(const DecodeArgs& da, int nrb, hipStream_t stream) {
+  constexpr int SP = TG == 1 ? 3 : 2;
+  if (nrb >= 640) return launch_skinny_t<TG, 4, 2, SP, OUT>(da, stream);
+  if (nrb >= 384) return launch_skinny_t<TG, 2, 4, SP, OUT>(da, stream);
+  return launch_skinny_t<TG, 1, 4, SP, OUT>(da, stream);
+}
+
+template <int OUT>
+hipError_t launch_skinny(const DecodeArgs& da, hipStream_t stream) {
+  const int nrb = decode_rows(da) / 16;
+  if (da.M <= 16) return launch_skinny_tg<1, OUT>(da, nrb, stream);
+  if (da.M <= 32) return launch_skinny_tg<2, OUT>(da, nrb, stream);
+  // 33-64 tokens (activation stages of 32 KB): 2 waves per row block, about
+  // 256 workgroups of up to 4 row blocks.
+  switch (std::min(4, std::max(1, (nrb + 255) / 256))) {
+    case 1: return launch_skinny_t<4, 1, 2, 2, OUT>(da, stream);
+    case 2: return launch_skinny_t<4, 2, 2, 2, OUT>(da, stream);
+    case 3: return launch_skinny_t<4, 3, 2, 2, OUT>(da, stream);
+    default: return launch_skinny_t<4, 4, 2, 2, OUT>(da, stream);
+  }
+}
+
+
 struct GemmCfg {
   int bm, bn;
   int splits;   // K splits (1: none)
@@ -1489,11 +1739,12 @@ hipError_t dispatch_out(const uint8_t* Wp, const float* gamma, int N, int K, con
 }  // namespace
 
 size_t forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16) return 0;
+  if (M <= 16 || skinny_ok(M, 16 * ((N + 15) / 16), K)) return 0;
   return gemm_workspace_bytes(gemm_cfg((int)M, (int)N, (int)K), M, N);
 }
 
 size_t forward_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K) {
+  if (M <= 16 || skinny_ok(M, group_rows(G, N), K)) return 0;   // one launch over the group
   size_t need = 0;
   for (int g = 0; g < G; ++g) need = std::max(need, forward_workspace_bytes(M, N[g], K));
   return need;
@@ -1520,14 +1771,16 @@ hipError_t forward_grouped_out(int G, const uint8_t* const* Wp, const float* con
                                const int64_t* N, int K, const int8_t* Xq, const float* xs,
                                const int32_t* xsum, int M, void* const* Y, void* workspace,
                                hipStream_t stream) {
-  if (M <= 16) {
-    DecodeArgs da = decode_args_group(G, Wp, gamma, N, K, M, Y);
-    da.Xq = Xq;
-    da.xs = xs;
-    da.xsum = xsum;
+  DecodeArgs da = decode_args_group(G, Wp, gamma, N, K, M, Y);
+  da.Xq = Xq;
+  da.xs = xs;
+  da.xsum = xsum;
+  // Every projection of the group in one launch where the skinny kernel or
+  // the decode takes the shape.
+  if (skinny_ok(M, decode_rows(da), K)) return launch_skinny<OUT>(da, stream);
+  if (M <= 16)
     return K % 64 == 0 ? decode_grouped<true, OUT>(da, stream)
                        : decode_grouped<false, OUT>(da, stream);
-  }
   // GEMM shapes: one projection after another (the workspace is reused in
   // stream order).
   for (int g = 0; g < G; ++g) {
@@ -1609,11 +1862,18 @@ hipError_t fused_dot_norm(const DecodeArgs& da, hipStream_t stream) {
 }
 }  // namespace
 
+// The matrix decode with the quantiser in its prologue, where the skinny
+// kernel does not take the shape (the quantiser then runs on its own: timed
+// faster for the 7B projections at 8 and 16 tokens).
+inline bool afuse(int64_t M, int G, const int64_t* N, int64_t K) {
+  return fused_cfg(M, G, N, K).am == kAFuse && !skinny_ok(M, group_rows(G, N), K);
+}
+
 // norm: RMS normalisation first; the single-token vector-ALU prologue fuses
 // it, the multi-token matrix prologue does not (two launches there).
 size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K,
                                            bool norm) {
-  if (fused_dot(M, K) || (!norm && fused_cfg(M, G, N, K).am == kAFuse)) return 0;
+  if (fused_dot(M, K) || (!norm && afuse(M, G, N, K))) return 0;
   return quant_region_bytes(M, K) + forward_grouped_workspace_bytes(M, G, N, K);
 }
 
@@ -1648,8 +1908,8 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
       default: return fused_dot_norm<kOutI32>(da, stream);
     }
   }
-  const DecodeCfg c = fused_cfg(M, G, N, K);
-  if (c.am == kAFuse && norm_g == nullptr) {
+  if (norm_g == nullptr && afuse(M, G, N, K)) {
+    const DecodeCfg c = fused_cfg(M, G, N, K);
     DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);
     da.X = X;
     da.Xq_out = X_q_out;
@@ -1680,6 +1940,17 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
   if (e != hipSuccess) return e;
   return launch_forward_grouped(G, W_packed, gamma, N, K, xq, xs, xsum, M, Y, y_dtype, fws,
                                 stream);
+}
+
+int forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K) {
+  constexpr int kFused = 16;
+  if (entry != 0) {
+    if (fused_dot(M, K)) return kKernelDecodeDot | kFused;
+    if (entry == 1 && afuse(M, G, N, K)) return kKernelDecode | kFused;
+  }
+  if (skinny_ok(M, group_rows(G, N), K)) return kKernelSkinny;
+  if (M <= 16) return M == 1 && K % 64 == 0 && K <= 64 * 64 ? kKernelDecodeDot : kKernelDecode;
+  return kKernelGemm;
 }
 
 hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64_t N, int64_t K,

@@ -61,4 +61,10 @@ hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64
                               int y_dtype, int8_t* X_q_out, float* x_scale_out,
                               int32_t* x_sum_out, void* workspace, hipStream_t stream);
 
+// The kernel a forward call launches for these sizes (host only): entry 0
+// for the pre-quantised projection, 1 for the fp32 one, 2 with the RMS
+// normalisation; kKernel* or'ed with 16 when the quantiser runs inside it.
+constexpr int kKernelDecodeDot = 1, kKernelDecode = 2, kKernelSkinny = 3, kKernelGemm = 4;
+int forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K);
+
 }  // namespace bl

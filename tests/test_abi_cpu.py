@@ -64,17 +64,19 @@ def test_size_queries(lib):
     assert 256 < ws <= 256 + 8192 * 10 * 8
     assert lib.bitlinear_pack_workspace_bytes(1, 16) >= 256 + 4 * 80
     assert lib.bitlinear_pack_workspace_bytes(1 << 20, 1 << 12) == 0   # N*K >= 2^31
-    # decode (M <= 16) and many-tile shapes need no workspace; few tiles with a
-    # long K split K: S int32 partial tiles, S <= K / (16 M), 256-byte rounded
+    # decode (M <= 16), skinny (M <= 64, M K <= 256 Ki) and many-tile shapes
+    # need no workspace; few tiles with a long K split K: S int32 partial
+    # tiles, S <= K / (16 M), 256-byte rounded
     assert lib.bitlinear_forward_workspace_bytes(4, 4096, 4096) == 0
+    assert lib.bitlinear_forward_workspace_bytes(64, 4096, 4096) == 0
     assert lib.bitlinear_forward_workspace_bytes(2048, 11008, 4096) == 0
-    ws = lib.bitlinear_forward_workspace_bytes(64, 4096, 4096)
+    ws = lib.bitlinear_forward_workspace_bytes(64, 4096, 4160)
     assert ws == 4 * 64 * 4096 * 4
     ws = lib.bitlinear_forward_workspace_bytes(64, 4096, 11008)
     assert ws % (64 * 4096 * 4) == 0 and 2 <= ws // (64 * 4096 * 4) <= 16
     assert lib.bitlinear_forward_workspace_bytes(0, 4096, 4096) == 0
-    f32 = lib.bitlinear_forward_f32_workspace_bytes(64, 4096, 4096)
-    assert f32 >= 64 * 4096 + 8 * 64 + 4 * 64 * 4096 * 4
+    f32 = lib.bitlinear_forward_f32_workspace_bytes(64, 4096, 4160)
+    assert f32 >= 64 * 4160 + 8 * 64 + 4 * 64 * 4096 * 4
 
 
 def _last(lib):
@@ -109,8 +111,8 @@ def test_validation_statuses_without_gpu_calls(lib):
     bad = list(args); bad[8] = FAKE + 1     # bf16 Y needs 2-byte alignment
     assert lib.bitlinear_forward(*bad) == 3
     # a split-K shape: workspace missing, too small, misaligned
-    split = [FAKE, FAKE, 4096, 4096, FAKE, FAKE, FAKE, 64, FAKE, 1, None, 0, None]
-    need = lib.bitlinear_forward_workspace_bytes(64, 4096, 4096)
+    split = [FAKE, FAKE, 4096, 4160, FAKE, FAKE, FAKE, 64, FAKE, 1, None, 0, None]
+    need = lib.bitlinear_forward_workspace_bytes(64, 4096, 4160)
     assert lib.bitlinear_forward(*split) == 7 and "workspace" in _last(lib)
     bad = list(split); bad[10] = FAKE; bad[11] = need - 16
     assert lib.bitlinear_forward(*bad) == 7
@@ -144,9 +146,10 @@ def test_grouped_validation_without_gpu_calls(lib):
     assert call(K=40) == 2 and call(dt=9) == 4
     # decode shapes need no workspace; a split GEMM group needs the largest member's
     assert lib.bitlinear_forward_grouped_workspace_bytes(1, 3, ns, 4096) == 0
-    big = lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 4096)
-    assert big == max(lib.bitlinear_forward_workspace_bytes(64, n, 4096) for n in (4096, 1024, 1024))
-    assert big > 0 and call(M=64) == 7
+    assert lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 4096) == 0   # skinny
+    big = lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 4160)
+    assert big == max(lib.bitlinear_forward_workspace_bytes(64, n, 4160) for n in (4096, 1024, 1024))
+    assert big > 0 and call(M=64, K=4160) == 7
     assert lib.bitlinear_forward_grouped_workspace_bytes(1, 5, ns, 4096) == 0
     f32 = lib.bitlinear_forward_f32_grouped(3, ptrs, ptrs, ns, 4096, None, 1, ptrs, 1,
                                             None, None, None, None, 0, None)
@@ -187,3 +190,42 @@ def test_rmsnorm_validation_without_gpu_calls(lib):
     assert lib.bitlinear_forward_rmsnorm_grouped_workspace_bytes(1, 3, ns, 4096) == 0
     assert lib.bitlinear_forward_rmsnorm_grouped_workspace_bytes(4, 3, ns, 4096) > 0
     assert lib.bitlinear_forward_rmsnorm_grouped_workspace_bytes(4, 5, ns, 4096) == 0
+
+
+def test_forward_kernel_query(lib):
+    """The host-side kernel choice: fixed points of the dispatch rule, and
+    agreement with the workspace queries (a fused launch needs none, only the
+    GEMM asks for projection workspace)."""
+    import ctypes
+    import ternary_bitlinear_amd as tb
+    fk = tb.forward_kernel
+    assert fk("forward", 1, [4096], 4096) == ("k_decode_dot", False)
+    assert fk("f32", 1, [4096], 4096) == ("k_decode_dot", True)
+    assert fk("rmsnorm", 1, [4096], 11008) == ("k_decode_dot", True)
+    assert fk("forward", 1, [4096], 11008) == ("k_decode", False)
+    assert fk("forward", 4, [4096], 4096) == ("k_decode", False)        # narrow, few tokens
+    assert fk("forward", 4, [11008], 4096) == ("k_skinny", False)       # wide
+    assert fk("forward", 4, [4096, 1024, 1024], 4096) == ("k_skinny", False)
+    assert fk("forward", 2, [11008], 4096) == ("k_decode", False)
+    assert fk("forward", 2, [28672], 8192) == ("k_skinny", False)
+    assert fk("forward", 8, [4096], 4096) == ("k_skinny", False)
+    assert fk("forward", 8, [4096], 4112) == ("k_decode", False)        # K % 64 != 0
+    assert fk("forward", 32, [4096], 28672) == ("k_skinny", False)
+    assert fk("forward", 64, [4096], 4096) == ("k_skinny", False)
+    assert fk("forward", 64, [4096], 11008) == ("k_gemm", False)
+    assert fk("forward", 2048, [11008], 4096) == ("k_gemm", False)
+    assert fk("f32", 8, [4096] * 3, 4096) == ("k_skinny", False)        # quantiser first
+    assert fk("f32", 4, [4096], 4096) == ("k_decode", True)
+    assert fk("rmsnorm", 4, [4096], 4096) == ("k_decode", False)
+    n1 = (ctypes.c_int64 * 1)(4096)
+    assert lib.bitlinear_forward_kernel(3, 1, 1, n1, 4096) == -2
+    assert lib.bitlinear_forward_kernel(0, 1, 1, n1, 40) == -2
+    assert lib.bitlinear_forward_kernel(0, 1, 0, n1, 4096) == -2
+    assert lib.bitlinear_forward_kernel(0, 0, 1, n1, 4096) == -2
+    for M in (1, 2, 3, 4, 8, 16, 17, 32, 48, 64, 65, 2048):
+        for N, K in ((4096, 4096), (11008, 4096), (4096, 11008), (3200, 8640), (28672, 8192),
+                     (300, 1040), (64, 64)):
+            name, fused = fk("f32", M, [N], K)
+            assert fused == (tb.forward_f32_workspace_bytes(M, N, K) == 0), (M, N, K)
+            if tb.forward_workspace_bytes(M, N, K) > 0:
+                assert fk("forward", M, [N], K)[0] == "k_gemm", (M, N, K)

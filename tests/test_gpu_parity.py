@@ -138,11 +138,12 @@ def test_quant_edge_rows(gpu_lib):
 
 # --------------------------------------------------------------------------- forward
 FWD_SHAPES = [
-    # decode path (M <= 16)
+    # matrix decode (M <= 16; one token with K > 4096, or K % 64 != 0); the
+    # skinny kernel for the rest of M >= 2
     (1, 1, 16), (1, 16, 64), (1, 17, 80), (2, 33, 1040), (5, 129, 512), (16, 300, 4096),
     (7, 64, 8640), (1, 3200, 8640),
     # decode with 2 and 4 row blocks per workgroup (needs >= 256 workgroups), ragged N
-    (7, 8200, 80), (13, 16400, 1040), (16, 16384, 256),
+    (7, 8200, 80), (13, 16400, 1040), (16, 16384, 272),
     # single token on the vector ALU (K % 64 == 0, K <= 4096): one piece per
     # row, N below and not a multiple of the rows per wave, full rows
     (1, 1, 64), (1, 3, 4096), (1, 1001, 192), (1, 8640, 3200), (1, 11008, 4096),
@@ -152,6 +153,16 @@ FWD_SHAPES = [
     # K split across workgroups (partial sums + reduction): with a K tail, with
     # N % 4 != 0 (scalar partial stores), two row tiles
     (24, 200, 4160), (40, 130, 2064), (100, 64, 8192),
+    # skinny kernel (K % 64 == 0; 8-32 tokens, 2-7 on wide outputs, 33-64
+    # with M K <= 256 Ki): fewer chunks than ring stages, K ending inside a
+    # chunk, ragged N in the last workgroup's row blocks, 1 row block of 4
+    # waves / 2 of 4 / 4 of 2 per workgroup, 16 / 32 / 64 token groups with
+    # ragged M
+    (2, 16384, 8192), (3, 6144, 64), (5, 10000, 128), (8, 100, 64), (9, 1, 128),
+    (8, 4099, 4096), (12, 4096, 11008), (16, 16400, 704), (16, 28672, 1024),
+    (17, 257, 576), (24, 4096, 11008), (31, 3000, 8192), (32, 6200, 3072),
+    (33, 1030, 2048), (48, 11990, 5440), (63, 4100, 4096), (64, 64, 4096), (64, 20, 64),
+    (45, 6000, 192),
 ]
 
 
@@ -193,7 +204,8 @@ def test_forward_extreme_accumulators(gpu_lib):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(1, 100, 512), (9, 77, 1040), (48, 200, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 100, 512), (9, 77, 1040), (48, 200, 2048),
+                                   (12, 1000, 3072), (40, 513, 6144)])
 def test_forward_rescale(gpu_lib, M, N, K, out):
     W = make_weight(0, f"test/fwd/{N}x{K}", N, K, 0.02)
     X = make_acts(0, f"test/fwd/X{M}x{K}", M, K, {})
@@ -374,6 +386,13 @@ GROUP_CASES = [
     (16, 8192, (2048, 1040)),
     (40, 4096, (512, 200)),
     (130, 1040, (300, 64)),
+    # one skinny launch over the group (workgroups never straddle two
+    # projections): 4 row blocks per workgroup, 2 of 4 waves, 1 of 4 waves,
+    # 64 tokens
+    (8, 4096, (4096, 4096, 4096)),
+    (32, 4096, (4096, 1024, 1024)),
+    (20, 2048, (1000, 17, 3, 2000)),
+    (64, 1024, (3000, 5000)),
 ]
 
 
