@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one plain copy of known size, then bitlinear_forward once per "
                          "projection and weight copy, and exit (for rocprofv3 --pmc runs)")
+    ap.add_argument("--probe-reps", type=int, default=1,
+                    help="with --traffic-probe: launches per weight copy (for a kernel trace)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn the FETCH_SIZE and WRITE_SIZE counter runs of "
                          "--traffic-probe into profiles/traffic.json")
@@ -163,7 +165,7 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped,
-                      step if fused_step else None)
+                      step if fused_step else None, reps=args.probe_reps)
         return
 
     def graph_of(fn_list):
@@ -481,11 +483,11 @@ CAL_BYTES = 256 << 20        # the calibration copy reads and writes this many b
 
 
 def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=False,
-                  fused_step=None):
+                  fused_step=None, reps=1):
     """One elementwise copy of CAL_BYTES (torch.neg on int32: reads and writes
-    CAL_BYTES), then the dominant kernel once per weight copy: the step's own
-    fused launches when it has nothing else (fused_step), else bitlinear_forward
-    once per projection (or bitlinear_forward_grouped once)."""
+    CAL_BYTES), then the dominant kernel `reps` times per weight copy: the
+    step's own fused launches when it has nothing else (fused_step), else
+    bitlinear_forward once per projection (or bitlinear_forward_grouped once)."""
     src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -496,27 +498,42 @@ def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=Fal
         if fused_step is None:
             for q in projs:
                 tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
-        for r in range(copies):
-            if fused_step is not None:
-                fused_step(r)
-                continue
-            if grouped:
-                tb.bitlinear_forward_grouped([q["Wc"][r % copies] for q in projs],
-                                             [q["g"] for q in projs], projs[0]["Xq"],
-                                             projs[0]["s"], projs[0]["xs"],
-                                             Ns=[q["p"].N for q in projs], K=projs[0]["p"].K,
-                                             y_dtype=out, Y=[q["Y"] for q in projs],
-                                             stream=stream)
-                continue
+    torch.cuda.synchronize()
+
+    def launch(r):
+        if fused_step is not None:
+            fused_step(r)
+        elif grouped:
+            tb.bitlinear_forward_grouped([q["Wc"][r % copies] for q in projs],
+                                         [q["g"] for q in projs], projs[0]["Xq"],
+                                         projs[0]["s"], projs[0]["xs"],
+                                         Ns=[q["p"].N for q in projs], K=projs[0]["p"].K,
+                                         y_dtype=out, Y=[q["Y"] for q in projs], stream=stream)
+        else:
             for q in projs:
                 tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
-                                     N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
+                                     N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"],
+                                     stream=stream)
+    if reps > 1:
+        # back to back as the bench times them: one graph over the weight
+        # copies, replayed `reps` times
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(copies):
+                    launch(r)
+        for _ in range(reps):
+            g.replay()
+    else:
+        with torch.cuda.stream(stream):
+            for r in range(copies):
+                launch(r)
     torch.cuda.synchronize()
     shapes = [q["p"] for q in projs]
     kern = step_kernels(tb, shapes, M, grouped, fused_step is not None)
     print(json.dumps({"traffic_probe": traffic_key(kern, shapes, M, out, fused_step is not None),
                       "workload": wl.name, "calibration_bytes": CAL_BYTES,
-                      "launches": copies * (1 if grouped else len(projs))}), flush=True)
+                      "launches": copies * reps * (1 if grouped else len(projs))}), flush=True)
 
 
 def _counters(d, name):
