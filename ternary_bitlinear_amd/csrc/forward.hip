@@ -1862,11 +1862,15 @@ hipError_t fused_dot_norm(const DecodeArgs& da, hipStream_t stream) {
 }
 }  // namespace
 
-// The matrix decode with the quantiser in its prologue, where the skinny
-// kernel does not take the shape (the quantiser then runs on its own: timed
-// faster for the 7B projections at 8 and 16 tokens).
+// The matrix decode with the quantiser in its prologue: one or two tokens,
+// where the skinny kernel does not take the shape.  Timed against the
+// quantiser launch + the unfused decode: faster at one token (70B down,
+// 8192 <- 28672: 19.0 vs 24.2 us) and two (3200 <- 8640: 7.7 vs 9.0 us);
+// slower from four tokens on (4096 <- 4096: 7.7 vs 7.1 us at 4, 8.3 vs
+// 7.3 us at 7), where every workgroup's re-quantisation of the fp32 rows
+// outweighs the saved launch.
 inline bool afuse(int64_t M, int G, const int64_t* N, int64_t K) {
-  return fused_cfg(M, G, N, K).am == kAFuse && !skinny_ok(M, group_rows(G, N), K);
+  return M <= 2 && fused_cfg(M, G, N, K).am == kAFuse && !skinny_ok(M, group_rows(G, N), K);
 }
 
 // norm: RMS normalisation first; the single-token vector-ALU prologue fuses

@@ -174,12 +174,14 @@ def test_rmsnorm_validation_without_gpu_calls(lib):
     # one token, K <= 12288 in steps of 64: fused, no workspace either way
     assert lib.bitlinear_forward_rmsnorm_workspace_bytes(1, 4096, 4096) == 0
     assert lib.bitlinear_forward_f32_workspace_bytes(1, 4096, 4096) == 0
-    # a few tokens: the quantiser alone fuses into the matrix decode, the
-    # normalising one takes two launches and needs the quantiser region
-    assert lib.bitlinear_forward_f32_workspace_bytes(4, 4096, 4096) == 0
-    need = lib.bitlinear_forward_rmsnorm_workspace_bytes(4, 4096, 4096)
-    assert need >= 4 * 4096 + 8 * 4
-    bad = list(args); bad[6] = 4
+    # two tokens: the quantiser alone fuses into the matrix decode, the
+    # normalising one takes two launches and needs the quantiser region; from
+    # four tokens both take two launches
+    assert lib.bitlinear_forward_f32_workspace_bytes(2, 4096, 4096) == 0
+    assert lib.bitlinear_forward_f32_workspace_bytes(4, 4096, 4096) >= 4 * 4096 + 8 * 4
+    need = lib.bitlinear_forward_rmsnorm_workspace_bytes(2, 4096, 4096)
+    assert need >= 2 * 4096 + 8 * 2
+    bad = list(args); bad[6] = 2
     assert lib.bitlinear_forward_rmsnorm(*bad) == 7 and "workspace" in _last(lib)
     # grouped form
     ptrs = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
@@ -215,7 +217,8 @@ def test_forward_kernel_query(lib):
     assert fk("forward", 64, [4096], 11008) == ("k_gemm", False)
     assert fk("forward", 2048, [11008], 4096) == ("k_gemm", False)
     assert fk("f32", 8, [4096] * 3, 4096) == ("k_skinny", False)        # quantiser first
-    assert fk("f32", 4, [4096], 4096) == ("k_decode", True)
+    assert fk("f32", 2, [4096], 4096) == ("k_decode", True)
+    assert fk("f32", 4, [4096], 4096) == ("k_decode", False)          # quantiser first
     assert fk("rmsnorm", 4, [4096], 4096) == ("k_decode", False)
     n1 = (ctypes.c_int64 * 1)(4096)
     assert lib.bitlinear_forward_kernel(3, 1, 1, n1, 4096) == -2

@@ -327,6 +327,53 @@ def test_workload_full_size(gpu_lib, wname, pname):
         torch.cuda.synchronize()
 
 
+GROUPED_FULL = [(wl.name, M) for wl in WORKLOADS.values() if wl.shared_input for M in wl.tokens]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wname,M", GROUPED_FULL, ids=[f"{w}:M{m}" for w, m in GROUPED_FULL])
+def test_workload_full_size_grouped(gpu_lib, wname, M):
+    """A workload whose projections share their input, at its real sizes, through
+    the grouped calls the bench times (one launch for all projections): the
+    quantiser's outputs and every projection's accumulators in full against the
+    oracle, and the bf16 outputs within tolerance."""
+    import torch
+    wl = WORKLOADS[wname]
+    ps = list(wl.projections)
+    K = ps[0].K
+    X = wl.acts(ps[0], M)
+    oq, os_, oxs, beta = O.quantize_activations(X)
+    Wp, gm, refs = [], [], []
+    for p in ps:
+        W = wl.weight(p)
+        gamma = O.absmean_gamma(W)
+        Wt = O.ternarize(W, gamma)
+        P, g = gpu_lib.bitlinear_pack_weights(dev(W))
+        Wp.append(P)
+        gm.append(g)
+        acc_ref = O.integer_matmul(Wt, oq)
+        refs.append((acc_ref, O.rescale(acc_ref, gamma, beta)))
+    kw = dict(X_q_out=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+              x_scale_out=torch.empty(M, dtype=torch.float32, device="cuda"),
+              x_sum_out=torch.empty(M, dtype=torch.int32, device="cuda"))
+    Xd = dev(X)
+    acc = gpu_lib.bitlinear_forward_f32_grouped(Wp, gm, Xd, y_dtype="i32", **kw)
+    Y = gpu_lib.bitlinear_forward_f32_grouped(Wp, gm, Xd, y_dtype=wl.out_dtype)
+    torch.cuda.synchronize()
+    assert_equal(host(kw["X_q_out"]), oq, "X~")
+    assert_equal(f32_bits(host(kw["x_scale_out"])), f32_bits(os_), "x_scale bits")
+    assert_equal(host(kw["x_sum_out"]).astype(np.int64), oxs, "x_sum")
+    for i, (acc_ref, y_ref) in enumerate(refs):
+        assert_equal(host(acc[i]).astype(np.int64), acc_ref, f"accumulators of projection {i}")
+        check_y(Y[i], y_ref, wl.out_dtype)
+    # the pre-quantised grouped call on the quantiser's outputs
+    acc2 = gpu_lib.bitlinear_forward_grouped(Wp, gm, kw["X_q_out"], kw["x_scale_out"],
+                                            kw["x_sum_out"], K=K, y_dtype="i32")
+    torch.cuda.synchronize()
+    for i, (acc_ref, _) in enumerate(refs):
+        assert_equal(host(acc2[i]).astype(np.int64), acc_ref, f"pre-quantised projection {i}")
+
+
 # --------------------------------------------------------------------------- fused quant + forward
 FUSED_SHAPES = [
     (1, 1, 16), (1, 40, 80), (2, 33, 1040), (3, 300, 4096), (5, 129, 512), (8, 64, 2048),
