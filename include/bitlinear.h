@@ -131,9 +131,10 @@ bitlinear_status bitlinear_quant_acts(const float* X, int64_t M, int64_t K,
                                       void* stream);
 
 /* Bytes of workspace bitlinear_forward needs: int32 partial accumulators
- * when the shape runs with K split across workgroups (few output tiles and a
- * long K, e.g. 17 <= M <= 128 on a few-thousand-row matrix), else 0 (a NULL
- * workspace is then accepted).  0 if the shape is invalid. */
+ * when the shape runs as a tiled product with K split across workgroups
+ * (few output tiles and a long K, e.g. 33 <= M <= 128 with M K > 256 Ki on
+ * a few-thousand-row matrix), else 0 (a NULL workspace is then accepted).
+ * 0 if the shape is invalid. */
 size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -157,7 +158,8 @@ size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *           the call (two calls in flight at once need two workspaces).  May
  *           be NULL when the size query returns 0.
  * Integer results are bit-exact and independent of the launch shape (split
- * partial sums are added in exact int32 arithmetic).
+ * partial sums are added in exact int32 arithmetic).  Which kernel runs
+ * (bitlinear_forward_kernel reports it) depends only on M, N and K.
  */
 bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma,
                                    int64_t N, int64_t K,
@@ -178,10 +180,10 @@ size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Computes exactly bitlinear_quant_acts followed by bitlinear_forward (same
  * X~, same x_scale, same x_sum, same accumulators; page section 2, absmax
  * activation quantiser and the linear transformation), as one launch for
- * decode shapes (one token with K a multiple of 64 up to 12288, or M <= 8
- * tokens whose int8 rows fit the on-chip staging; every workgroup quantises
- * the activations it needs), else as those two launches.  This is the
- * quantiser folded into the projection's prologue.
+ * single-token shapes (K a multiple of 64 up to 12288, or longer rows whose
+ * int8 copy fits the on-chip staging) and two-token narrow ones (every
+ * workgroup quantises the activations it needs), else as those two
+ * launches.  This is the quantiser folded into the projection's prologue.
  *
  * X        [M][K] fp32, device, 16-byte aligned (read only).
  * Y        [M][N], device, as in bitlinear_forward.
@@ -205,9 +207,9 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
  * g < G this computes exactly what bitlinear_forward(W_packed[g], gamma[g],
  * N[g], K, X_q, x_scale, x_sum, M, Y[g], y_dtype, ...) computes (page
  * section 2, "The Linear Transformation and Rescaling").  Decode shapes
- * (M <= 16) run as one launch over the rows of all G matrices, so the group
- * pays one launch instead of G; larger M runs the projections one after
- * another.
+ * (M <= 16, and up to 64 tokens where the skinny kernel applies) run as one
+ * launch over the rows of all G matrices, so the group pays one launch
+ * instead of G; tiled-product shapes run the projections one after another.
  *
  * G          1 .. BITLINEAR_MAX_GROUP.
  * W_packed, gamma, N, Y   HOST arrays of G entries (read during the call,
