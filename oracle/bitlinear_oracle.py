@@ -185,6 +185,73 @@ def unpack_codes(P: np.ndarray, K: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Base-3 packing, five weights per byte (format BLT3-v1)
+# --------------------------------------------------------------------------
+BLT3_PIECE = 80   # weights per 16-byte piece (four words of 20)
+
+
+def base3_row_bytes(K: int) -> int:
+    """Bytes of one BLT3-v1 row: K rounded up to whole 80-weight pieces."""
+    return 16 * ((K + BLT3_PIECE - 1) // BLT3_PIECE)
+
+
+def pack_codes_base3(Wt: np.ndarray) -> np.ndarray:
+    """Pack ternary W~ [N][K] into bytes [N][base3_row_bytes(K)].
+
+    [B158] section 4, "Memory Bandwidth and Latency Bounds": five ternary
+    values fit one byte because 3^5 = 243 < 256.  The layout is this
+    library's own (the page gives none): code c = W~ + 1; a row is padded with
+    W~ = 0 to a multiple of 80 weights; little-endian 32-bit word g of the row
+    holds k = 20g + 4j + b (j = 0..4, b = 0..3) in its byte b, which stores
+    the base-3 number Nb = sum_j c_{20g+4j+b} 3^(4-j) (j = 0 the leading
+    digit) as the byte ceil(256 Nb / 243).
+    """
+    Wt = np.asarray(Wt)
+    N, K = Wt.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    c0 = Wt.astype(np.int64) + 1
+    if c0.min(initial=0) < 0 or c0.max(initial=0) > 2:
+        raise ValueError("not ternary")
+    Kp = base3_row_bytes(K) * 5
+    c = np.ones((N, Kp), dtype=np.int64)
+    c[:, :K] = c0
+    c = c.reshape(N, Kp // 20, 5, 4)                  # axes: n, g, j, b
+    num = np.zeros((N, Kp // 20, 4), dtype=np.int64)  # axes: n, g, b
+    for j in range(5):
+        num += c[:, :, j, :] * 3 ** (4 - j)
+    byte = (256 * num + 242) // 243                   # ceil(256 Nb / 243)
+    return byte.reshape(N, Kp // 5).astype(np.uint8)
+
+
+def unpack_codes_base3(P: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_codes_base3: bytes -> int8 W~ [N][K].
+
+    A byte B read as the fraction B / 256 approximates Nb / 243, the five
+    digits after the point in base 3; multiplying by 3 moves the next digit
+    into bits 8 and up: for j = 0..4, B = 3 B, digit j = B >> 8, B = B & 255.
+    """
+    P = np.asarray(P, dtype=np.uint8)
+    N = P.shape[0]
+    Kp = base3_row_bytes(K) * 5
+    b0 = P.reshape(N, Kp // 20, 4).astype(np.int64)    # n, g, b
+    x = b0
+    c = np.empty((N, Kp // 20, 5, 4), dtype=np.int64)  # n, g, j, b
+    for j in range(5):
+        x = 3 * x
+        c[:, :, j, :] = x >> 8
+        x = x & 255
+    # 13 of the 256 byte values are never written: re-encode and compare
+    num = sum(c[:, :, j, :] * 3 ** (4 - j) for j in range(5))
+    if ((256 * num + 242) // 243 != b0).any():
+        raise ValueError("byte outside the format")
+    c = c.reshape(N, Kp)
+    if (c[:, K:] != 1).any():
+        raise ValueError("padding weights must be zero")
+    return (c[:, :K] - 1).astype(np.int8)
+
+
+# --------------------------------------------------------------------------
 # RMS normalisation of the activations (before the quantiser)
 # --------------------------------------------------------------------------
 def exact_sum_squares(X: np.ndarray) -> list:

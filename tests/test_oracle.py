@@ -169,6 +169,59 @@ def test_pack_zero_group_and_size_and_roundtrip():
         assert not (fields == 3).any()
 
 
+def test_base3_every_digit_pattern_decodes():
+    """All 3^5 digit patterns of one byte: the byte is ceil(256 Nb / 243)
+    (taken from exact rationals here), all 243 bytes differ, and the
+    multiply-by-3 decode returns every pattern (a floor in place of the
+    ceiling decodes 242 of them wrongly)."""
+    rows = []
+    for nb in range(243):
+        w = np.zeros(80, np.int8)
+        for j in range(5):
+            w[4 * j] = (nb // 3 ** (4 - j)) % 3 - 1      # byte 0 of word 0, digit j
+        rows.append(w)
+    Wt = np.stack(rows)
+    P = O.pack_codes_base3(Wt)
+    for nb in range(243):
+        assert int(P[nb, 0]) == math.ceil(Fraction(256 * nb, 243))
+    assert len(set(P[:, 0].tolist())) == 243
+    assert (O.unpack_codes_base3(P, 80) == Wt).all()
+
+
+def test_base3_worked_bytes():
+    """Hand-derived bytes (tests/golden/worked_example_base3.json, with its
+    citation and derivation)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "worked_example_base3.json")))
+    P = O.pack_codes_base3(np.array(g["W_ternary"], np.int8))
+    assert [bytes(r).hex() for r in P] == g["packed_hex"]
+
+
+def test_base3_layout_size_and_roundtrip():
+    rng = np.random.default_rng(8)
+    # a lone +1 at k of the first 80 weights: word k // 20, byte k % 4, digit
+    # (k % 20) // 4; every other byte holds five zero weights (Nb = 121)
+    for k in range(80):
+        w = np.zeros((1, 80), np.int8)
+        w[0, k] = 1
+        got = O.pack_codes_base3(w)[0].tolist()
+        want = [128] * 16
+        want[4 * (k // 20) + k % 4] = math.ceil(Fraction(256 * (121 + 3 ** (4 - (k % 20) // 4)), 243))
+        assert got == want, k
+    for K in (16, 64, 80, 96, 160, 1040, 8640):
+        Wt = rng.integers(-1, 2, size=(3, K)).astype(np.int8)
+        P = O.pack_codes_base3(Wt)
+        assert P.shape == (3, 16 * -(-K // 80)) and P.dtype == np.uint8
+        assert (O.unpack_codes_base3(P, K) == Wt).all()
+        assert (O.unpack_codes(O.pack_codes(Wt), K) == Wt).all()
+    assert O.base3_row_bytes(8640) * 8 / 8640 == 1.6        # 1.6 bits per weight
+    assert (O.unpack_codes_base3(np.full((1, 16), 255, np.uint8), 80) == 1).all()   # Nb = 242
+    with pytest.raises(ValueError):
+        O.unpack_codes_base3(np.full((1, 16), 1, np.uint8), 80)     # byte 1 is never written
+
+
 def test_pack_word_shift_mask_gives_consecutive_codes():
     # (word >> 2j) & 0x03030303 must hold the codes of k = 16g+4j .. 16g+4j+3
     # in byte order (little endian), i.e. ready as four int8 operands.
