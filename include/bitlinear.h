@@ -309,6 +309,65 @@ bitlinear_status bitlinear_forward_rmsnorm_grouped(int G, const uint8_t* const* 
                                                    int32_t* x_sum_out, void* workspace,
                                                    size_t workspace_bytes, void* stream);
 
+/*
+ * Base-3 weights, format BLT3-v1: five ternary weights per byte, 1.6 bits
+ * per weight.  Page section 4, "Memory Bandwidth and Latency Bounds": five
+ * ternary values fit one byte because 3^5 = 243 < 256.  The layout is this
+ * library's own: code c = W~ + 1; a row is padded with W~ = 0 to a multiple
+ * of 80 weights and takes 16 * ceil(K / 80) bytes; little-endian 32-bit word
+ * g of a row holds k = 20g + 4j + b (j = 0..4, b = 0..3) in its byte b, which
+ * stores Nb = sum_j c_{20g+4j+b} 3^(4-j) as ceil(256 Nb / 243).  Same gamma
+ * and the same ternary codes as bitlinear_pack_weights; only the packing
+ * differs.
+ */
+#define BITLINEAR_PACK_FORMAT_BLT3_V1 2
+/* Tokens per bitlinear_forward_base3 call. */
+#define BITLINEAR_BASE3_MAX_M 16
+
+/* Bytes of BLT3-v1 weights for an N x K matrix: N * 16 * ceil(K / 80).  0 if
+ * the shape is invalid (as for bitlinear_packed_bytes). */
+size_t bitlinear_packed3_bytes(int64_t N, int64_t K);
+
+/*
+ * Absmean ternarisation (as bitlinear_pack_weights: page section 2, "Weight
+ * Quantization: Absmean Scaling"; gamma bit for bit the same) packed as
+ * BLT3-v1.
+ *
+ * W          [N][K] fp32, device, 16-byte aligned (read only).
+ * W_packed3  bitlinear_packed3_bytes(N, K) bytes, device, 16-byte aligned
+ *            (written).
+ * gamma      one fp32, device, 4-byte aligned (written).
+ * workspace  device, 16-byte aligned, >= bitlinear_pack_workspace_bytes(N, K)
+ *            bytes, scratch after the call.
+ * Errors as bitlinear_pack_weights.
+ */
+bitlinear_status bitlinear_pack_weights_base3(const float* W, int64_t N, int64_t K,
+                                              uint8_t* W_packed3, float* gamma,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream);
+
+/*
+ * The projection of bitlinear_forward (page section 2, "The Linear
+ * Transformation and Rescaling"; same accumulators, same epilogue) on BLT3-v1
+ * weights, for 1 <= M <= BITLINEAR_BASE3_MAX_M tokens (decode).  Larger M:
+ * convert the weights once with bitlinear_base3_to_blt2 and call
+ * bitlinear_forward.  Arguments as in bitlinear_forward, with W_packed3 in
+ * place of W_packed (16-byte aligned); no workspace.
+ */
+bitlinear_status bitlinear_forward_base3(const uint8_t* W_packed3, const float* gamma,
+                                         int64_t N, int64_t K, const int8_t* X_q,
+                                         const float* x_scale, const int32_t* x_sum,
+                                         int64_t M, void* Y, bitlinear_dtype y_dtype,
+                                         void* stream);
+
+/*
+ * Rewrites BLT3-v1 weights as BLT2-v1 (the same codes), e.g. for prefill with
+ * bitlinear_forward.  W_packed3 as above (read only); W_packed
+ * bitlinear_packed_bytes(N, K) bytes, device, 16-byte aligned (written).
+ */
+bitlinear_status bitlinear_base3_to_blt2(const uint8_t* W_packed3, int64_t N, int64_t K,
+                                         uint8_t* W_packed, void* stream);
+
 /* Kernels a forward call may launch (values of bitlinear_forward_kernel). */
 typedef enum bitlinear_kernel {
   BITLINEAR_KERNEL_DECODE_DOT = 1, /* one token: dot products on the vector ALU */

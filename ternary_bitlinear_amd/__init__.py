@@ -11,13 +11,16 @@ from .binding import (  # noqa: F401
     STATUS,
     MAX_GROUP,
     BitLinearError,
+    bitlinear_base3_to_blt2,
     bitlinear_forward,
+    bitlinear_forward_base3,
     bitlinear_forward_f32,
     bitlinear_forward_f32_grouped,
     bitlinear_forward_grouped,
     bitlinear_forward_rmsnorm,
     bitlinear_forward_rmsnorm_grouped,
     bitlinear_pack_weights,
+    bitlinear_pack_weights_base3,
     bitlinear_quant_acts,
     bitlinear_rmsnorm_quant,
     forward_f32_grouped_workspace_bytes,
@@ -29,5 +32,6 @@ from .binding import (  # noqa: F401
     forward_workspace_bytes,
     load,
     pack_workspace_bytes,
+    packed3_bytes,
     packed_bytes,
 )

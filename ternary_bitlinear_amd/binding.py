@@ -50,6 +50,12 @@ SIGNATURES = {
                                                          _vp, _c_i64, _vp, ctypes.c_int, _vp, _vp,
                                                          _vp, _vp, _c_size, _vp]),
     "bitlinear_forward_kernel": (ctypes.c_int, [ctypes.c_int, _c_i64, ctypes.c_int, _vp, _c_i64]),
+    "bitlinear_packed3_bytes": (_c_size, [_c_i64, _c_i64]),
+    "bitlinear_pack_weights_base3": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_size,
+                                                    _vp]),
+    "bitlinear_forward_base3": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64,
+                                               _vp, ctypes.c_int, _vp]),
+    "bitlinear_base3_to_blt2": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -136,6 +142,66 @@ def bitlinear_pack_weights(W, W_packed=None, gamma=None, workspace=None, stream=
                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
     return W_packed, gamma
+
+
+def packed3_bytes(N: int, K: int) -> int:
+    return load().bitlinear_packed3_bytes(N, K)
+
+
+def bitlinear_pack_weights_base3(W, W_packed3=None, gamma=None, workspace=None, stream=None):
+    """W [N][K] fp32 -> (W_packed3 uint8 [N][16 ceil(K/80)] in format BLT3-v1, gamma fp32 [1])."""
+    import torch
+    lib = load()
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    if W_packed3 is None:
+        W_packed3 = torch.empty((N, 16 * -(-K // 80)), dtype=torch.uint8, device=W.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    need = lib.bitlinear_pack_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=W.device)
+    _dev(W_packed3, torch.uint8, "W_packed3")
+    _dev(gamma, torch.float32, "gamma")
+    _check(lib.bitlinear_pack_weights_base3(W.data_ptr(), N, K, W_packed3.data_ptr(),
+                                            gamma.data_ptr(), workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
+    return W_packed3, gamma
+
+
+def bitlinear_forward_base3(W_packed3, gamma, X_q, x_scale, x_sum, N=None, K=None,
+                            y_dtype="bf16", Y=None, stream=None):
+    """BLT3-v1 weights and quantised X (1 <= M <= 16) -> Y [M][N]."""
+    import torch
+    lib = load()
+    _dev(W_packed3, torch.uint8, "W_packed3")
+    _dev(X_q, torch.int8, "X_q")
+    M, Kx = X_q.shape
+    K = Kx if K is None else K
+    N = W_packed3.shape[0] if N is None else N
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[y_dtype]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=tdt, device=X_q.device)
+    _dev(Y, tdt, "Y")
+    _check(lib.bitlinear_forward_base3(W_packed3.data_ptr(), gamma.data_ptr(), N, K,
+                                       X_q.data_ptr(), x_scale.data_ptr(), x_sum.data_ptr(), M,
+                                       Y.data_ptr(), DTYPES[y_dtype], _stream(stream)))
+    return Y
+
+
+def bitlinear_base3_to_blt2(W_packed3, K, W_packed=None, stream=None):
+    """BLT3-v1 rows [N][16 ceil(K/80)] -> BLT2-v1 rows [N][K/4] (the same codes)."""
+    import torch
+    lib = load()
+    _dev(W_packed3, torch.uint8, "W_packed3")
+    N = W_packed3.shape[0]
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W_packed3.device)
+    _dev(W_packed, torch.uint8, "W_packed")
+    _check(lib.bitlinear_base3_to_blt2(W_packed3.data_ptr(), N, K, W_packed.data_ptr(),
+                                       _stream(stream)))
+    return W_packed
 
 
 def bitlinear_quant_acts(X, X_q=None, x_scale=None, x_sum=None, stream=None):

@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["abi.hip", "pack.hip", "quant.hip", "forward.hip"]
+SOURCES = ["abi.hip", "pack.hip", "quant.hip", "forward.hip", "base3.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: no multiply-add fusion anywhere (the quantisers' rounding

@@ -13,6 +13,7 @@
 #include "kernels.hpp"
 
 static_assert(BITLINEAR_MAX_GROUP == bl::kMaxGroupProjections, "group size");
+static_assert(BITLINEAR_BASE3_MAX_M == bl::kBase3MaxTokens, "base-3 tokens");
 
 namespace {
 
@@ -388,6 +389,72 @@ bitlinear_status bitlinear_forward_rmsnorm_grouped(int G, const uint8_t* const* 
   return forward_f32_grouped_impl("forward_rmsnorm_grouped", G, W_packed, gamma, N, K, X, norm_g,
                                   M, Y, y_dtype, X_q_out, x_scale_out, x_sum_out, workspace,
                                   workspace_bytes, stream);
+}
+
+size_t bitlinear_packed3_bytes(int64_t N, int64_t K) {
+  if (N < 1 || N > kMaxDim || !shape_ok_k(K)) return 0;
+  return (size_t)N * bl::packed3_row_bytes(K);
+}
+
+bitlinear_status bitlinear_pack_weights_base3(const float* W, int64_t N, int64_t K,
+                                              uint8_t* W_packed3, float* gamma, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  if (!W || !W_packed3 || !gamma) return fail(BITLINEAR_ERR_NULL, "pack_weights_base3: NULL buffer");
+  if (N < 1 || N > kMaxDim || !shape_ok_k(K) || N * K > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "pack_weights_base3: invalid shape N=%lld K=%lld (need N>=1, "
+                "K%%16==0, 16<=K<=%d, N*K<2^31)", (long long)N, (long long)K, BITLINEAR_MAX_K);
+  if (!aligned(W, 16) || !aligned(W_packed3, 16) || !aligned(gamma, 4))
+    return fail(BITLINEAR_ERR_ALIGN, "pack_weights_base3: W and W_packed3 need 16-byte alignment, "
+                "gamma 4-byte");
+  const size_t need = bl::pack_workspace_bytes(N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(BITLINEAR_ERR_WORKSPACE, "pack_weights_base3: workspace of %zu bytes needed, got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "pack_weights_base3: workspace alignment");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_pack3(W, N, K, W_packed3, gamma, workspace,
+                                   reinterpret_cast<hipStream_t>(stream)),
+                  "pack_weights_base3 launch");
+}
+
+bitlinear_status bitlinear_forward_base3(const uint8_t* W_packed3, const float* gamma, int64_t N,
+                                         int64_t K, const int8_t* X_q, const float* x_scale,
+                                         const int32_t* x_sum, int64_t M, void* Y,
+                                         bitlinear_dtype y_dtype, void* stream) {
+  if (!W_packed3 || !gamma || !X_q || !x_scale || !x_sum || !Y)
+    return fail(BITLINEAR_ERR_NULL, "forward_base3: NULL buffer");
+  if (M < 1 || M > BITLINEAR_BASE3_MAX_M || N < 1 || N > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "forward_base3: invalid shape M=%lld N=%lld K=%lld (need "
+                "1<=M<=%d)", (long long)M, (long long)N, (long long)K, BITLINEAR_BASE3_MAX_M);
+  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+    return fail(BITLINEAR_ERR_DTYPE, "forward_base3: unknown y_dtype %d", (int)y_dtype);
+  const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
+  if (!aligned(W_packed3, 16) || !aligned(X_q, 16) || !aligned(gamma, 4) ||
+      !aligned(x_scale, 4) || !aligned(x_sum, 4) || !aligned(Y, ya))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_base3: W_packed3/X_q need 16-byte alignment, Y its "
+                "element size");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward_b3(W_packed3, gamma, N, K, X_q, x_scale, x_sum, M, Y,
+                                        (int)y_dtype, reinterpret_cast<hipStream_t>(stream)),
+                  "forward_base3 launch");
+}
+
+bitlinear_status bitlinear_base3_to_blt2(const uint8_t* W_packed3, int64_t N, int64_t K,
+                                         uint8_t* W_packed, void* stream) {
+  if (!W_packed3 || !W_packed) return fail(BITLINEAR_ERR_NULL, "base3_to_blt2: NULL buffer");
+  if (N < 1 || N > kMaxDim || !shape_ok_k(K))
+    return fail(BITLINEAR_ERR_SHAPE, "base3_to_blt2: invalid shape N=%lld K=%lld", (long long)N,
+                (long long)K);
+  if (!aligned(W_packed3, 16) || !aligned(W_packed, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "base3_to_blt2: both buffers need 16-byte alignment");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_b3_to_b2(W_packed3, N, K, W_packed,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                  "base3_to_blt2 launch");
 }
 
 int bitlinear_forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K) {

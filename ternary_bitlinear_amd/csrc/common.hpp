@@ -122,6 +122,23 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
+// ---- output store (page section 2 rescale; section 6 "Scaling Factor Fusion") --
+constexpr int kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2;
+
+// y = fl32(fl32((float)acc * gamma) * scale), stored as fp32 or bf16 (nearest
+// even); int32 output stores acc itself.
+template <int OUT>
+__device__ __forceinline__ void store_out(void* Y, int64_t idx, int32_t acc, float gamma,
+                                          float scale) {
+  if constexpr (OUT == kOutI32) {
+    reinterpret_cast<int32_t*>(Y)[idx] = acc;
+  } else {
+    const float y = ((float)acc * gamma) * scale;
+    if constexpr (OUT == kOutF32) reinterpret_cast<float*>(Y)[idx] = y;
+    else reinterpret_cast<uint16_t*>(Y)[idx] = f32_to_bf16_rne(y);
+  }
+}
+
 // ---- MFMA int8 operand types --------------------------------------------------
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 

@@ -27,20 +27,6 @@ namespace bl {
 
 namespace {
 
-constexpr int kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2;
-
-template <int OUT>
-__device__ __forceinline__ void store_out(void* Y, int64_t idx, int32_t acc, float gamma,
-                                          float scale) {
-  if constexpr (OUT == kOutI32) {
-    reinterpret_cast<int32_t*>(Y)[idx] = acc;
-  } else {
-    const float y = ((float)acc * gamma) * scale;
-    if constexpr (OUT == kOutF32) reinterpret_cast<float*>(Y)[idx] = y;
-    else reinterpret_cast<uint16_t*>(Y)[idx] = f32_to_bf16_rne(y);
-  }
-}
-
 // Four consecutive outputs Y[idx .. idx + 3] (idx a multiple of 4, Y aligned
 // for the vector), one store.
 template <int OUT>

@@ -61,6 +61,20 @@ hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64
                               int y_dtype, int8_t* X_q_out, float* x_scale_out,
                               int32_t* x_sum_out, void* workspace, hipStream_t stream);
 
+// Base-3 weights (BLT3-v1, five per byte; rows padded to 80 weights).
+// launch_pack3 computes gamma and the codes as launch_pack does (same
+// workspace); launch_forward_b3 takes 1 <= M <= kBase3MaxTokens tokens;
+// launch_b3_to_b2 rewrites BLT3-v1 rows as BLT2-v1 rows (for larger M).
+constexpr int kBase3MaxTokens = 16;
+size_t packed3_row_bytes(int64_t K);
+hipError_t launch_pack3(const float* W, int64_t N, int64_t K, uint8_t* W_packed3, float* gamma,
+                        void* workspace, hipStream_t stream);
+hipError_t launch_forward_b3(const uint8_t* W_packed3, const float* gamma, int64_t N, int64_t K,
+                             const int8_t* X_q, const float* x_scale, const int32_t* x_sum,
+                             int64_t M, void* Y, int y_dtype, hipStream_t stream);
+hipError_t launch_b3_to_b2(const uint8_t* W_packed3, int64_t N, int64_t K, uint8_t* W_packed,
+                           hipStream_t stream);
+
 // The kernel a forward call launches for these sizes (host only): entry 0
 // for the pre-quantised projection, 1 for the fp32 one, 2 with the RMS
 // normalisation; kKernel* or'ed with 16 when the quantiser runs inside it.

@@ -239,6 +239,46 @@ __global__ __launch_bounds__(256) void k_ternarize_pack(const float4* __restrict
   }
 }
 
+// Base-3 packing (BLT3-v1, page section 4 "Memory Bandwidth and Latency
+// Bounds": five ternary values per byte).  Thread per 20-weight word of a
+// row (rows padded with W~ = 0 to a multiple of 80 weights): the same two
+// thresholds decide each code c = W~ + 1, and byte b of the word stores
+// Nb = sum_j c_{20g + 4j + b} 3^(4 - j) as ceil(256 Nb / 243).  20 weights
+// are five float4 (K % 16 == 0, so a row's last word is cut at a float4).
+__global__ __launch_bounds__(256) void k_ternarize_pack3(const float* __restrict__ W, int64_t N,
+                                                         int K, const float* __restrict__ thresholds,
+                                                         uint32_t* __restrict__ out) {
+  const float t_pos = thresholds[0];
+  const float t_neg = thresholds[1];
+  const int words = 4 * ((K + 79) / 80);
+  const int64_t total = N * words;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t n = i / words;
+    const int g = (int)(i - n * words);
+    uint32_t code[20];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int k = 20 * g + 4 * q;
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < K) f = *reinterpret_cast<const float4*>(W + n * K + k);
+      const float v[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        code[4 * q + t] = k >= K ? 1u : (v[t] >= t_pos ? 2u : (v[t] < t_neg ? 0u : 1u));
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint32_t nb = 0;
+#pragma unroll
+      for (int j = 0; j < 5; ++j) nb = 3 * nb + code[4 * j + b];
+      word |= ((256 * nb + 242) / 243) << (8 * b);
+    }
+    out[i] = word;
+  }
+}
+
 int64_t abs_tiles(int64_t nk) { return (nk + kAbsTile - 1) / kAbsTile; }
 int64_t abs_blocks(int64_t nk) {
   const int64_t b = (abs_tiles(nk) + kAbsWavesPerBlock - 1) / kAbsWavesPerBlock;
@@ -269,6 +309,25 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* W_packed, 
   k_ternarize_pack<<<dim3((unsigned)pb), dim3(256), 0, stream>>>(
       reinterpret_cast<const float4*>(W), n_words, thresholds,
       reinterpret_cast<uint32_t*>(W_packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack3(const float* W, int64_t N, int64_t K, uint8_t* W_packed3, float* gamma,
+                        void* workspace, hipStream_t stream) {
+  const int64_t nk = N * K;
+  float* thresholds = reinterpret_cast<float*>(workspace);
+  uint64_t* partials =
+      reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(workspace) + kPackWsHeader);
+  const int64_t blocks = abs_blocks(nk);
+  k_abs_sum_partials<<<dim3((unsigned)blocks), dim3(kAbsThreads), 0, stream>>>(
+      reinterpret_cast<const float4*>(W), nk / 4, abs_tiles(nk), partials);
+  k_gamma_finalize<<<1, 256, 0, stream>>>(partials, blocks * kAbsWavesPerBlock, nk, gamma,
+                                          thresholds);
+  const int64_t total = N * 4 * ((K + 79) / 80);
+  int64_t pb = (total + 255) / 256;
+  if (pb > 8192) pb = 8192;
+  k_ternarize_pack3<<<dim3((unsigned)pb), dim3(256), 0, stream>>>(
+      W, N, (int)K, thresholds, reinterpret_cast<uint32_t*>(W_packed3));
   return hipGetLastError();
 }
 

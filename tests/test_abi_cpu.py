@@ -232,3 +232,33 @@ def test_forward_kernel_query(lib):
             assert fused == (tb.forward_f32_workspace_bytes(M, N, K) == 0), (M, N, K)
             if tb.forward_workspace_bytes(M, N, K) > 0:
                 assert fk("forward", M, [N], K)[0] == "k_gemm", (M, N, K)
+
+
+def test_base3_validation_without_gpu_calls(lib):
+    """Size query and the argument checks of the base-3 entry points, all taken
+    before any HIP call."""
+    assert lib.bitlinear_packed3_bytes(8640, 3200) == 8640 * 640      # 1.6 bits per weight
+    assert lib.bitlinear_packed3_bytes(3, 16) == 3 * 16               # padded to 80 weights
+    assert lib.bitlinear_packed3_bytes(2, 4096) == 2 * 16 * 52
+    assert lib.bitlinear_packed3_bytes(4, 40) == 0                    # K % 16 != 0
+    ws = lib.bitlinear_pack_workspace_bytes(64, 4096)
+    assert lib.bitlinear_pack_weights_base3(None, 64, 4096, FAKE, FAKE, FAKE, ws, None) == 1
+    assert lib.bitlinear_pack_weights_base3(FAKE, 64, 40, FAKE, FAKE, FAKE, ws, None) == 2
+    assert lib.bitlinear_pack_weights_base3(FAKE, 64, 4096, FAKE + 4, FAKE, FAKE, ws, None) == 3
+    assert lib.bitlinear_pack_weights_base3(FAKE, 64, 4096, FAKE, FAKE, FAKE, ws - 16, None) == 7
+    args = [FAKE, FAKE, 4096, 4096, FAKE, FAKE, FAKE, 1, FAKE, 1, None]
+    bad = list(args); bad[4] = None
+    assert lib.bitlinear_forward_base3(*bad) == 1
+    bad = list(args); bad[7] = 17                                     # M above 16
+    assert lib.bitlinear_forward_base3(*bad) == 2 and "M<=16" in _last(lib)
+    bad = list(args); bad[7] = 0
+    assert lib.bitlinear_forward_base3(*bad) == 2
+    bad = list(args); bad[3] = 40
+    assert lib.bitlinear_forward_base3(*bad) == 2
+    bad = list(args); bad[9] = 7
+    assert lib.bitlinear_forward_base3(*bad) == 4
+    bad = list(args); bad[0] = FAKE + 8
+    assert lib.bitlinear_forward_base3(*bad) == 3
+    assert lib.bitlinear_base3_to_blt2(FAKE, 4, 4096, None, None) == 1
+    assert lib.bitlinear_base3_to_blt2(FAKE, 4, 4100, FAKE, None) == 2
+    assert lib.bitlinear_base3_to_blt2(FAKE + 4, 4, 4096, FAKE, None) == 3
