@@ -289,6 +289,53 @@ def main():
                                (2 * M * P.N * P.K / t_fwd / 1e12) if prefill
                                else f32_bytes / t_fwd / 1e9, 2 if prefill else 1)}
 
+    # base-3 weights (1.6 bits per weight, up to 16 tokens): each projection
+    # on the same quantised activations in both formats, back to back over
+    # >= 512 MB of weight copies, in one process
+    if M <= 16:
+        b3 = {"us": [], "us_blt2": [], "bytes": []}
+        for q in projs:
+            N_, K_ = q["p"].N, q["p"].K
+            P3, g3 = tb.bitlinear_pack_weights_base3(q["Wd"])
+            c3 = max(1, math.ceil(ROTATE_BYTES / P3.numel()))
+            W3 = [P3] + [P3.clone() for _ in range(c3 - 1)]
+            torch.cuda.synchronize()
+
+            def f3(r, q=q, W3=W3, g3=g3, N_=N_, K_=K_):
+                tb.bitlinear_forward_base3(W3[r], g3, q["Xq"], q["s"], q["xs"], N=N_, K=K_,
+                                           y_dtype=out, Y=q["Y"], stream=stream)
+
+            def f2(r, q=q, N_=N_, K_=K_):
+                tb.bitlinear_forward(q["Wc"][r % copies], q["g"], q["Xq"], q["s"], q["xs"],
+                                     N=N_, K=K_, y_dtype=out, Y=q["Y"], stream=stream)
+            for key, fn, n_c in (("us", f3, c3), ("us_blt2", f2, copies)):
+                gq = graph_of([lambda r=r, fn=fn: fn(r) for r in range(n_c)])
+                gq.replay()
+                rq = max(1, 2000 // n_c)
+                b3[key].append(timer(gq.replay, rq) / (rq * n_c))
+                del gq
+            b3["bytes"].append(P3.numel() + M * K_ + 8 * M + OUT_BYTES[out] * M * N_ + 4)
+            del W3, P3
+            torch.cuda.empty_cache()
+        t3 = sum(b3["us"]) / len(b3["us"])
+        rows["forward_base3"] = {
+            "shape": f"M{M} " + ", ".join(f"{q['p'].K}->{q['p'].N}" for q in projs),
+            "format": "BLT3-v1 (5 weights per byte)", "entry_point": "bitlinear_forward_base3",
+            "us": round(t3 * 1e6, 3),
+            "us_per_projection": [round(t * 1e6, 3) for t in b3["us"]],
+            "blt2_us_per_projection": [round(t * 1e6, 3) for t in b3["us_blt2"]],
+            "GB/s": round(sum(b3["bytes"]) / len(b3["bytes"]) / t3 / 1e9, 1)}
+        ws3 = torch.empty(tb.pack_workspace_bytes(q0["p"].N, q0["p"].K), dtype=torch.uint8,
+                          device=dev)
+        P3_tmp = torch.empty((q0["p"].N, 16 * -(-q0["p"].K // 80)), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            tb.bitlinear_pack_weights_base3(q0["Wd"], P3_tmp, g_tmp, ws3, stream=stream)
+        t_pack3 = timer(lambda: tb.bitlinear_pack_weights_base3(q0["Wd"], P3_tmp, g_tmp, ws3,
+                                                                stream=stream), 5) / 5
+        rows["pack_weights_base3"] = {"shape": f"{q0['p'].K}->{q0['p'].N}",
+                                      "us": round(t_pack3 * 1e6, 2)}
+        del P3_tmp, ws3
+
     # RMS normalisation in front of the quantiser (the step before the
     # projection): the normalising quantiser alone, and fused into the
     # projection as the dominant projection would run it
