@@ -563,27 +563,22 @@ hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t s
 // 16 columns to keep one.  Lanes past a row's end re-read its first piece and
 // multiply it by zeroed activations.
 //
-// FUSE (fp32 input) quantises the token inside the kernel,
+// FUSE = kDotFuseBlock (fp32 input) quantises the token inside the kernel,
 // with the same per-element arithmetic as the standalone quantiser (absmax on
 // bit patterns, one correctly rounded divide, one multiply and the exact
-// round-half-up per element):
-//   kDotFuseWave  (Q = 1) every wave quantises the whole row itself: lane l
-//                 holds the 64 fp32 activations of piece l; wave reductions
-//                 only, no LDS and no barrier, but the row's conversion is
-//                 repeated per wave (measured slower than the next mode).
-//   kDotFuseBlock the WV waves of a workgroup convert the row once: each thread
-//                 takes every (64 WV)-th group of four, the absmax and the code
-//                 sum go through LDS (two barriers), and each lane then reads
-//                 its piece's codes from LDS.
-// In both, the weight loads are issued before the quantiser's chain starts,
-// and wave 0 of workgroup 0 may also write X~, x_scale and x_sum out.
+// round-half-up per element).  The WV waves of a workgroup convert the row
+// once: each thread takes every (64 WV)-th group of four, the absmax and the
+// code sum go through LDS (two barriers), and each lane then reads its
+// piece's codes from LDS.  (Every wave converting the whole row itself, with
+// wave reductions only, measured 35-45 % slower: the conversion is then
+// repeated per wave.)  The weight loads are issued before the quantiser's
+// chain starts, and workgroup 0 may also write X~, x_scale and x_sum out.
 // ---------------------------------------------------------------------------
-constexpr int kDotFuseNone = 0, kDotFuseWave = 1, kDotFuseBlock = 2;
+constexpr int kDotFuseNone = 0, kDotFuseBlock = 1;
 constexpr int kDotWaves = 4;   // waves per workgroup without block fusion
 
 template <int OUT, int R, int Q, int FUSE, int WV, bool NORM = false>
 __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
-  static_assert(FUSE != kDotFuseWave || Q == 1, "the per-wave prologue holds one piece per lane");
   static_assert(!NORM || FUSE == kDotFuseBlock, "normalisation only in the block-fused prologue");
   constexpr int kFuseK4 = 64 * 64 / 4 * Q;                   // groups of four at K = 4096 Q
   constexpr int kJ = FUSE == kDotFuseBlock ? kFuseK4 / (WV * kWave) : 1;   // groups per thread
@@ -625,45 +620,7 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
   void* const yout = view.Y;
   int32_t sx;
   float sc;
-  if constexpr (FUSE == kDotFuseWave) {
-    const bool live = lane < npieces;
-    const float4* src = reinterpret_cast<const float4*>(da.X) + 16 * (live ? lane : 0);
-    float4 xv[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d) xv[d] = src[d];
-    __builtin_amdgcn_sched_barrier(0);
-    load_weights();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::"s"(gamma), "s"(yout));
-    uint32_t lmax = 0;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) lmax = max(lmax, absmax4(xv[d]));
-    lmax = wave_max_u32(live ? lmax : 0u);
-    const float beta = __uint_as_float(lmax);
-    const float inv = 127.0f / (beta + 1e-5f);
-    int32_t lsum = 0;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) xa[0][d] = (int32_t)quant4(xv[d], inv, lsum);
-    if (!live) {
-      lsum = 0;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) xa[0][d] = 0;
-    }
-    sx = wave_sum_i32(lsum);
-    sc = beta / 127.0f;
-    if (unit == 0 && da.Xq_out != nullptr) {
-      if (live) {
-        i32x4* dst = reinterpret_cast<i32x4*>(da.Xq_out + 64 * lane);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          dst[v] = i32x4{xa[0][4 * v + 0], xa[0][4 * v + 1], xa[0][4 * v + 2], xa[0][4 * v + 3]};
-      }
-      if (lane == 0) {
-        da.xs_out[0] = sc;
-        da.xsum_out[0] = sx;
-      }
-    }
-  } else if constexpr (FUSE == kDotFuseBlock) {
+  if constexpr (FUSE == kDotFuseBlock) {
     const int K4 = K / 4;
     const float4* src = reinterpret_cast<const float4*>(da.X);
     float4 xv[kJ];
@@ -1387,7 +1344,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs ga) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny projections: a few dozen tokens (M <= 16 TG), K % 64 == 0.
+// Skinny projections: 2 to 64 tokens (M <= 16 TG), K % 64 == 0.
 //
 // Between the single-token decode and the GEMM.  A workgroup owns RB blocks
 // of 16 weight rows and runs NWK waves per block; K advances in chunks of
@@ -1399,8 +1356,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs ga) {
 // wave and step, so one vmcnt wait per step retires exactly the stage about
 // to be read (a ring of registers carried across the loop would make the
 // compiler drain every load at the loop head).  With about one workgroup per
-// CU (RB ~ row blocks / 256), the activations are read from L2 about once per
-// CU rather than once per output tile, and every SIMD runs RB NWK / 4 waves.
+// CU (about 256 workgroups of RB NWK = 8 waves, or RB = 1 with 4 waves on
+// narrow outputs), the activations are read from L2 about once per CU rather
+// than once per output tile.
 //
 // Stage layouts (16-byte pieces XOR-swizzled by row, so that the lanes of a
 // fragment read, 16 rows and one piece, fall in different bank groups):
