@@ -1784,7 +1784,13 @@ inline DecodeCfg fused_cfg(int64_t M, int G, const int64_t* N, int64_t K) {
 
 // One token with K <= 12288 (a multiple of 64): the vector-ALU decode
 // quantises in place (the workgroup converts the row once into LDS), one
-// launch and no workspace; Q = ceil(K / 4096) pieces per lane.
+// launch and no workspace; Q = ceil(K / 4096) pieces per lane.  4 rows per
+// wave and 4 waves per workgroup, except at Q = 3 without the normalisation:
+// 2 rows per wave and 8 waves, timed 3-8 % faster there (3200 <- 8640: 5.8
+// vs 6.3 us; 4096 <- 11008: 6.6 vs 6.9 us; 8192 <- 12288: 9.3-9.8 vs
+// 10.0-10.4 us) and no faster at Q = 1, 2.  With the normalisation the
+// 4-wave split of the row stays: its fp64 sum of squares must add in the
+// standalone normalising quantiser's order.
 constexpr int kDotFuseRows = 4;   // rows per wave in that mode
 constexpr int kDotFuseWaves = 4;  // waves per workgroup in that mode
 constexpr int kDotFuseMaxQ = 3;
@@ -1798,7 +1804,8 @@ hipError_t fused_dot_out(const DecodeArgs& da, hipStream_t stream) {
   const int q = (da.K + 64 * 64 - 1) / (64 * 64);
   if (q <= 1) return launch_decode_dot_t<OUT, kDotFuseRows, 1, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
   if (q == 2) return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
-  return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
+  if constexpr (NORM) return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves, true>(da, stream);
+  else return launch_decode_dot_t<OUT, 2, 3, kDotFuseBlock, 8, false>(da, stream);
 }
 template <int OUT>
 hipError_t fused_dot_norm(const DecodeArgs& da, hipStream_t stream) {
