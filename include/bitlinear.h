@@ -180,7 +180,7 @@ size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Computes exactly bitlinear_quant_acts followed by bitlinear_forward (same
  * X~, same x_scale, same x_sum, same accumulators; page section 2, absmax
  * activation quantiser and the linear transformation), as one launch for
- * single-token shapes (K a multiple of 64 up to 12288, or longer rows whose
+ * single-token shapes (K a multiple of 64 up to 16384, or longer rows whose
  * int8 copy fits the on-chip staging) and two-token narrow ones (every
  * workgroup quantises the activations it needs), else as those two
  * launches.  This is the quantiser folded into the projection's prologue.
@@ -282,8 +282,9 @@ size_t bitlinear_forward_rmsnorm_workspace_bytes(int64_t M, int64_t N, int64_t K
 /*
  * RMS normalisation, quantiser and projection: bitlinear_rmsnorm_quant
  * followed by bitlinear_forward (same X~, x_scale, x_sum and accumulators).
- * One launch for one token with K a multiple of 64 up to 12288, else those
- * two launches.  Arguments as in bitlinear_forward_f32, plus the gain norm_g
+ * One launch for one token with K a multiple of 64 up to 12288 (the fp32 row
+ * and the gain are held in registers while the sum of squares forms), else
+ * those two launches.  Arguments as in bitlinear_forward_f32, plus the gain norm_g
  * ([K] fp32, device, 16-byte aligned); workspace from
  * bitlinear_forward_rmsnorm_workspace_bytes, with the same exception when the
  * quantiser outputs are given.

@@ -575,6 +575,7 @@ hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t s
 // chain starts, and workgroup 0 may also write X~, x_scale and x_sum out.
 // ---------------------------------------------------------------------------
 constexpr int kDotFuseNone = 0, kDotFuseBlock = 1;
+constexpr int kDotHeldQ = 3;   // pieces per lane whose activations stay in registers
 constexpr int kDotWaves = 4;   // waves per workgroup without block fusion
 
 template <int OUT, int R, int Q, int FUSE, int WV, bool NORM = false>
@@ -688,7 +689,7 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
       da.xsum_out[0] = sx;
     }
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
+    for (int q = 0; q < (Q <= kDotHeldQ ? Q : 0); ++q) {
       const int p = lane + kWave * q;
       const i32x4* lp = reinterpret_cast<const i32x4*>(s_codes) + 4 * (p < npieces ? p : 0);
 #pragma unroll
@@ -728,23 +729,63 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
   }
 
   int32_t mine = 0;   // lane r keeps row r's sum
+  if constexpr (FUSE == kDotFuseBlock && Q > kDotHeldQ) {
+    // Long rows: each piece's codes are read from LDS when its turn comes
+    // (piece outer, rows inner), so only one piece of activations is held.
+    int32_t accr[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int32_t acc = 0;
+    for (int r = 0; r < R; ++r) accr[r] = 0;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-      const uint32_t w4[4] = {wq[r][q].x, wq[r][q].y, wq[r][q].z, wq[r][q].w};
+      const int p = lane + kWave * q;
+      const i32x4* lp = reinterpret_cast<const i32x4*>(s_codes) + 4 * (p < npieces ? p : 0);
+      int32_t xq[16];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const i32x4 c = expand_codes(w4[t]);
-        acc = __builtin_amdgcn_sdot4(c.x, xa[q][4 * t + 0], acc, false);
-        acc = __builtin_amdgcn_sdot4(c.y, xa[q][4 * t + 1], acc, false);
-        acc = __builtin_amdgcn_sdot4(c.z, xa[q][4 * t + 2], acc, false);
-        acc = __builtin_amdgcn_sdot4(c.w, xa[q][4 * t + 3], acc, false);
+      for (int v = 0; v < 4; ++v) {
+        const i32x4 a = lp[v];
+        xq[4 * v + 0] = a.x; xq[4 * v + 1] = a.y; xq[4 * v + 2] = a.z; xq[4 * v + 3] = a.w;
+      }
+      if (p >= npieces) {
+#pragma unroll
+        for (int d = 0; d < 16; ++d) xq[d] = 0;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w4[4] = {wq[r][q].x, wq[r][q].y, wq[r][q].z, wq[r][q].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const i32x4 c = expand_codes(w4[t]);
+          accr[r] = __builtin_amdgcn_sdot4(c.x, xq[4 * t + 0], accr[r], false);
+          accr[r] = __builtin_amdgcn_sdot4(c.y, xq[4 * t + 1], accr[r], false);
+          accr[r] = __builtin_amdgcn_sdot4(c.z, xq[4 * t + 2], accr[r], false);
+          accr[r] = __builtin_amdgcn_sdot4(c.w, xq[4 * t + 3], accr[r], false);
+        }
       }
     }
-    acc = wave_sum_i32(acc);
-    if (lane == r) mine = acc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int32_t acc = wave_sum_i32(accr[r]);
+      if (lane == r) mine = acc;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int32_t acc = 0;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint32_t w4[4] = {wq[r][q].x, wq[r][q].y, wq[r][q].z, wq[r][q].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const i32x4 c = expand_codes(w4[t]);
+          acc = __builtin_amdgcn_sdot4(c.x, xa[q][4 * t + 0], acc, false);
+          acc = __builtin_amdgcn_sdot4(c.y, xa[q][4 * t + 1], acc, false);
+          acc = __builtin_amdgcn_sdot4(c.z, xa[q][4 * t + 2], acc, false);
+          acc = __builtin_amdgcn_sdot4(c.w, xa[q][4 * t + 3], acc, false);
+        }
+      }
+      acc = wave_sum_i32(acc);
+      if (lane == r) mine = acc;
+    }
   }
   if (lane < R && n0 + lane < N) store_out<OUT>(yout, n0 + lane, mine - sx, gamma, sc);
 }
@@ -1782,20 +1823,25 @@ inline DecodeCfg fused_cfg(int64_t M, int G, const int64_t* N, int64_t K) {
   return decode_cfg((int)M, rows, (int)K, true);
 }
 
-// One token with K <= 12288 (a multiple of 64): the vector-ALU decode
-// quantises in place (the workgroup converts the row once into LDS), one
-// launch and no workspace; Q = ceil(K / 4096) pieces per lane.  4 rows per
-// wave and 4 waves per workgroup, except at Q = 3 without the normalisation:
-// 2 rows per wave and 8 waves, timed 3-8 % faster there (3200 <- 8640: 5.8
-// vs 6.3 us; 4096 <- 11008: 6.6 vs 6.9 us; 8192 <- 12288: 9.3-9.8 vs
-// 10.0-10.4 us) and no faster at Q = 1, 2.  With the normalisation the
-// 4-wave split of the row stays: its fp64 sum of squares must add in the
-// standalone normalising quantiser's order.
+// One token with K a multiple of 64 up to 16384 (12288 with the
+// normalisation): the vector-ALU decode quantises in place (the workgroup
+// converts the row once into LDS), one launch and no workspace; Q =
+// ceil(K / 4096) pieces per lane.  4 rows per wave and 4 waves per
+// workgroup, except at Q = 3, 4 without the normalisation: 2 rows per wave
+// and 8 waves, timed faster there (3200 <- 8640: 5.8 vs 6.3 us; 4096 <-
+// 11008: 6.6 vs 6.9 us; 8192 <- 12288: 9.3-9.8 vs 10.0-10.4 us) and no
+// faster at Q = 1, 2.  At Q = 4 (8192 <- 16384) it takes 12.3-12.7 us
+// against 14.6 us for the matrix decode with the quantiser in its prologue;
+// beyond (Q = 5..7: 4096 <- 20480, 8192 <- 28672) it no longer wins.  With
+// the normalisation the 4-wave split of the row stays: its fp64 sum of
+// squares must add in the standalone normalising quantiser's order (and
+// its fp32 row and gain then fill the registers at Q = 4).
 constexpr int kDotFuseRows = 4;   // rows per wave in that mode
 constexpr int kDotFuseWaves = 4;  // waves per workgroup in that mode
-constexpr int kDotFuseMaxQ = 3;
-inline bool fused_dot(int64_t M, int64_t K) {
-  return M == 1 && K % 64 == 0 && K <= 64 * 64 * kDotFuseMaxQ;
+constexpr int kDotFuseMaxQ = 4;
+constexpr int kDotFuseNormMaxQ = 3;
+inline bool fused_dot(int64_t M, int64_t K, bool norm) {
+  return M == 1 && K % 64 == 0 && K <= 64 * 64 * (norm ? kDotFuseNormMaxQ : kDotFuseMaxQ);
 }
 
 namespace {
@@ -1804,8 +1850,12 @@ hipError_t fused_dot_out(const DecodeArgs& da, hipStream_t stream) {
   const int q = (da.K + 64 * 64 - 1) / (64 * 64);
   if (q <= 1) return launch_decode_dot_t<OUT, kDotFuseRows, 1, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
   if (q == 2) return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
-  if constexpr (NORM) return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves, true>(da, stream);
-  else return launch_decode_dot_t<OUT, 2, 3, kDotFuseBlock, 8, false>(da, stream);
+  if constexpr (NORM) {
+    return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves, true>(da, stream);
+  } else {
+    if (q == 3) return launch_decode_dot_t<OUT, 2, 3, kDotFuseBlock, 8, false>(da, stream);
+    return launch_decode_dot_t<OUT, 2, 4, kDotFuseBlock, 8, false>(da, stream);
+  }
 }
 template <int OUT>
 hipError_t fused_dot_norm(const DecodeArgs& da, hipStream_t stream) {
@@ -1828,7 +1878,7 @@ inline bool afuse(int64_t M, int G, const int64_t* N, int64_t K) {
 // it, the multi-token matrix prologue does not (two launches there).
 size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K,
                                            bool norm) {
-  if (fused_dot(M, K) || (!norm && afuse(M, G, N, K))) return 0;
+  if (fused_dot(M, K, norm) || (!norm && afuse(M, G, N, K))) return 0;
   return quant_region_bytes(M, K) + forward_grouped_workspace_bytes(M, G, N, K);
 }
 
@@ -1850,7 +1900,7 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
                                       void* const* Y, int y_dtype, int8_t* X_q_out,
                                       float* x_scale_out, int32_t* x_sum_out, void* workspace,
                                       hipStream_t stream) {
-  if (fused_dot(M, K)) {
+  if (fused_dot(M, K, norm_g != nullptr)) {
     DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);
     da.X = X;
     da.Xq_out = X_q_out;
@@ -1900,7 +1950,7 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
 int forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K) {
   constexpr int kFused = 16;
   if (entry != 0) {
-    if (fused_dot(M, K)) return kKernelDecodeDot | kFused;
+    if (fused_dot(M, K, entry == 2)) return kKernelDecodeDot | kFused;
     if (entry == 1 && afuse(M, G, N, K)) return kKernelDecode | kFused;
   }
   if (skinny_ok(M, group_rows(G, N), K)) return kKernelSkinny;

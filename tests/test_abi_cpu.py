@@ -171,9 +171,12 @@ def test_rmsnorm_validation_without_gpu_calls(lib):
     assert lib.bitlinear_forward_rmsnorm(*bad) == 3
     bad = list(args); bad[3] = 40
     assert lib.bitlinear_forward_rmsnorm(*bad) == 2
-    # one token, K <= 12288 in steps of 64: fused, no workspace either way
+    # one token, K <= 12288 in steps of 64: fused, no workspace either way;
+    # up to 16384 only without the normalisation
     assert lib.bitlinear_forward_rmsnorm_workspace_bytes(1, 4096, 4096) == 0
     assert lib.bitlinear_forward_f32_workspace_bytes(1, 4096, 4096) == 0
+    assert lib.bitlinear_forward_f32_workspace_bytes(1, 4096, 16384) == 0
+    assert lib.bitlinear_forward_rmsnorm_workspace_bytes(1, 4096, 16384) > 0
     # two tokens: the quantiser alone fuses into the matrix decode, the
     # normalising one takes two launches and needs the quantiser region; from
     # four tokens both take two launches
@@ -204,6 +207,8 @@ def test_forward_kernel_query(lib):
     assert fk("forward", 1, [4096], 4096) == ("k_decode_dot", False)
     assert fk("f32", 1, [4096], 4096) == ("k_decode_dot", True)
     assert fk("rmsnorm", 1, [4096], 11008) == ("k_decode_dot", True)
+    assert fk("f32", 1, [8192], 16384) == ("k_decode_dot", True)
+    assert fk("rmsnorm", 1, [8192], 16384)[1] is False
     assert fk("forward", 1, [4096], 11008) == ("k_decode", False)
     assert fk("forward", 4, [4096], 4096) == ("k_decode", False)        # narrow, few tokens
     assert fk("forward", 4, [11008], 4096) == ("k_skinny", False)       # wide

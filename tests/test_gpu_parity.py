@@ -382,6 +382,8 @@ FUSED_SHAPES = [
     # (row counts that leave a workgroup, and a wave, partly past the end)
     (1, 1, 64), (1, 3, 128), (1, 1001, 192), (1, 4096, 4096), (1, 11008, 4096),
     (1, 5, 4160), (1, 77, 8192), (1, 4096, 11008), (1, 33, 12288), (1, 9, 12352),
+    # four pieces per lane, the activations of one piece held at a time
+    (1, 1000, 16384), (1, 3, 16320), (1, 300, 14336), (1, 7, 16448),
     # outside the fused kernel's reach: two launches
     (9, 77, 1040), (16, 300, 4096), (8, 64, 8640), (40, 130, 1024), (2, 50, 40960),
     # two launches with K split across workgroups (workspace needed either way)
