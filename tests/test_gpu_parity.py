@@ -99,7 +99,10 @@ def test_pack_threshold_neighbours(gpu_lib):
 
 # --------------------------------------------------------------------------- quant
 QUANT_SHAPES = [(1, 16), (3, 48), (5, 512), (64, 4096), (2, 8640), (17, 3200), (300, 128),
-                (2, 33280), (1, 131072), (3, 28672)]
+                (2, 33280), (1, 131072), (3, 28672),
+                # 1024-thread workgroups past 4096 values: 2, 4, 8, 16 groups of
+                # four per thread, ragged rows, and the looped variant past 65536
+                (1, 4112), (2, 8192), (3, 12304), (4, 16400), (1, 65536), (2, 65552)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES, ids=[f"M{m}xK{k}" for m, k in QUANT_SHAPES])

@@ -53,10 +53,11 @@ def oracle_rms_quant(X, g, got_xq=None):
 
 
 RMS_SHAPES = [
-    # (M, K): one group of four per thread up to 16 (register rows), the looped
-    # variant past 16384, the decode and prefill widths, a ragged K
-    (1, 16), (3, 64), (2, 1040), (2, 3200), (4, 8192), (2, 16384), (3, 16400), (2, 28672),
-    (1, 65536),
+    # (M, K): one group of four per thread up to 16 (register rows), 1024
+    # threads past 12288 values (register rows up to 32768, then looped), the
+    # decode and prefill widths, ragged K
+    (1, 16), (3, 64), (2, 1040), (2, 3200), (4, 8192), (1, 12288), (1, 12304), (2, 16384),
+    (3, 16400), (2, 28672), (1, 32768), (2, 32784), (1, 65536),
 ]
 
 
