@@ -24,7 +24,9 @@ reason in the design notes):
   * gamma is the exact mean of |W| rounded once to the nearest fp32 (ties to
     even); the page gives the mean, not a summation order.
   * Activations use one absmax per token (the page allows per-token or
-    per-tensor) and the symmetric range [-127, 127] (Q_b - 1 = 127).
+    per-tensor) and the symmetric range [-127, 127] (Q_b - 1 = 127).  The
+    4-bit activations the page's overview names (A4) take the same formula
+    with Q_b = 2^(4-1): the range [-7, 7] and x_scale = beta / 7.
   * The per-token reciprocal 127 / (absmax + eps) is formed in fp32 first and
     each element is multiplied by it (one fp32 multiply per element).
   * RMS normalisation before the quantiser ([B158] section 2 names it and
@@ -317,18 +319,30 @@ def rmsnorm(X: np.ndarray, g: np.ndarray, ms=None):
 # --------------------------------------------------------------------------
 # Activation quantisation: per-token absmax to int8
 # --------------------------------------------------------------------------
-def quantize_activations(X: np.ndarray):
-    """Per-token absmax int8 quantisation ([B158] section 2, absmax scaling).
+def act_qmax(bits: int) -> int:
+    """Q_b - 1 for b-bit symmetric activations: Q_b = 2^(b - 1) levels per sign
+    ([B158] section 2 gives it for b = 8; b = 4 is the "A4" of the W1A4KV2
+    standard its overview names, with no formula of its own)."""
+    if bits not in (4, 8):
+        raise ValueError("activation bits must be 8 or 4")
+    return 2 ** (bits - 1) - 1
 
-    beta_m = max_k |X_mk|;  X~_mk = RoundClip(X_mk * (127 / (beta_m + eps)), -127, 127).
-    Returns (X~ int8 [M][K], x_scale fp32 [M] = beta/127, x_sum int64 [M], beta fp32 [M]).
+
+def quantize_activations(X: np.ndarray, bits: int = 8):
+    """Per-token absmax quantisation ([B158] section 2, absmax scaling), b = 8
+    (int8) by default or b = 4 (values in [-7, 7], still one per byte).
+
+    beta_m = max_k |X_mk|;  X~_mk = RoundClip(X_mk * (Qm / (beta_m + eps)), -Qm, Qm),
+    Qm = 2^(b-1) - 1.  Returns (X~ int8 [M][K], x_scale fp32 [M] = beta/Qm,
+    x_sum int64 [M], beta fp32 [M]).
     """
+    qm = act_qmax(bits)
     X = np.ascontiguousarray(X, dtype=np.float32)
     beta = np.abs(X).max(axis=1) if X.shape[1] else np.zeros(X.shape[0], np.float32)
-    inv = np.float32(QMAX) / (beta + EPS)            # fp32 add, fp32 divide
+    inv = np.float32(qm) / (beta + EPS)               # fp32 add, fp32 divide
     q = X * inv[:, None]                              # one fp32 multiply per element
-    Xq = round_clip(q, -QMAX, QMAX).astype(np.int8)
-    x_scale = beta / np.float32(QMAX)                 # fp32 divide
+    Xq = round_clip(q, -qm, qm).astype(np.int8)
+    x_scale = beta / np.float32(qm)                   # fp32 divide
     x_sum = Xq.astype(np.int64).sum(axis=1)
     return Xq, x_scale.astype(np.float32), x_sum, beta.astype(np.float32)
 
@@ -391,25 +405,26 @@ def masked_add_matmul(Wt: np.ndarray, Xq: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Rescale
 # --------------------------------------------------------------------------
-def rescale(acc: np.ndarray, gamma: np.float32, beta: np.ndarray) -> np.ndarray:
+def rescale(acc: np.ndarray, gamma: np.float32, beta: np.ndarray, bits: int = 8) -> np.ndarray:
     """Y = (X~ W~^T) * beta * gamma / (Q_b - 1)  ([B158] section 2), in float64.
 
     beta is the per-token absmax (without epsilon).  Returns float64 [M][N].
     """
     return (acc.astype(np.float64) * np.float64(gamma)
-            * np.asarray(beta, dtype=np.float64)[:, None] / QMAX)
+            * np.asarray(beta, dtype=np.float64)[:, None] / act_qmax(bits))
 
 
 # --------------------------------------------------------------------------
 # The whole projection
 # --------------------------------------------------------------------------
-def bitlinear(W: np.ndarray, X: np.ndarray) -> dict:
-    """Every intermediate of the projection for latent W [N][K] and X [M][K]."""
+def bitlinear(W: np.ndarray, X: np.ndarray, bits: int = 8) -> dict:
+    """Every intermediate of the projection for latent W [N][K] and X [M][K]
+    (activations quantised to `bits` bits)."""
     gamma = absmean_gamma(W)
     Wt = ternarize(W, gamma)
     packed = pack_codes(Wt)
-    Xq, x_scale, x_sum, beta = quantize_activations(X)
+    Xq, x_scale, x_sum, beta = quantize_activations(X, bits)
     acc = integer_matmul(Wt, Xq)
-    y = rescale(acc, gamma, beta)
+    y = rescale(acc, gamma, beta, bits)
     return dict(gamma=gamma, Wt=Wt, packed=packed, Xq=Xq, x_scale=x_scale,
                 x_sum=x_sum, beta=beta, acc=acc, y=y)

@@ -414,6 +414,43 @@ def test_worked_example_end_to_end():
     assert (c @ r["Xq"][0].astype(int) - g["x_sum"][0]).tolist() == acc0
 
 
+def test_a4_worked_example():
+    """4-bit activations: hand-derived X~, sum and accumulators
+    (tests/golden/worked_example_a4.json, with its citation and derivation)."""
+    import json
+    import os
+    gd = os.path.join(os.path.dirname(__file__), "golden")
+    g = json.load(open(os.path.join(gd, "worked_example_a4.json")))
+    g8 = json.load(open(os.path.join(gd, "worked_example.json")))
+    r = O.bitlinear(np.array(g8["W"], np.float32), np.array(g["X"], np.float32), bits=4)
+    assert r["Xq"].tolist() == g["X_q"]
+    assert r["x_sum"].tolist() == g["x_sum"]
+    assert r["acc"].tolist() == g["acc"]
+    assert r["x_scale"][0] == np.float32(4.0) / np.float32(7)
+    num, den = g8["gamma_num_den"]
+    assert abs(r["y"][0, 1] - (-15 * num / den * 4 / 7)) < 1e-12
+
+
+def test_a4_invariants():
+    """|X~| <= 7; the absmax element maps to +-7 once beta >= 13 eps (beta 7 /
+    (beta + eps) >= 6.5); reconstruction within (beta + eps) / 14 up to fp32
+    rounding; values on the grid k beta / 7 (beta a power of two, no eps
+    effect at this scale) come back as k; ties round half up."""
+    rng = np.random.default_rng(41)
+    X = (rng.standard_normal((64, 512)) * rng.uniform(0.01, 30, (64, 1))).astype(np.float32)
+    Xq, xs, xsum, beta = O.quantize_activations(X, bits=4)
+    assert np.abs(Xq).max() <= 7 and Xq.dtype == np.int8
+    am = np.abs(X).argmax(axis=1)
+    assert (np.abs(Xq[np.arange(64), am]) == 7).all()
+    err = np.abs(X.astype(np.float64) - Xq * (beta[:, None].astype(np.float64) + 1e-5) / 7)
+    assert (err <= (beta[:, None] + 1e-5) / 14 * (1 + 1e-5)).all()
+    assert (xsum == Xq.astype(np.int64).sum(1)).all()
+    # the 8-bit default is unchanged
+    assert (O.quantize_activations(X)[0] == O.quantize_activations(X, bits=8)[0]).all()
+    with pytest.raises(ValueError):
+        O.quantize_activations(X, bits=2)
+
+
 # ---------------------------------------------------------------- RMS normalisation
 def test_sum_squares_bruteforce_fraction_tiny():
     # Fraction(float) is the exact value of each element; squares and sums of
