@@ -130,6 +130,22 @@ bitlinear_status bitlinear_quant_acts(const float* X, int64_t M, int64_t K,
                                       int8_t* X_q, float* x_scale, int32_t* x_sum,
                                       void* stream);
 
+/*
+ * The quantiser of bitlinear_quant_acts at b-bit width (page section 2,
+ * absmax scaling with Q_b = 2^(b-1) levels per sign): bits = 8 computes
+ * exactly bitlinear_quant_acts; bits = 4 gives the 4-bit activations ("A4")
+ * of the W1A4KV2 combination that the page "The End of Matrix
+ * Multiplications: Welcome to Addition" names without a quantiser:
+ *   X~ = RoundClip(X * 7 / (beta + eps), -7, 7),  x_scale = beta / 7,
+ * stored one value per int8 element, so every projection entry point
+ * (bitlinear_forward, _grouped, _base3) takes them unchanged and its
+ * epilogue rescales by that x_scale.  Arguments as bitlinear_quant_acts;
+ * bits other than 8 and 4 return BITLINEAR_ERR_DTYPE.
+ */
+bitlinear_status bitlinear_quant_acts_bits(const float* X, int64_t M, int64_t K, int bits,
+                                           int8_t* X_q, float* x_scale, int32_t* x_sum,
+                                           void* stream);
+
 /* Bytes of workspace bitlinear_forward needs: int32 partial accumulators
  * when the shape runs as a tiled product with K split across workgroups
  * (few output tiles and a long K, e.g. 33 <= M <= 128 with M K > 256 Ki on

@@ -25,8 +25,9 @@ reason in the design notes):
     even); the page gives the mean, not a summation order.
   * Activations use one absmax per token (the page allows per-token or
     per-tensor) and the symmetric range [-127, 127] (Q_b - 1 = 127).  The
-    4-bit activations the page's overview names (A4) take the same formula
-    with Q_b = 2^(4-1): the range [-7, 7] and x_scale = beta / 7.
+    4-bit activations that "The End of Matrix Multiplications" names (A4,
+    no formula there) take the same formula with Q_b = 2^(4-1): the range
+    [-7, 7] and x_scale = beta / 7.
   * The per-token reciprocal 127 / (absmax + eps) is formed in fp32 first and
     each element is multiplied by it (one fp32 multiply per element).
   * RMS normalisation before the quantiser ([B158] section 2 names it and
@@ -322,7 +323,8 @@ def rmsnorm(X: np.ndarray, g: np.ndarray, ms=None):
 def act_qmax(bits: int) -> int:
     """Q_b - 1 for b-bit symmetric activations: Q_b = 2^(b - 1) levels per sign
     ([B158] section 2 gives it for b = 8; b = 4 is the "A4" of the W1A4KV2
-    standard its overview names, with no formula of its own)."""
+    combination named by "The End of Matrix Multiplications: Welcome to
+    Addition", which prints no quantiser of its own)."""
     if bits not in (4, 8):
         raise ValueError("activation bits must be 8 or 4")
     return 2 ** (bits - 1) - 1

@@ -27,6 +27,8 @@ SIGNATURES = {
     "bitlinear_pack_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
     "bitlinear_pack_weights": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_size, _vp]),
     "bitlinear_quant_acts": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "bitlinear_quant_acts_bits": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, _vp, _vp, _vp,
+                                                 _vp]),
     "bitlinear_forward_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "bitlinear_forward": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp,
                                          ctypes.c_int, _vp, _c_size, _vp]),
@@ -204,8 +206,9 @@ def bitlinear_base3_to_blt2(W_packed3, K, W_packed=None, stream=None):
     return W_packed
 
 
-def bitlinear_quant_acts(X, X_q=None, x_scale=None, x_sum=None, stream=None):
-    """X [M][K] fp32 -> (X_q int8 [M][K], x_scale fp32 [M], x_sum int32 [M])."""
+def bitlinear_quant_acts(X, X_q=None, x_scale=None, x_sum=None, stream=None, bits=8):
+    """X [M][K] fp32 -> (X_q int8 [M][K], x_scale fp32 [M], x_sum int32 [M]); bits = 8,
+    or 4 for activations in [-7, 7] (still one per int8 element)."""
     import torch
     lib = load()
     _dev(X, torch.float32, "X")
@@ -219,8 +222,8 @@ def bitlinear_quant_acts(X, X_q=None, x_scale=None, x_sum=None, stream=None):
     _dev(X_q, torch.int8, "X_q")
     _dev(x_scale, torch.float32, "x_scale")
     _dev(x_sum, torch.int32, "x_sum")
-    _check(lib.bitlinear_quant_acts(X.data_ptr(), M, K, X_q.data_ptr(), x_scale.data_ptr(),
-                                    x_sum.data_ptr(), _stream(stream)))
+    _check(lib.bitlinear_quant_acts_bits(X.data_ptr(), M, K, bits, X_q.data_ptr(),
+                                         x_scale.data_ptr(), x_sum.data_ptr(), _stream(stream)))
     return X_q, x_scale, x_sum
 
 

@@ -112,7 +112,15 @@ bitlinear_status bitlinear_pack_weights(const float* W, int64_t N, int64_t K, ui
 
 bitlinear_status bitlinear_quant_acts(const float* X, int64_t M, int64_t K, int8_t* X_q,
                                       float* x_scale, int32_t* x_sum, void* stream) {
+  return bitlinear_quant_acts_bits(X, M, K, 8, X_q, x_scale, x_sum, stream);
+}
+
+bitlinear_status bitlinear_quant_acts_bits(const float* X, int64_t M, int64_t K, int bits,
+                                           int8_t* X_q, float* x_scale, int32_t* x_sum,
+                                           void* stream) {
   if (!X || !X_q || !x_scale || !x_sum) return fail(BITLINEAR_ERR_NULL, "quant_acts: NULL buffer");
+  if (bits != 8 && bits != 4)
+    return fail(BITLINEAR_ERR_DTYPE, "quant_acts: activation bits %d (8 or 4)", bits);
   if (M < 1 || M > kMaxDim || !shape_ok_k(K))
     return fail(BITLINEAR_ERR_SHAPE, "quant_acts: invalid shape M=%lld K=%lld", (long long)M,
                 (long long)K);
@@ -121,7 +129,7 @@ bitlinear_status bitlinear_quant_acts(const float* X, int64_t M, int64_t K, int8
   bitlinear_status s = check_device();
   if (s != BITLINEAR_OK) return s;
   return launched(bl::launch_quant(X, M, K, X_q, x_scale, x_sum,
-                                   reinterpret_cast<hipStream_t>(stream)),
+                                   reinterpret_cast<hipStream_t>(stream), bits),
                   "quant_acts launch");
 }
 

@@ -14,7 +14,8 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* W_packed, 
                        void* workspace, hipStream_t stream);
 
 hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float* x_scale,
-                        int32_t* x_sum, hipStream_t stream);
+                        int32_t* x_sum, hipStream_t stream,
+                        int bits = 8);
 
 // RMS normalisation with gain G [K], then the same quantiser.
 hipError_t launch_rmsnorm_quant(const float* X, const float* G, int64_t M, int64_t K,

@@ -60,11 +60,14 @@ __device__ __forceinline__ int32_t block_sum(int32_t v, int32_t* sh) {
 // R float4 per thread held in registers: the row is read once, with every
 // load in flight together.  R = 0 selects the looped variant (two passes) for
 // rows longer than the register-resident maximum.
+// qmax = Q_b - 1: 127 for int8 activations, 7 for 4-bit ones (stored one
+// per byte).  The per-element clip to +-127 is inactive at either width:
+// |x| (qmax / (beta + eps)) stays below qmax + 1/2.
 template <int R, int T = kQuantThreads>
 __global__ __launch_bounds__(T) void k_quant_acts(const float* __restrict__ X,
                                                   int64_t K, int8_t* __restrict__ Xq,
                                                   float* __restrict__ x_scale,
-                                                  int32_t* __restrict__ x_sum) {
+                                                  int32_t* __restrict__ x_sum, float qmax) {
   __shared__ uint32_t s_max[T / kWave];
   __shared__ int32_t s_sum[T / kWave];
   const int64_t m = blockIdx.x;
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(T) void k_quant_acts(const float* __restrict__ X,
                            max(abs_bits(v[r].z), abs_bits(v[r].w))));
     amax = block_max<T>(amax, s_max);
     const float beta = __uint_as_float(amax);
-    const float inv = 127.0f / (beta + 1e-5f);
+    const float inv = qmax / (beta + 1e-5f);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t i = threadIdx.x + (int64_t)r * T;
@@ -100,13 +103,13 @@ __global__ __launch_bounds__(T) void k_quant_acts(const float* __restrict__ X,
     }
     amax = block_max<T>(amax, s_max);
     const float beta = __uint_as_float(amax);
-    const float inv = 127.0f / (beta + 1e-5f);
+    const float inv = qmax / (beta + 1e-5f);
     for (int64_t i = threadIdx.x; i < K4; i += T) qrow[i] = quant4(row[i], inv, sum);
   }
   sum = block_sum<T>(sum, s_sum);
   if (threadIdx.x == 0) {
     x_sum[m] = sum;
-    x_scale[m] = __uint_as_float(amax) / 127.0f;
+    x_scale[m] = __uint_as_float(amax) / qmax;
   }
 }
 
@@ -217,12 +220,13 @@ hipError_t launch_rmsnorm_quant(const float* X, const float* G, int64_t M, int64
 }
 
 hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float* x_scale,
-                        int32_t* x_sum, hipStream_t stream) {
+                        int32_t* x_sum, hipStream_t stream, int bits) {
+  const float qmax = bits == 4 ? 7.0f : 127.0f;
   const dim3 grid((unsigned)M);
   const bool wide = K > kQuantWideKPlain;
   const int T = wide ? kQuantWideThreads : kQuantThreads;
   const int64_t per = (K / 4 + T - 1) / T;   // float4 per thread
-#define BL_Q(RR, TT) k_quant_acts<RR, TT><<<grid, dim3(TT), 0, stream>>>(X, K, X_q, x_scale, x_sum)
+#define BL_Q(RR, TT) k_quant_acts<RR, TT><<<grid, dim3(TT), 0, stream>>>(X, K, X_q, x_scale, x_sum, qmax)
   if (!wide) {
     if (per <= 1) BL_Q(1, kQuantThreads);
     else if (per <= 2) BL_Q(2, kQuantThreads);

@@ -267,3 +267,10 @@ def test_base3_validation_without_gpu_calls(lib):
     assert lib.bitlinear_base3_to_blt2(FAKE, 4, 4096, None, None) == 1
     assert lib.bitlinear_base3_to_blt2(FAKE, 4, 4100, FAKE, None) == 2
     assert lib.bitlinear_base3_to_blt2(FAKE + 4, 4, 4096, FAKE, None) == 3
+
+
+def test_quant_bits_validation_without_gpu_calls(lib):
+    assert lib.bitlinear_quant_acts_bits(FAKE, 2, 64, 5, FAKE, FAKE, FAKE, None) == 4
+    assert lib.bitlinear_quant_acts_bits(FAKE, 2, 64, 16, FAKE, FAKE, FAKE, None) == 4
+    assert lib.bitlinear_quant_acts_bits(None, 2, 64, 4, FAKE, FAKE, FAKE, None) == 1
+    assert lib.bitlinear_quant_acts_bits(FAKE, 2, 40, 4, FAKE, FAKE, FAKE, None) == 2
