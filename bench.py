@@ -282,6 +282,8 @@ def main():
         ("TOP/s" if prefill else "GB/s"): proj_roof["achieved"],
         "entry_point": proj_roof["entry_point"],
         "epilogue": f"gamma*beta rescale fused, {out} out"}
+    if prefill:
+        rows["vendor_int8_mm"] = vendor_int8_mm(tb, torch, timer, stream, dom, M)
     f32_bytes = P.N * P.K // 4 + 4 * M * P.K + OUT_BYTES[out] * M * P.N + 4
     rows["forward_f32"] = {"shape": f"M{M} {P.K}->{P.N}", "us": round(t_fwd * 1e6, 3),
                            "fused": dom["fused"],
@@ -432,6 +434,42 @@ def alg_bytes_f32(P, M, out):
     """Algorithmic bytes of one fused launch (quantiser in the prologue):
     packed W, fp32 X, Y, gamma."""
     return P.N * P.K // 4 + 4 * M * P.K + OUT_BYTES[out] * M * P.N + 4
+
+
+def vendor_int8_mm(tb, torch, timer, stream, q, M):
+    """The vendor's int8 GEMM (torch._int_mm, hipBLASLt underneath) on the same
+    operands as the projection: X~ [M][K] and W~ unpacked to int8 [N][K] (four
+    times the packed bytes), given as the transposed right operand, its faster
+    layout here.  It calibrates the MFMA fraction on this chip with these
+    value distributions; it is not part of the path.  Its int32 product must
+    equal the projection's raw accumulators."""
+    P = q["p"]
+    N, K = P.N, P.K
+    if not hasattr(torch, "_int_mm"):
+        return {"note": "torch._int_mm not available"}
+    with torch.cuda.stream(stream):
+        # BLT2-v1: byte i of word g holds k = 16 g + 4 j + i at bits 2j..2j+1
+        b = q["Wp"].view(N, K // 16, 1, 4).to(torch.int16)
+        sh = torch.arange(0, 8, 2, device=b.device, dtype=torch.int16).view(1, 1, 4, 1)
+        Wt8 = (((b >> sh) & 3) - 1).to(torch.int8).reshape(N, K).contiguous()
+        del b
+        acc_v = torch._int_mm(q["Xq"], Wt8.t())
+    acc = tb.bitlinear_forward(q["Wp"], q["g"], q["Xq"], q["s"], q["xs"], N=N, K=K,
+                               y_dtype="i32", stream=stream)
+    stream.synchronize()
+    same = bool(torch.equal(acc, acc_v))
+    del acc, acc_v
+    reps = 20
+    timer(lambda: torch._int_mm(q["Xq"], Wt8.t()), 3)
+    t = timer(lambda: torch._int_mm(q["Xq"], Wt8.t()), reps) / reps
+    del Wt8
+    torch.cuda.empty_cache()
+    tops = 2 * M * N * K / t / 1e12
+    return {"shape": f"M{M} {K}->{N}", "us": round(t * 1e6, 2), "TOP/s": round(tops, 1),
+            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+            "equals_forward_accumulators": same,
+            "note": "torch._int_mm on W~ unpacked to int8 (4x the bytes), one weight copy: "
+                    "calibration, not the path"}
 
 
 def launch_alg_bytes(shapes, M, out, fused, grouped):
