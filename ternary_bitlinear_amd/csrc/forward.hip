@@ -105,6 +105,8 @@ struct DecodeArgs {
   int8_t* Xq_out;          // kAFuse: optional copies of the quantiser outputs
   float* xs_out;
   int32_t* xsum_out;
+  int splits;              // k_skinny, one projection: K splits (<= 1: none)
+  int32_t* part;           //   and their raw partial accumulators [splits][M][N]
 };
 
 inline DecodeArgs decode_args_one(const uint8_t* Wp, const float* gamma, int N, int K, int M,
@@ -1464,7 +1466,11 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
   int8_t* const sX[4] = {sX0, sX1, sX2, sX3};
   uint8_t* const sW[4] = {sW0, sW1, sW2, sW3};
 
-  const DecodeView view = decode_view(da, blockIdx.x);
+  // With K split S ways (one projection), the S workgroups of a row group
+  // are adjacent and split sp takes chunks [cb, cb + nch).
+  const int S = da.splits > 1 ? da.splits : 1;
+  const int wg = blockIdx.x / S, sp = blockIdx.x - wg * S;
+  const DecodeView view = decode_view(da, wg);
   const int N = view.N, K = da.K, M = da.M;
   const uint8_t* const Wp = view.Wp;
   const int lane = threadIdx.x & (kWave - 1);
@@ -1474,7 +1480,10 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
   const int nb0 = view.unit * RB;             // first row block of the workgroup
   const int npieces = K / 64;
   const int kbytes = K / 4;
-  const int nch = (K + CK - 1) / CK;
+  const int nch_all = (K + CK - 1) / CK;
+  const int cps = (nch_all + S - 1) / S;
+  const int cb = min(sp * cps, nch_all);
+  const int nch = min(cps, nch_all - cb);     // >= 1 (skinny_splits sizes S so)
 
   // Epilogue inputs now, so no memory round trip follows the reduction.
   const float gamma = view.gamma[0];
@@ -1502,7 +1511,7 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
       const int r = off / CK;
       const int q = ((off % CK) / 16) ^ (r & 15);
       const int m = min(r, M - 1);
-      const int k = min(c * CK + 16 * q, K - 16);
+      const int k = min((cb + c) * CK + 16 * q, K - 16);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(da.Xq + (int64_t)m * K + k),
                                        static_cast<void*>(A + 1024 * b), 16, 0, 0);
     }
@@ -1511,7 +1520,7 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
       const int r = off / WROW;                 // row within the workgroup's 16 RB rows
       const int q = ((off % WROW) / 16) ^ (r & WSW);
       const int n = min(16 * nb0 + r, N - 1);
-      const int kb = min(c * (CK / 4) + 16 * q, kbytes - 16);
+      const int kb = min((cb + c) * (CK / 4) + 16 * q, kbytes - 16);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(Wp + (int64_t)n * kbytes + kb),
                                        static_cast<void*>(B + 1024 * wave), 16, 0, 0);
     }
@@ -1536,7 +1545,7 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
       wait_vmcnt<(SP - 1) * NLD>();
       stage_barrier();
       // pieces past K: code 0 (the mask does not depend on the loaded value)
-      const uint32_t wmask = c * (CK / 64) + qw < npieces ? 0xffffffffu : 0u;
+      const uint32_t wmask = (cb + c) * (CK / 64) + qw < npieces ? 0xffffffffu : 0u;
       skinny_step<TG, NWK>(sX[s], sW[s], sX[(s + SP) % NS], sW[(s + SP) % NS],
                            [&](int8_t* An, uint8_t* Bn) { issue(min(c + SP, nch - 1), An, Bn); },
                            wr, qw, j, wmask, acc);
@@ -1566,6 +1575,21 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
   // Lane (j, g) register r of token group tg: token 16 tg + 4 g + r, row n.
   const int n = 16 * (nb0 + rb) + j;
   if (n >= N) return;
+  if (S > 1) {
+    // Raw partial sums of this split; k_splitk_reduce adds the splits and
+    // applies the epilogue.
+    int32_t* P = da.part + (int64_t)sp * M * N;
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      const int32_t v[4] = {acc[tg].x, acc[tg].y, acc[tg].z, acc[tg].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * tg + 4 * g + r;
+        if (m < M) P[(int64_t)m * N + n] = v[r];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     const int32_t v[4] = {acc[tg].x, acc[tg].y, acc[tg].z, acc[tg].w};
@@ -1579,8 +1603,27 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
 
 template <int TG, int RB, int NWK, int SP, int OUT>
 hipError_t launch_skinny_t(DecodeArgs da, hipStream_t stream) {
-  const int grid = set_units(da, 16 * RB);
+  const int grid = set_units(da, 16 * RB) * (da.splits > 1 ? da.splits : 1);
   k_skinny<TG, RB, NWK, SP, OUT><<<dim3(grid), dim3(RB * NWK * kWave), 0, stream>>>(da);
+  return hipGetLastError();
+}
+
+// K split S ways over one projection: raw partial sums into `part`
+// ([S][M][N] int32, exact), then k_splitk_reduce adds them in split order
+// and applies the epilogue.
+template <int TG, int RB, int NWK, int SP, int OUT>
+hipError_t launch_skinny_split_t(DecodeArgs da, int S, int32_t* part, int vec_out,
+                                 hipStream_t stream) {
+  if (da.G != 1 || S < 2 || S > kMaxSplits) return hipErrorInvalidValue;
+  da.splits = S;
+  da.part = part;
+  hipError_t e = launch_skinny_t<TG, RB, NWK, SP, OUT>(da, stream);
+  if (e != hipSuccess) return e;
+  const GemmArgs ga{da.Wp[0], da.gamma[0], da.Ng[0], da.K, da.M, da.Xq, da.xs, da.xsum,
+                    da.Y[0], 0, 0, vec_out, 0, S, part};
+  const int64_t MN = (int64_t)ga.M * ga.N;
+  const int64_t threads = ga.N % 4 == 0 ? MN / 4 : MN;
+  k_splitk_reduce<OUT><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(ga);
   return hipGetLastError();
 }
 
@@ -1634,6 +1677,48 @@ hipError_t launch_skinny(const DecodeArgs& da, hipStream_t stream) {
   }
 }
 
+// 17-64 tokens on one projection whose K is long against its rows (K >= 2 N,
+// M K > 256 Ki): the skinny kernel with 4 row blocks per workgroup (8 at 33+
+// tokens on 8192+ rows), so that more rows share each activation chunk, and
+// K split S ways to keep about 256 workgroups; the partial sums are added
+// exactly by k_splitk_reduce.  Timed on MI355X (bf16 out): 8192 <- 28672 at
+// 64 tokens 25.5 us against 38.4 us for the GEMM, at 32 tokens 20.4 against
+// 23.4 us for the unsplit skinny kernel; 4096 <- 11008 at 33-64 tokens
+// 6-8 % faster than the GEMM, at 32 tokens 5 % faster than unsplit.  Wide
+// projections (4096 -> 11008) and 16 tokens were slower split.
+struct SkinnySplit {
+  int tg, rb, s;   // token groups, row blocks per workgroup, K splits (s < 2: none)
+};
+
+inline SkinnySplit skinny_split_cfg(int64_t M, int64_t N, int64_t K) {
+  SkinnySplit c{0, 0, 1};
+  if (M < 17 || M > 64 || K % 64 != 0 || K < 2 * N || M * K <= 256 * 1024) return c;
+  const int64_t nrb = (N + 15) / 16;
+  c.tg = M <= 32 ? 2 : 4;
+  c.rb = (c.tg == 4 && nrb >= 512) ? 8 : 4;
+  const int64_t groups = (nrb + c.rb - 1) / c.rb;
+  int s = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(2, (256 + groups / 2) / groups));
+  // every split gets at least two 512-wide chunks
+  const int64_t nch = (K + 511) / 512;
+  while (s >= 2 && nch < 2 * s) --s;
+  c.s = s;
+  return c;
+}
+
+inline size_t skinny_split_workspace_bytes(const SkinnySplit& c, int64_t M, int64_t N) {
+  return c.s < 2 ? 0 : (size_t)(((c.s * M * N * 4) + 255) / 256 * 256);
+}
+
+template <int OUT>
+hipError_t launch_skinny_split(const SkinnySplit& c, const DecodeArgs& da, void* workspace,
+                               hipStream_t stream) {
+  const uintptr_t ya = reinterpret_cast<uintptr_t>(da.Y[0]);
+  const int vec_out = (da.Ng[0] % 4 == 0) && (ya % (OUT == kOutBF16 ? 8 : 16) == 0);
+  int32_t* part = reinterpret_cast<int32_t*>(workspace);
+  if (c.tg == 2) return launch_skinny_split_t<2, 4, 2, 2, OUT>(da, c.s, part, vec_out, stream);
+  if (c.rb == 8) return launch_skinny_split_t<4, 8, 2, 2, OUT>(da, c.s, part, vec_out, stream);
+  return launch_skinny_split_t<4, 4, 2, 2, OUT>(da, c.s, part, vec_out, stream);
+}
 
 struct GemmCfg {
   int bm, bn;
@@ -1723,15 +1808,27 @@ hipError_t dispatch_out(const uint8_t* Wp, const float* gamma, int N, int K, con
 
 }  // namespace
 
-size_t forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+namespace {
+// Workspace of one projection on the GEMM (0 where the shape takes another kernel).
+size_t gemm_path_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || skinny_ok(M, 16 * ((N + 15) / 16), K)) return 0;
   return gemm_workspace_bytes(gemm_cfg((int)M, (int)N, (int)K), M, N);
 }
+}  // namespace
 
+size_t forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const SkinnySplit ss = skinny_split_cfg(M, N, K);
+  if (ss.s >= 2) return skinny_split_workspace_bytes(ss, M, N);
+  return gemm_path_workspace_bytes(M, N, K);
+}
+
+// A group splits no projection's K in the skinny kernel: it runs as one
+// skinny or decode launch, or as one GEMM per projection.
 size_t forward_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K) {
+  if (G == 1) return forward_workspace_bytes(M, N[0], K);
   if (M <= 16 || skinny_ok(M, group_rows(G, N), K)) return 0;   // one launch over the group
   size_t need = 0;
-  for (int g = 0; g < G; ++g) need = std::max(need, forward_workspace_bytes(M, N[g], K));
+  for (int g = 0; g < G; ++g) need = std::max(need, gemm_path_workspace_bytes(M, N[g], K));
   return need;
 }
 
@@ -1760,6 +1857,9 @@ hipError_t forward_grouped_out(int G, const uint8_t* const* Wp, const float* con
   da.Xq = Xq;
   da.xs = xs;
   da.xsum = xsum;
+  // One projection with a long K: the K-split skinny kernel.
+  const SkinnySplit ss = G == 1 ? skinny_split_cfg(M, N[0], K) : SkinnySplit{0, 0, 1};
+  if (ss.s >= 2) return launch_skinny_split<OUT>(ss, da, workspace, stream);
   // Every projection of the group in one launch where the skinny kernel or
   // the decode takes the shape.
   if (skinny_ok(M, decode_rows(da), K)) return launch_skinny<OUT>(da, stream);
@@ -1953,6 +2053,7 @@ int forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K) {
     if (fused_dot(M, K, entry == 2)) return kKernelDecodeDot | kFused;
     if (entry == 1 && afuse(M, G, N, K)) return kKernelDecode | kFused;
   }
+  if (G == 1 && skinny_split_cfg(M, N[0], K).s >= 2) return kKernelSkinny;
   if (skinny_ok(M, group_rows(G, N), K)) return kKernelSkinny;
   if (M <= 16) return M == 1 && K % 64 == 0 && K <= 64 * 64 ? kKernelDecodeDot : kKernelDecode;
   return kKernelGemm;

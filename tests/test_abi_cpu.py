@@ -199,8 +199,8 @@ def test_rmsnorm_validation_without_gpu_calls(lib):
 
 def test_forward_kernel_query(lib):
     """The host-side kernel choice: fixed points of the dispatch rule, and
-    agreement with the workspace queries (a fused launch needs none, only the
-    GEMM asks for projection workspace)."""
+    agreement with the workspace queries (a fused launch needs none; only the
+    GEMM and the K-split skinny kernel ask for projection workspace)."""
     import ctypes
     import ternary_bitlinear_amd as tb
     fk = tb.forward_kernel
@@ -219,7 +219,9 @@ def test_forward_kernel_query(lib):
     assert fk("forward", 8, [4096], 4112) == ("k_decode", False)        # K % 64 != 0
     assert fk("forward", 32, [4096], 28672) == ("k_skinny", False)
     assert fk("forward", 64, [4096], 4096) == ("k_skinny", False)
-    assert fk("forward", 64, [4096], 11008) == ("k_gemm", False)
+    assert fk("forward", 64, [4096], 11008) == ("k_skinny", False)     # K split
+    assert fk("forward", 64, [4096, 4096], 11008) == ("k_gemm", False)  # a group: no split
+    assert fk("forward", 64, [11008], 8192) == ("k_gemm", False)         # K < 2 N
     assert fk("forward", 2048, [11008], 4096) == ("k_gemm", False)
     assert fk("f32", 8, [4096] * 3, 4096) == ("k_skinny", False)        # quantiser first
     assert fk("f32", 2, [4096], 4096) == ("k_decode", True)
@@ -236,7 +238,28 @@ def test_forward_kernel_query(lib):
             name, fused = fk("f32", M, [N], K)
             assert fused == (tb.forward_f32_workspace_bytes(M, N, K) == 0), (M, N, K)
             if tb.forward_workspace_bytes(M, N, K) > 0:
-                assert fk("forward", M, [N], K)[0] == "k_gemm", (M, N, K)
+                kern = fk("forward", M, [N], K)[0]
+                assert kern == "k_gemm" or (kern == "k_skinny" and 17 <= M <= 64
+                                            and K >= 2 * N), (M, N, K)
+
+
+def test_skinny_split_rule():
+    """The K-split skinny kernel (one projection, 17-64 tokens, K >= 2 N and
+    M K > 256 Ki): its workspace is S M N int32 partial sums, S chosen for
+    about 256 workgroups of 4 row blocks (8 at 33+ tokens on 8192+ rows)."""
+    import ternary_bitlinear_amd as tb
+    ws = tb.forward_workspace_bytes
+    assert ws(64, 4096, 11008) == 4 * 64 * 4096 * 4        # 64 row groups, S = 4
+    assert ws(64, 8192, 28672) == 4 * 64 * 8192 * 4        # 8 row blocks: 64 groups, S = 4
+    assert ws(32, 8192, 28672) == 2 * 32 * 8192 * 4        # 128 groups, S = 2
+    assert ws(32, 4096, 11008) == 4 * 32 * 4096 * 4
+    assert ws(17, 1000, 16384) == -(-4 * 17 * 1000 * 4 // 256) * 256   # ragged N; 256 B units
+    assert ws(16, 4096, 11008) == 0                        # 16 tokens: unsplit skinny
+    assert ws(64, 11008, 4096) == 0                        # K < 2 N
+    assert ws(20, 4096, 8192) == 0                         # M K <= 256 Ki
+    for M, N, K in ((64, 4096, 11008), (17, 1000, 16384), (32, 8192, 28672)):
+        assert tb.forward_kernel("forward", M, [N], K) == ("k_skinny", False)
+        assert tb.forward_f32_workspace_bytes(M, N, K) >= ws(M, N, K) > 0
 
 
 def test_base3_validation_without_gpu_calls(lib):
