@@ -147,10 +147,11 @@ bitlinear_status bitlinear_quant_acts_bits(const float* X, int64_t M, int64_t K,
                                            void* stream);
 
 /* Bytes of workspace bitlinear_forward needs: int32 partial accumulators
- * when the shape runs as a tiled product with K split across workgroups
- * (few output tiles and a long K, e.g. 33 <= M <= 128 with M K > 256 Ki on
- * a few-thousand-row matrix), else 0 (a NULL workspace is then accepted).
- * 0 if the shape is invalid. */
+ * where K is split across workgroups (added exactly by a second launch):
+ * the tiled product with few output tiles and a long K (e.g. 33 <= M <= 128
+ * with M K > 256 Ki on a few-thousand-row matrix), and the skinny kernel on
+ * a K at least twice N at 17 <= M <= 64 with M K > 256 Ki; else 0 (a NULL
+ * workspace is then accepted).  0 if the shape is invalid. */
 size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -389,7 +390,8 @@ bitlinear_status bitlinear_base3_to_blt2(const uint8_t* W_packed3, int64_t N, in
 typedef enum bitlinear_kernel {
   BITLINEAR_KERNEL_DECODE_DOT = 1, /* one token: dot products on the vector ALU */
   BITLINEAR_KERNEL_DECODE = 2,     /* up to 16 tokens: matrix instructions, weights streamed once */
-  BITLINEAR_KERNEL_SKINNY = 3,     /* 2-64 tokens: activations and codes through an LDS ring */
+  BITLINEAR_KERNEL_SKINNY = 3,     /* 2-64 tokens: activations and codes through an LDS ring
+                                      (K split over workgroups on long-K shapes) */
   BITLINEAR_KERNEL_GEMM = 4,       /* tiled matrix product (K split over workgroups when tiles are few) */
   BITLINEAR_KERNEL_FUSED_QUANT = 16 /* or'ed in: the activation quantiser runs in the same launch */
 } bitlinear_kernel;
