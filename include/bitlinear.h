@@ -148,9 +148,10 @@ bitlinear_status bitlinear_quant_acts_bits(const float* X, int64_t M, int64_t K,
 
 /* Bytes of workspace bitlinear_forward needs: int32 partial accumulators
  * where K is split across workgroups (added exactly by a second launch):
- * the tiled product with few output tiles and a long K (e.g. 33 <= M <= 128
- * with M K > 256 Ki on a few-thousand-row matrix), and the skinny kernel on
- * a K at least twice N at 17 <= M <= 64 with M K > 256 Ki; else 0 (a NULL
+ * the tiled product with few output tiles and a long K (e.g. 65 <= M <= 128
+ * with M K > 256 Ki, or 33 <= M <= 64 with K > 8192, on a few-thousand-row
+ * matrix), and the skinny kernel on a K at least twice N at 17 <= M <= 64
+ * with M K > 256 Ki; else 0 (a NULL
  * workspace is then accepted).  0 if the shape is invalid. */
 size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

@@ -1634,8 +1634,9 @@ hipError_t launch_skinny_split_t(DecodeArgs da, int S, int32_t* part, int vec_ou
 //   2-7 tokens: the matrix decode keeps more weight loads in flight on
 //     narrow outputs (< 384 row blocks), and at 2 tokens on matrices of
 //     less than 2^27 weights;
-//   33-64 tokens: the GEMM's K split wins once a workgroup's activations
-//     outgrow its codes (M K > 256 Ki, e.g. 4096 <- 11008 at 64 tokens).
+//   33-64 tokens: up to K = 8192 (8192 <- 8192 at 64 tokens: 13.7 us
+//     against 16.5 us for the GEMM; 28672 <- 8192: 23.7 against 36.7 us);
+//     longer K takes the GEMM unless the K-split skinny kernel applies.
 inline int64_t group_rows(int G, const int64_t* N) {
   int64_t rows = 0;
   for (int g = 0; g < G; ++g) rows += 16 * ((N[g] + 15) / 16);
@@ -1644,7 +1645,7 @@ inline int64_t group_rows(int G, const int64_t* N) {
 
 inline bool skinny_ok(int64_t M, int64_t rows, int64_t K) {
   if (K % 64 != 0 || M < 2 || M > 64) return false;
-  if (M > 32) return M * K <= 256 * 1024;
+  if (M > 32) return K <= 8192;
   if (M >= 8) return true;
   if (rows < 16 * 384) return false;
   return M > 2 || rows * K >= (int64_t(1) << 27);
@@ -1667,14 +1668,18 @@ hipError_t launch_skinny(const DecodeArgs& da, hipStream_t stream) {
   const int nrb = decode_rows(da) / 16;
   if (da.M <= 16) return launch_skinny_tg<1, OUT>(da, nrb, stream);
   if (da.M <= 32) return launch_skinny_tg<2, OUT>(da, nrb, stream);
-  // 33-64 tokens (activation stages of 32 KB): 2 waves per row block, about
-  // 256 workgroups of up to 4 row blocks.
-  switch (std::min(4, std::max(1, (nrb + 255) / 256))) {
-    case 1: return launch_skinny_t<4, 1, 2, 2, OUT>(da, stream);
-    case 2: return launch_skinny_t<4, 2, 2, 2, OUT>(da, stream);
-    case 3: return launch_skinny_t<4, 3, 2, 2, OUT>(da, stream);
-    default: return launch_skinny_t<4, 4, 2, 2, OUT>(da, stream);
-  }
+  // 33-64 tokens (at 2 waves per row block, activation stages of 32 KB and
+  // one workgroup per CU): as
+  // many row blocks per workgroup as keep the launch to one round of at most
+  // 256 workgroups, 2 waves per row block, and 8 one-wave row blocks past
+  // 1024 row blocks.  Timed at 64 tokens: 4096 rows 8.9 us at 2 row blocks
+  // (9.4 at 1); 11008 rows 10.3 us at 3 (16.6 at 2, two rounds); 28672 rows
+  // 23.7 us at 8 one-wave row blocks (29.5 at 4 of 2 waves, two rounds).
+  if (nrb > 1024) return launch_skinny_t<4, 8, 1, 2, OUT>(da, stream);
+  if (nrb > 768) return launch_skinny_t<4, 4, 2, 2, OUT>(da, stream);
+  if (nrb > 512) return launch_skinny_t<4, 3, 2, 2, OUT>(da, stream);
+  if (nrb > 128) return launch_skinny_t<4, 2, 2, 2, OUT>(da, stream);
+  return launch_skinny_t<4, 1, 2, 2, OUT>(da, stream);
 }
 
 // 17-64 tokens on one projection whose K is long against its rows (K >= 2 N,

@@ -64,19 +64,20 @@ def test_size_queries(lib):
     assert 256 < ws <= 256 + 8192 * 10 * 8
     assert lib.bitlinear_pack_workspace_bytes(1, 16) >= 256 + 4 * 80
     assert lib.bitlinear_pack_workspace_bytes(1 << 20, 1 << 12) == 0   # N*K >= 2^31
-    # decode (M <= 16), skinny (M <= 64, M K <= 256 Ki) and many-tile shapes
-    # need no workspace; few tiles with a long K split K: S int32 partial
-    # tiles, S <= K / (16 M), 256-byte rounded
+    # decode (M <= 16), unsplit skinny (M <= 64; K <= 8192 above 32 tokens)
+    # and many-tile shapes need no workspace; few tiles with a long K split K:
+    # S int32 partial tiles, S <= K / (16 M), 256-byte rounded
     assert lib.bitlinear_forward_workspace_bytes(4, 4096, 4096) == 0
     assert lib.bitlinear_forward_workspace_bytes(64, 4096, 4096) == 0
     assert lib.bitlinear_forward_workspace_bytes(2048, 11008, 4096) == 0
-    ws = lib.bitlinear_forward_workspace_bytes(64, 4096, 4160)
-    assert ws == 4 * 64 * 4096 * 4
+    assert lib.bitlinear_forward_workspace_bytes(64, 8192, 8192) == 0   # skinny
+    ws = lib.bitlinear_forward_workspace_bytes(64, 8192, 12288)           # GEMM, 128 tiles
+    assert ws == 4 * 64 * 8192 * 4
     ws = lib.bitlinear_forward_workspace_bytes(64, 4096, 11008)
     assert ws % (64 * 4096 * 4) == 0 and 2 <= ws // (64 * 4096 * 4) <= 16
     assert lib.bitlinear_forward_workspace_bytes(0, 4096, 4096) == 0
-    f32 = lib.bitlinear_forward_f32_workspace_bytes(64, 4096, 4160)
-    assert f32 >= 64 * 4160 + 8 * 64 + 4 * 64 * 4096 * 4
+    f32 = lib.bitlinear_forward_f32_workspace_bytes(64, 8192, 12288)
+    assert f32 >= 64 * 12288 + 8 * 64 + 4 * 64 * 8192 * 4
 
 
 def _last(lib):
@@ -111,8 +112,8 @@ def test_validation_statuses_without_gpu_calls(lib):
     bad = list(args); bad[8] = FAKE + 1     # bf16 Y needs 2-byte alignment
     assert lib.bitlinear_forward(*bad) == 3
     # a split-K shape: workspace missing, too small, misaligned
-    split = [FAKE, FAKE, 4096, 4160, FAKE, FAKE, FAKE, 64, FAKE, 1, None, 0, None]
-    need = lib.bitlinear_forward_workspace_bytes(64, 4096, 4160)
+    split = [FAKE, FAKE, 8192, 12288, FAKE, FAKE, FAKE, 64, FAKE, 1, None, 0, None]
+    need = lib.bitlinear_forward_workspace_bytes(64, 8192, 12288)
     assert lib.bitlinear_forward(*split) == 7 and "workspace" in _last(lib)
     bad = list(split); bad[10] = FAKE; bad[11] = need - 16
     assert lib.bitlinear_forward(*bad) == 7
@@ -147,9 +148,12 @@ def test_grouped_validation_without_gpu_calls(lib):
     # decode shapes need no workspace; a split GEMM group needs the largest member's
     assert lib.bitlinear_forward_grouped_workspace_bytes(1, 3, ns, 4096) == 0
     assert lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 4096) == 0   # skinny
-    big = lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 4160)
-    assert big == max(lib.bitlinear_forward_workspace_bytes(64, n, 4160) for n in (4096, 1024, 1024))
-    assert big > 0 and call(M=64, K=4160) == 7
+    assert lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 8192) == 0   # skinny
+    # past K = 8192 at 64 tokens: one GEMM per projection (a group never
+    # splits K in the skinny kernel), K split 4 ways on the 4096-row member
+    big = lib.bitlinear_forward_grouped_workspace_bytes(64, 3, ns, 12288)
+    assert big == 4 * 64 * 4096 * 4
+    assert call(M=64, K=12288) == 7
     assert lib.bitlinear_forward_grouped_workspace_bytes(1, 5, ns, 4096) == 0
     f32 = lib.bitlinear_forward_f32_grouped(3, ptrs, ptrs, ns, 4096, None, 1, ptrs, 1,
                                             None, None, None, None, 0, None)
@@ -221,7 +225,9 @@ def test_forward_kernel_query(lib):
     assert fk("forward", 64, [4096], 4096) == ("k_skinny", False)
     assert fk("forward", 64, [4096], 11008) == ("k_skinny", False)     # K split
     assert fk("forward", 64, [4096, 4096], 11008) == ("k_gemm", False)  # a group: no split
-    assert fk("forward", 64, [11008], 8192) == ("k_gemm", False)         # K < 2 N
+    assert fk("forward", 64, [11008], 8192) == ("k_skinny", False)       # K <= 8192
+    assert fk("forward", 64, [28672], 8192) == ("k_skinny", False)
+    assert fk("forward", 64, [11008], 12288) == ("k_gemm", False)        # K > 8192, K < 2 N
     assert fk("forward", 2048, [11008], 4096) == ("k_gemm", False)
     assert fk("f32", 8, [4096] * 3, 4096) == ("k_skinny", False)        # quantiser first
     assert fk("f32", 2, [4096], 4096) == ("k_decode", True)

@@ -157,15 +157,18 @@ FWD_SHAPES = [
     # N % 4 != 0 (scalar partial stores), two row tiles
     (24, 200, 4160), (40, 130, 2064), (100, 64, 8192),
     # skinny kernel (K % 64 == 0; 8-32 tokens, 2-7 on wide outputs, 33-64
-    # with M K <= 256 Ki): fewer chunks than ring stages, K ending inside a
+    # up to K = 8192): fewer chunks than ring stages, K ending inside a
     # chunk, ragged N in the last workgroup's row blocks, 1 row block of 4
     # waves / 2 of 4 / 4 of 2 per workgroup, 16 / 32 / 64 token groups with
-    # ragged M
+    # ragged M; at 33-64 tokens 1, 2, 3, 4 row blocks of 2 waves and 8 of 1
+    # wave (a last workgroup of one row block, K ending inside a chunk,
+    # fewer chunks than stages); past K = 8192 the GEMM, K split
     (2, 16384, 8192), (3, 6144, 64), (5, 10000, 128), (8, 100, 64), (9, 1, 128),
     (8, 4099, 4096), (12, 4096, 11008), (16, 16400, 704), (16, 28672, 1024),
     (17, 257, 576), (24, 4096, 11008), (31, 3000, 8192), (32, 6200, 3072),
     (33, 1030, 2048), (48, 11990, 5440), (63, 4100, 4096), (64, 64, 4096), (64, 20, 64),
-    (45, 6000, 192),
+    (45, 6000, 192), (40, 16000, 1024), (64, 16400, 1088), (37, 20000, 320),
+    (40, 5000, 8320),
 ]
 
 
