@@ -228,6 +228,8 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
  * (M <= 16, and up to 64 tokens where the skinny kernel applies) run as one
  * launch over the rows of all G matrices, so the group pays one launch
  * instead of G; tiled-product shapes run the projections one after another.
+ * With G > 1 the skinny kernel never splits K (with G = 1 the call is
+ * bitlinear_forward, which may).
  *
  * G          1 .. BITLINEAR_MAX_GROUP.
  * W_packed, gamma, N, Y   HOST arrays of G entries (read during the call,
