@@ -543,10 +543,13 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
     g.replay()
     per_replay = 1 if grouped else len(projs)
     launches_per_replay = copies * per_replay
-    reps = max(1, (4000 if not prefill else 200) // launches_per_replay)
-    t_all = timer(g.replay, reps)
-    n_launch = reps * launches_per_replay
-    t_launch = t_all / n_launch
+    # the replays in ROOF_GROUPS timed groups; the median group's mean launch
+    # is reported, with the spread of the group means
+    reps = max(1, (4000 if not prefill else 200) // (launches_per_replay * ROOF_GROUPS))
+    per_group = sorted(timer(g.replay, reps) / (reps * launches_per_replay)
+                       for _ in range(ROOF_GROUPS))
+    n_launch = ROOF_GROUPS * reps * launches_per_replay
+    t_launch = per_group[ROOF_GROUPS // 2]
     shapes = [q["p"] for q in projs]
     bytes_launch = launch_alg_bytes(shapes, M, out, fused, grouped)
     ops_launch = sum(2 * M * P.N * P.K for P in shapes) / (1 if grouped else len(shapes))
@@ -565,17 +568,20 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
         "kernel": kern, "entry_point": api,
         "shape": f"M{M} " + ", ".join(f"{P.K}->{P.N}" for P in shapes),
         "us_per_launch": round(t_launch * 1e6, 3), "launches_timed": n_launch,
+        "us_per_launch_min_max": [round(per_group[0] * 1e6, 3), round(per_group[-1] * 1e6, 3)],
         "algorithmic_bytes_per_launch": int(bytes_launch),
         "ops_per_launch": int(ops_launch),
         "grouped": grouped, "fused_quantiser": fused,
-        "timing": f"HIP events on the launch stream around a graph of back-to-back {api} "
-                  + ("launches (all projections in one, " if grouped
-                     else "launches (every projection, ")
-                  + "rotated weight copies)"})
+        "timing": f"HIP events on the launch stream around replays of a graph of back-to-back "
+                  f"{api} launches ("
+                  + ("all projections in one, " if grouped else "every projection, ")
+                  + f"rotated weight copies), in {ROOF_GROUPS} timed groups: the median "
+                  "group's mean launch"})
     return roof, t_launch
 
 
 CAL_BYTES = 256 << 20        # the calibration copy reads and writes this many bytes
+ROOF_GROUPS = 9              # timed groups of the roofline's graph replays
 
 
 def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=False,
