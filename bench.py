@@ -406,7 +406,13 @@ def main():
     # ---------------- CPU oracle on a bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(projs, M, args.cpu_seconds, wbytes_step, prefill)
+        # the timed step once more, its outputs for the oracle leg to check
+        with torch.cuda.stream(stream):
+            step(0)
+        stream.synchronize()
+        y_gpu = [q["Y"].float().cpu().numpy() for q in projs]
+        cpu = cpu_baseline(projs, M, args.cpu_seconds, wbytes_step, prefill, grouped, y_gpu,
+                           out)
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
@@ -742,9 +748,12 @@ def load_traffic(kernel, projs, M, out, fused=False):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(projs, M, seconds, wbytes_step, prefill):
+def cpu_baseline(projs, M, seconds, wbytes_step, prefill, grouped, y_gpu, out):
     """The oracle's per-step work (quantise, integer product, rescale) for every
-    projection, repeated on the host for about `seconds`."""
+    projection, repeated on the host for about `seconds`; its last step's
+    outputs are compared element by element with the GPU step's (y_gpu):
+    |y - y_oracle| <= tol |y_oracle| (1e-5 fp32, 1e-2 bf16), and exactly 0
+    where the accumulator is 0."""
     import numpy as np
     from oracle import bitlinear_oracle as O
     try:
@@ -755,16 +764,20 @@ def cpu_baseline(projs, M, seconds, wbytes_step, prefill):
     prep = []
     for q in projs:
         gamma = O.absmean_gamma(q["W_host"])
-        prep.append((O.ternarize(q["W_host"], gamma), gamma, q["X_host"]))
+        # a grouped step feeds every projection the first one's activations
+        X = projs[0]["X_host"] if grouped else q["X_host"]
+        prep.append((O.ternarize(q["W_host"], gamma), gamma, X))
 
     def one_step():
+        ys = []
         for Wt, gamma, X in prep:
             Xq, _, _, beta = O.quantize_activations(X)
-            O.rescale(O.integer_matmul(Wt, Xq), gamma, beta)
+            ys.append(O.rescale(O.integer_matmul(Wt, Xq), gamma, beta))
+        return ys
     n = 0
     t0 = time.perf_counter()
     while True:
-        one_step()
+        ys = one_step()
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or (n >= 1 and el * (n + 1) / n > 3 * seconds):
@@ -775,9 +788,18 @@ def cpu_baseline(projs, M, seconds, wbytes_step, prefill):
         v, unit = ops / per / 1e12, "TOP/s"
     else:
         v, unit = wbytes_step / per / 1e9, "GB/s"
+    tol = {"f32": 1e-5, "bf16": 1e-2}[out]
+    bad = 0
+    for y, yg in zip(ys, y_gpu):
+        zero = y == 0
+        bad += int((yg[zero] != 0).sum())
+        bad += int((np.abs(yg - y) > tol * np.abs(y))[~zero].sum())
     return {"value": round(v, 6), "unit": unit, "cores": cores, "kind": "oracle",
             "sample": f"{n} full steps of the same workload ({el:.1f} s)",
-            "ms_per_step": round(per * 1e3, 3)}
+            "ms_per_step": round(per * 1e3, 3),
+            "timed_outputs_checked": int(sum(y.size for y in ys)),
+            "timed_outputs_mismatched": bad,
+            "timed_outputs_tolerance": f"{tol:g} relative ({out}); exact 0 for a zero accumulator"}
 
 
 if __name__ == "__main__":
