@@ -1935,7 +1935,10 @@ inline DecodeCfg fused_cfg(int64_t M, int G, const int64_t* N, int64_t K) {
 // workgroup, except at Q = 3, 4 without the normalisation: 2 rows per wave
 // and 8 waves, timed faster there (3200 <- 8640: 5.8 vs 6.3 us; 4096 <-
 // 11008: 6.6 vs 6.9 us; 8192 <- 12288: 9.3-9.8 vs 10.0-10.4 us) and no
-// faster at Q = 1, 2.  At Q = 4 (8192 <- 16384) it takes 12.3-12.7 us
+// faster at Q = 1, 2; and at Q = 2 without the normalisation on 16384+
+// output rows, 4 rows per wave and 8 waves (half as many workgroups, each
+// converting the row once: 28672 <- 8192 15.8 vs 16.4 us, 16384 <- 8192
+// 10.1 vs 11.0 us; 8 waves were no faster at Q = 1).  At Q = 4 (8192 <- 16384) it takes 12.3-12.7 us
 // against 14.6 us for the matrix decode with the quantiser in its prologue;
 // beyond (Q = 5..7: 4096 <- 20480, 8192 <- 28672) it no longer wins.  With
 // the normalisation the 4-wave split of the row stays: its fp64 sum of
@@ -1954,7 +1957,11 @@ template <int OUT, bool NORM>
 hipError_t fused_dot_out(const DecodeArgs& da, hipStream_t stream) {
   const int q = (da.K + 64 * 64 - 1) / (64 * 64);
   if (q <= 1) return launch_decode_dot_t<OUT, kDotFuseRows, 1, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
-  if (q == 2) return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
+  if (q == 2) {
+    if (!NORM && decode_rows(da) >= 16384)
+      return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, 8, false>(da, stream);
+    return launch_decode_dot_t<OUT, kDotFuseRows, 2, kDotFuseBlock, kDotFuseWaves, NORM>(da, stream);
+  }
   if constexpr (NORM) {
     return launch_decode_dot_t<OUT, kDotFuseRows, 3, kDotFuseBlock, kDotFuseWaves, true>(da, stream);
   } else {

@@ -390,10 +390,14 @@ FUSED_SHAPES = [
     (1, 5, 4160), (1, 77, 8192), (1, 4096, 11008), (1, 33, 12288), (1, 9, 12352),
     # four pieces per lane, the activations of one piece held at a time
     (1, 1000, 16384), (1, 3, 16320), (1, 300, 14336), (1, 7, 16448),
+    # two pieces per lane on 16384+ rows (8 waves per workgroup), the last
+    # wave and workgroup partly past the end
+    (1, 16390, 4160),
     # outside the fused kernel's reach: two launches
     (9, 77, 1040), (16, 300, 4096), (8, 64, 8640), (40, 130, 1024), (2, 50, 40960),
-    # two launches with K split across workgroups (workspace needed either way)
-    (48, 200, 4096),
+    # two launches with K split across workgroups (workspace needed either
+    # way): the skinny kernel's split, the GEMM's
+    (48, 200, 8192), (100, 64, 8192),
 ]
 
 
@@ -439,15 +443,15 @@ GROUP_CASES = [
     (3, 4096, (4096, 1024, 1024)),
     (16, 1040, (300, 17, 64, 129)),
     (16, 8192, (2048, 1040)),
-    (40, 4096, (512, 200)),
+    (40, 12288, (512, 200)),
     (130, 1040, (300, 64)),
     # one skinny launch over the group (workgroups never straddle two
     # projections): 4 row blocks per workgroup, 2 of 4 waves, 1 of 4 waves,
-    # 64 tokens
+    # 64 tokens (and 40 tokens up to K = 8192)
     (8, 4096, (4096, 4096, 4096)),
     (32, 4096, (4096, 1024, 1024)),
     (20, 2048, (1000, 17, 3, 2000)),
-    (64, 1024, (3000, 5000)),
+    (64, 1024, (3000, 5000)), (40, 4096, (512, 200)),
 ]
 
 
