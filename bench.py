@@ -783,11 +783,35 @@ def cpu_baseline(projs, M, seconds, wbytes_step, prefill, grouped, y_gpu, out):
         if el >= seconds or (n >= 1 and el * (n + 1) / n > 3 * seconds):
             break
     per = el / n
+    macs = sum(M * q["p"].N * q["p"].K for q in projs)
     if prefill:
-        ops = sum(2 * M * q["p"].N * q["p"].K for q in projs)
-        v, unit = ops / per / 1e12, "TOP/s"
+        v, unit = 2 * macs / per / 1e12, "TOP/s"
     else:
         v, unit = wbytes_step / per / 1e9, "GB/s"
+    # the same step on one thread (decode shapes only: a prefill step takes
+    # tens of seconds there), for about a third of the time
+    single = None
+    if not prefill:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                n1, t1 = 0, time.perf_counter()
+                while True:
+                    one_step()
+                    n1 += 1
+                    e1 = time.perf_counter() - t1
+                    if e1 >= seconds / 3:
+                        break
+            single = {"value": round(wbytes_step / (e1 / n1) / 1e9, 6), "unit": "GB/s",
+                      "ms_per_step": round(e1 / n1 * 1e3, 3), "sample": f"{n1} steps ({e1:.1f} s)"}
+        except Exception:  # pragma: no cover
+            single = None
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     tol = {"f32": 1e-5, "bf16": 1e-2}[out]
     bad = 0
     for y, yg in zip(ys, y_gpu):
@@ -797,6 +821,9 @@ def cpu_baseline(projs, M, seconds, wbytes_step, prefill, grouped, y_gpu, out):
     return {"value": round(v, 6), "unit": unit, "cores": cores, "kind": "oracle",
             "sample": f"{n} full steps of the same workload ({el:.1f} s)",
             "ms_per_step": round(per * 1e3, 3),
+            "gmac_per_s": round(macs / per / 1e9, 3),
+            "cpu_model": cpu_model, "nproc": os.cpu_count(),
+            "single_core": single,
             "timed_outputs_checked": int(sum(y.size for y in ys)),
             "timed_outputs_mismatched": bad,
             "timed_outputs_tolerance": f"{tol:g} relative ({out}); exact 0 for a zero accumulator"}
