@@ -1703,9 +1703,10 @@ inline SkinnySplit skinny_split_cfg(int64_t M, int64_t N, int64_t K) {
   c.rb = (c.tg == 4 && nrb >= 512) ? 8 : 4;
   const int64_t groups = (nrb + c.rb - 1) / c.rb;
   int s = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(2, (256 + groups / 2) / groups));
-  // every split gets at least two 512-wide chunks
+  // two 512-wide chunks per split on average, and none empty: the kernel
+  // gives split sp the chunks from sp * ceil(nch / s) on
   const int64_t nch = (K + 511) / 512;
-  while (s >= 2 && nch < 2 * s) --s;
+  while (s >= 2 && (nch < 2 * s || (s - 1) * ((nch + s - 1) / s) >= nch)) --s;
   c.s = s;
   return c;
 }

@@ -263,6 +263,8 @@ def test_skinny_split_rule():
     assert ws(16, 4096, 11008) == 0                        # 16 tokens: unsplit skinny
     assert ws(64, 11008, 4096) == 0                        # K < 2 N
     assert ws(20, 4096, 8192) == 0                         # M K <= 256 Ki
+    # 9 chunks: 4 splits of ceil(9 / 4) = 3 would leave the last one empty
+    assert ws(64, 2000, 4160) == 3 * 64 * 2000 * 4
     for M, N, K in ((64, 4096, 11008), (17, 1000, 16384), (32, 8192, 28672)):
         assert tb.forward_kernel("forward", M, [N], K) == ("k_skinny", False)
         assert tb.forward_f32_workspace_bytes(M, N, K) >= ws(M, N, K) > 0

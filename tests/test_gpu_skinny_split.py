@@ -16,9 +16,9 @@ pytestmark = pytest.mark.gpu
 # (M, N, K): two and four token groups; 4 and 8 row blocks per workgroup;
 # ragged N (1000, 999, 8200: the last row group part-empty; 999 also rules
 # out vector stores); K ending inside a 512-wide chunk (11008) or 64 into one
-# (16448); 2 to 4 splits.
+# (16448); 2 to 4 splits (3 where 4 would leave a split without a chunk).
 SPLIT_SHAPES = [(17, 1000, 16384), (32, 4096, 11008), (33, 999, 8192), (48, 2000, 8192),
-                (40, 300, 65536), (64, 8200, 16448)]
+                (40, 300, 65536), (64, 8200, 16448), (64, 2000, 4160)]
 
 
 def _is_split(M, N, K):
