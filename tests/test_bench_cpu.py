@@ -1,0 +1,41 @@
+"""The bench's algorithmic bytes per launch (the numerator of the roofline's
+`achieved`), against per-call totals worked out by hand for the workloads'
+shapes (MB, two decimals): packed W (N K / 4) + X~ (M K) + per-token scale
+and sum + Y (2 M N for bf16).  No GPU."""
+import pytest
+
+import bench
+from synth import WORKLOADS
+
+
+def _p(wname, pname):
+    return next(q for q in WORKLOADS[wname].projections if q.name == pname)
+
+
+@pytest.mark.parametrize("wname,pname,M,mb", [
+    ("decode-3b", "ffn_up", 1, 6.93),
+    ("decode-7b", "ffn_up", 1, 11.30), ("decode-7b", "ffn_up", 8, 11.48),
+    ("decode-7b", "ffn_up", 32, 12.11), ("decode-7b", "ffn_up", 64, 12.94),
+    ("prefill-7b", "ffn_up", 2048, 64.76),
+    ("ffn-70b", "ffn_up", 1, 58.8),
+])
+def test_alg_bytes_match_the_tables(wname, pname, M, mb):
+    P = _p(wname, pname)
+    b = bench.alg_bytes(P, M, "bf16")
+    assert b == P.N * P.K // 4 + M * P.K + 8 * M + 2 * M * P.N + 4
+    assert abs(b / 1e6 - mb) < 0.0105 * max(1.0, mb / 10), (b, mb)
+
+
+def test_fused_and_grouped_counting():
+    P = _p("decode-3b", "ffn_up")
+    # fused: fp32 X read in place of X~, x_scale and x_sum
+    assert bench.alg_bytes_f32(P, 1, "bf16") - bench.alg_bytes(P, 1, "bf16") == 4 * P.K - P.K - 8
+    qkv = list(WORKLOADS["attn-qkv-7b"].projections)
+    M = 16
+    one = [bench.alg_bytes(Q, M, "bf16") for Q in qkv]
+    # a grouped launch reads the shared activations once
+    assert bench.launch_alg_bytes(qkv, M, "bf16", False, True) == sum(one) - 2 * (M * 4096 + 8 * M)
+    # separate launches: the mean launch
+    ffn = list(WORKLOADS["decode-3b"].projections)
+    want = sum(bench.alg_bytes_f32(Q, 1, "bf16") for Q in ffn) / 2
+    assert bench.launch_alg_bytes(ffn, 1, "bf16", True, False) == want
