@@ -146,10 +146,18 @@ hipError_t launch_b3_q(const B3Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Rows per wave and token capacity by M.  Decoding costs about two vector
+// instructions per weight, so at one token the rows are spread over more
+// waves: 2 rows per wave below 16384 rows (timed on MI355X: 8640 <- 3200
+// 5.8 vs 6.8 us at 4 rows, 4096 <- 11008 7.6 vs 8.1 us), 4 rows on wider
+// outputs (28672 <- 8192: 22.3 vs 22.8 us at 2).  At 5-8 tokens an 8-token
+// instance (11008 <- 4096 at 8 tokens: 21.2 vs 22.0 us for the 16-token one).
 template <int OUT>
 hipError_t launch_b3_out(const B3Args& a, hipStream_t stream) {
-  if (a.M <= 1) return launch_b3_q<OUT, 4, 1>(a, stream);
+  if (a.M <= 1) return a.N >= 16384 ? launch_b3_q<OUT, 4, 1>(a, stream)
+                                    : launch_b3_q<OUT, 2, 1>(a, stream);
   if (a.M <= 4) return launch_b3_q<OUT, 2, 4>(a, stream);
+  if (a.M <= 8) return launch_b3_q<OUT, 1, 8>(a, stream);
   return launch_b3_q<OUT, 1, 16>(a, stream);
 }
 
