@@ -169,6 +169,8 @@ FWD_SHAPES = [
     (33, 1030, 2048), (48, 11990, 5440), (63, 4100, 4096), (64, 64, 4096), (64, 20, 64),
     (45, 6000, 192), (40, 16000, 1024), (64, 16400, 1088), (37, 20000, 320),
     (40, 5000, 8320),
+    # 128 x 256 GEMM tiles (1024+ tokens, K <= 8192): ragged M and N, a K tail
+    (1030, 300, 1040), (1024, 520, 4160),
 ]
 
 
