@@ -277,12 +277,11 @@ bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_pa
  * Zhang and Sennrich, "Root Mean Square Layer Normalization"):
  *   y_k = x_k / sqrt(mean_k x_k^2 + eps) * g_k,   eps = 1e-5,
  * per token, with a gain vector g and no centring.  The mean of squares is
- * accumulated in fp64 and rounded once to fp32; then one fp32 add, a correctly
- * rounded fp32 square root and reciprocal r, and y_k = fl32(fl32(x_k r) g_k).
- * The fp64 sum equals the exact sum to within K 2^-53 (relative), so the fp32
- * mean is the correctly rounded one except when the exact mean lies that close
- * to a rounding boundary between two fp32 values.  Then y goes through exactly
- * bitlinear_quant_acts.
+ * the exact rational sum_k x_k^2 / K rounded once to fp32 (nearest, ties to
+ * even; the sum is accumulated in exact integer arithmetic, so the result does
+ * not depend on the launch shape); then one fp32 add, a correctly rounded fp32
+ * square root and reciprocal r, and y_k = fl32(fl32(x_k r) g_k).  Then y goes
+ * through exactly bitlinear_quant_acts.
  *
  * X       [M][K] fp32, device, 16-byte aligned (read only).
  * norm_g  [K] fp32 gain, device, 16-byte aligned (read only).

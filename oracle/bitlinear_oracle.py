@@ -278,39 +278,24 @@ def exact_sum_squares(X: np.ndarray) -> list:
     return out
 
 
-def mean_square_candidates(X: np.ndarray, rel_err: float) -> list:
-    """Per row, the fp32 values fl32(m') for every m' within relative rel_err
-    of the exact mean of squares m: the correctly rounded value and, when m
-    lies that close to a rounding boundary, its neighbour across it.  (Rounding
-    is monotone, so the two ends of the interval bound every case.)  A
-    computation that accumulates the mean with at most that error may return
-    any of them, and no other value.  rel_err must be far below an fp32
-    spacing (2^-24 relative), so at most one boundary lies in the interval."""
-    assert 0 <= rel_err < 2.0 ** -26, "the interval must be far narrower than an fp32 spacing"
+def mean_square(X: np.ndarray) -> np.ndarray:
+    """Per row, the mean of squares sum_k x_k^2 / K: the exact rational,
+    rounded once to fp32 (nearest, ties to even).  fp32 [M]."""
     X = np.ascontiguousarray(X, dtype=np.float32)
     K = X.shape[1]
-    e = Fraction(rel_err)
-    out = []
-    for s in exact_sum_squares(X):
-        m = s / K
-        out.append(sorted({f32_nearest(m), f32_nearest(m * (1 - e)), f32_nearest(m * (1 + e))}))
-    return out
+    return np.array([f32_nearest(s / K) for s in exact_sum_squares(X)], dtype=np.float32)
 
 
-def rmsnorm(X: np.ndarray, g: np.ndarray, ms=None):
+def rmsnorm(X: np.ndarray, g: np.ndarray):
     """RMS-normalised activations ([B158] section 2; the normalisation of the
     reference it cites), fp32 [M][K], and the per-token reciprocal r [M].
 
     ms = fl32(exact mean of x^2);  d = fl32(sqrt(fl32(ms + eps)));  r = fl32(1 / d);
-    y_k = fl32(fl32(x_k r) g_k).  `ms` may be given per row (fp32) instead,
-    to follow a row through another admissible rounding of the mean.
+    y_k = fl32(fl32(x_k r) g_k).
     """
     X = np.ascontiguousarray(X, dtype=np.float32)
     g = np.ascontiguousarray(g, dtype=np.float32)
-    M, K = X.shape
-    if ms is None:
-        ms = np.array([f32_nearest(s / K) for s in exact_sum_squares(X)], dtype=np.float32)
-    ms = np.asarray(ms, dtype=np.float32)
+    ms = mean_square(X)
     d = np.sqrt(ms + EPS)                                # fp32 add, correctly rounded fp32 sqrt
     r = np.float32(1.0) / d                              # correctly rounded fp32 division
     Y = (X * r[:, None]) * g[None, :]                    # two fp32 multiplies per element

@@ -1,21 +1,28 @@
-"""Build the HIP library libbitlinear.so in-tree for gfx950 (hipcc, no GPU needed)."""
+"""Build the HIP library libbitlinear.so in-tree for gfx950 (hipcc, no GPU needed).
+
+Each source compiles to an object of its own (in parallel); the objects are
+linked into one shared library.  Every kernel is launched from the source that
+defines it, so no device code crosses objects.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["abi.hip", "pack.hip", "quant.hip", "forward.hip", "base3.hip"]
+OBJ_DIR = os.path.join(PKG, "_build")
+SOURCES = ["abi.hip", "pack.hip", "quant.hip", "forward.hip", "base3.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: no multiply-add fusion anywhere (the quantisers' rounding
 #   decisions depend on each fp32 operation rounding on its own).
 # -Xclang -target-feature -Xclang -packed-fp32-ops: no packed fp32 VALU ops.
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math",
     "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -23,18 +30,26 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed ({r.returncode})")
+        raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd[-3:])}")
     if verbose and (r.stdout or r.stderr):
         sys.stderr.write(r.stdout + r.stderr)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    objs = [os.path.join(OBJ_DIR, s.replace(".hip", ".o")) for s in srcs]
+    cmds = [[HIPCC, *FLAGS, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(srcs, objs)]
+    with ThreadPoolExecutor(max_workers=jobs or min(len(cmds), os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     # A kernel the host pass rejects silently leaves its launch stub undefined;
     # a shared library links anyway and only fails at load time.  Refuse it.
     nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)

@@ -587,7 +587,7 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
   constexpr int kJ = FUSE == kDotFuseBlock ? kFuseK4 / (WV * kWave) : 1;   // groups per thread
   __shared__ uint32_t s_codes[FUSE == kDotFuseBlock ? kFuseK4 : 1];
   __shared__ uint32_t s_red[2][WV];
-  __shared__ double s_sq[NORM ? WV : 1];
+  __shared__ SqShared<WV * kWave> s_sq[1];   // used with NORM only
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * WV + wave;   // the wave's index over all projections
@@ -639,19 +639,26 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::"s"(gamma), "s"(yout));
     if constexpr (NORM) {
-      // RMS normalisation first (the standalone normalising quantiser's
-      // arithmetic and, with four waves, its exact fp64 summation order).
-      double sq = 0.0;
+      // RMS normalisation first: the standalone normalising quantiser's
+      // arithmetic (an exact mean of squares rounded once, so the partition
+      // of the row does not matter).  Groups past the row's end were loaded
+      // from its first group and are skipped.
+      auto visit = [&](auto&& f) {
 #pragma unroll
-      for (int j = 0; j < kJ; ++j)
-        if (threadIdx.x + WV * kWave * j < K4) sq += sum_sq4(xv[j]);
-      sq = wave_sum_f64(sq);
-      if (lane == 0) s_sq[wave] = sq;
-      __syncthreads();
-      double tot = s_sq[0];
+        for (int j = 0; j < kJ; ++j)
+          if (threadIdx.x + WV * kWave * j < K4) f(xv[j]);
+      };
+      float ms;
+      if (!block_mean_square_fast<WV * kWave>(visit, (uint32_t)K, s_sq[0], ms)) {
+        ms = block_mean_square_exact<WV * kWave>(src, K4, (uint32_t)K, s_sq[0]);
 #pragma unroll
-      for (int w = 1; w < WV; ++w) tot += s_sq[w];
-      const float rr = rms_reciprocal(tot, K);
+        for (int j = 0; j < kJ; ++j) {   // reloaded: nothing held across the exact path
+          const int i = threadIdx.x + WV * kWave * j;
+          xv[j] = src[i < K4 ? i : 0];
+          gv[j] = reinterpret_cast<const float4*>(da.norm_g)[i < K4 ? i : 0];
+        }
+      }
+      const float rr = rms_reciprocal(ms);
 #pragma unroll
       for (int j = 0; j < kJ; ++j) xv[j] = rms_apply(xv[j], rr, gv[j]);
     }
@@ -1953,9 +1960,8 @@ inline DecodeCfg fused_cfg(int64_t M, int G, const int64_t* N, int64_t K) {
 // 10.1 vs 11.0 us; 8 waves were no faster at Q = 1).  At Q = 4 (8192 <- 16384) it takes 12.3-12.7 us
 // against 14.6 us for the matrix decode with the quantiser in its prologue;
 // beyond (Q = 5..7: 4096 <- 20480, 8192 <- 28672) it no longer wins.  With
-// the normalisation the 4-wave split of the row stays: its fp64 sum of
-// squares must add in the standalone normalising quantiser's order (and
-// its fp32 row and gain then fill the registers at Q = 4).
+// the normalisation 4 rows per wave and 4 waves throughout (its fp32 row and
+// gain fill the registers at Q = 4, so it stops at Q = 3).
 constexpr int kDotFuseRows = 4;   // rows per wave in that mode
 constexpr int kDotFuseWaves = 4;  // waves per workgroup in that mode
 constexpr int kDotFuseMaxQ = 4;

@@ -26,8 +26,7 @@ constexpr int kQuantThreads = 256;
 // K = 8192 in 2.25 vs 2.91 us, 12288 in 2.8 vs 3.85 us, 28672 in 4.3 vs
 // 6.7 us, 65536 in 7.5 vs 22.3 us; the normalising quantiser at 28672 in
 // 6.7 vs 15.4 us, 65536 in 13.4 vs 32.4 us.  The normalising quantiser
-// keeps 256 threads up to 12288 values: the single-token decode's fused
-// prologue splits such rows the same way, so both form the same fp64 sums.
+// keeps 256 threads up to 12288 values.
 constexpr int64_t kQuantWideKPlain = 4096;
 constexpr int64_t kQuantWideK = 12288;
 constexpr int kQuantWideThreads = 4 * kQuantThreads;
@@ -113,34 +112,20 @@ __global__ __launch_bounds__(T) void k_quant_acts(const float* __restrict__ X,
   }
 }
 
-// Block-wide fp64 sum: waves added in wave order after the DPP tree, so the
-// order is the same in every launch (and the same as in the single-token
-// decode's fused prologue, which partitions a row the same way).
-template <int T>
-__device__ __forceinline__ double block_sum_f64(double v, double* sh) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  v = wave_sum_f64(v);
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  double t = sh[0];
-#pragma unroll
-  for (int w = 1; w < T / kWave; ++w) t += sh[w];
-  return t;
-}
-
 // RMS normalisation, then the absmax quantiser, per token (page section 2:
 // the activations are RMS-normalised, then quantised to int8).  One
-// workgroup per token; thread t holds groups of four t, t + 256, ... of the
-// row and of the gain (R of them in registers; R = 0: three passes over the
-// row for rows beyond the register-resident maximum).  Sum of squares in
-// fp64, then r = 1 / sqrt(fl32(sum / K) + eps); the normalised values
-// fl32(fl32(x r) g) go through the same absmax, factor and per-element
-// rounding as k_quant_acts.
+// workgroup per token; thread t holds groups of four t, t + T, ... of the row
+// and of the gain (R of them in registers; R = 0: passes over the row for
+// rows beyond the register-resident maximum).  The mean of squares is exact,
+// rounded once to fp32 (block_mean_square_fast, else _exact), then
+// r = 1 / sqrt(ms + eps); the
+// normalised values fl32(fl32(x r) g) go through the same absmax, factor and
+// per-element rounding as k_quant_acts.
 template <int R, int T = kQuantThreads>
 __global__ __launch_bounds__(T) void k_rmsnorm_quant(
     const float* __restrict__ X, const float* __restrict__ G, int64_t K, int8_t* __restrict__ Xq,
     float* __restrict__ x_scale, int32_t* __restrict__ x_sum) {
-  __shared__ double s_sq[T / kWave];
+  __shared__ SqShared<T> s_sq;
   __shared__ uint32_t s_max[T / kWave];
   __shared__ int32_t s_sum[T / kWave];
   const int64_t m = blockIdx.x;
@@ -160,10 +145,21 @@ __global__ __launch_bounds__(T) void k_rmsnorm_quant(
       v[r] = i < K4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
       gv[r] = i < K4 ? grow[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    double sq = 0.0;
+    auto visit = [&](auto&& f) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) sq += sum_sq4(v[r]);
-    const float rr = rms_reciprocal(block_sum_f64<T>(sq, s_sq), K);
+      for (int r = 0; r < R; ++r) f(v[r]);
+    };
+    float ms;
+    if (!block_mean_square_fast<T>(visit, (uint32_t)K, s_sq, ms)) {
+      ms = block_mean_square_exact<T>(row, K4, (uint32_t)K, s_sq);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {   // reloaded: nothing held across the exact path
+        const int64_t i = threadIdx.x + (int64_t)r * T;
+        v[r] = i < K4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        gv[r] = i < K4 ? grow[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    const float rr = rms_reciprocal(ms);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       v[r] = rms_apply(v[r], rr, gv[r]);
@@ -177,9 +173,13 @@ __global__ __launch_bounds__(T) void k_rmsnorm_quant(
       if (i < K4) qrow[i] = quant4(v[r], inv, sum);
     }
   } else {
-    double sq = 0.0;
-    for (int64_t i = threadIdx.x; i < K4; i += T) sq += sum_sq4(row[i]);
-    const float rr = rms_reciprocal(block_sum_f64<T>(sq, s_sq), K);
+    auto visit = [&](auto&& f) {
+      for (int64_t i = threadIdx.x; i < K4; i += T) f(row[i]);
+    };
+    float ms;
+    if (!block_mean_square_fast<T>(visit, (uint32_t)K, s_sq, ms))
+      ms = block_mean_square_exact<T>(row, K4, (uint32_t)K, s_sq);
+    const float rr = rms_reciprocal(ms);
     for (int64_t i = threadIdx.x; i < K4; i += T)
       amax = max(amax, absmax4(rms_apply(row[i], rr, grow[i])));
     amax = block_max<T>(amax, s_max);

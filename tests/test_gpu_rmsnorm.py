@@ -1,12 +1,8 @@
 """RMS normalisation before the quantiser on the GPU, against the oracle.
 
-The kernels accumulate the mean of squares in fp64 (relative error at most
-(K + 2) 2^-53); the oracle rounds the exact mean.  The two agree unless a
-row's exact mean lies within that error of an fp32 rounding boundary; for such
-a row both roundings are admissible, and the row is checked against the
-oracle's result for the one the GPU took (the oracle follows either through
-the rest of the path).  Everything after the mean -- X~, x_scale, x_sum,
-accumulators -- is then compared exactly.
+The kernels sum the squares exactly and round the mean once, as the oracle
+does, so X~, x_scale, x_sum and the accumulators are compared exactly with
+the oracle's single value for every row.
 """
 from fractions import Fraction
 
@@ -28,28 +24,11 @@ def _acts(M, K, name):
     return make_acts(0, name, M, K, {"outlier_frac": Fraction(1, 100), "outlier_scale": 50.0})
 
 
-def oracle_rms_quant(X, g, got_xq=None):
-    """The oracle's X~, x_scale, x_sum per row, at the admissible rounding of
-    the mean of squares that matches the GPU's X~ (the correctly rounded one
-    when the row has only that), and the number of rows with two."""
-    M, K = X.shape
-    cands = O.mean_square_candidates(X, (K + 2) * 2.0 ** -53)
-    Xq = np.empty((M, K), np.int8)
-    xs = np.empty(M, np.float32)
-    xsum = np.empty(M, np.int64)
-    for m in range(M):
-        options = []
-        for c in cands[m]:
-            Y, _ = O.rmsnorm(X[m:m + 1], g, ms=[c])
-            q, s, t, _ = O.quantize_activations(Y)
-            options.append((q[0], s[0], t[0]))
-        pick = options[0]
-        if got_xq is not None:
-            for o in options[1:]:
-                if np.array_equal(o[0], got_xq[m]):
-                    pick = o
-        Xq[m], xs[m], xsum[m] = pick
-    return Xq, xs, xsum, sum(len(c) > 1 for c in cands)
+def oracle_rms_quant(X, g):
+    """The oracle's X~, x_scale and x_sum of the normalised rows."""
+    Y, _ = O.rmsnorm(X, g)
+    Xq, xs, xsum, _ = O.quantize_activations(Y)
+    return Xq, xs, xsum
 
 
 RMS_SHAPES = [
@@ -67,7 +46,7 @@ def test_rmsnorm_quant(gpu_lib, M, K):
     g = _gain(K, f"test/rms/g{K}")
     q, s, t = gpu_lib.bitlinear_rmsnorm_quant(dev(X), dev(g))
     gq = host(q)
-    Xq, xs, xsum, amb = oracle_rms_quant(X, g, gq)
+    Xq, xs, xsum = oracle_rms_quant(X, g)
     assert_equal(gq, Xq, "X~")
     assert_equal(f32_bits(host(s)), f32_bits(xs), "x_scale")
     assert_equal(host(t).astype(np.int64), xsum, "x_sum")
@@ -85,7 +64,7 @@ def test_rmsnorm_quant_special_rows(gpu_lib):
     X[5] = _acts(1, K, "test/rms/plain")[0]
     g = _gain(K, "test/rms/gspecial")
     q, s, t = gpu_lib.bitlinear_rmsnorm_quant(dev(X), dev(g))
-    Xq, xs, xsum, _ = oracle_rms_quant(X, g, host(q))
+    Xq, xs, xsum = oracle_rms_quant(X, g)
     assert_equal(host(q), Xq, "X~")
     assert_equal(f32_bits(host(s)), f32_bits(xs), "x_scale")
     assert_equal(host(t).astype(np.int64), xsum, "x_sum")
@@ -117,18 +96,16 @@ def test_forward_rmsnorm(gpu_lib, M, N, K):
     acc = gpu_lib.bitlinear_forward_rmsnorm(P, gd, dev(X), dev(g), N=N, y_dtype="i32", **outs)
     torch.cuda.synchronize()
     gq = host(outs["X_q_out"])
-    Xq, xs, xsum, _ = oracle_rms_quant(X, g, gq)
+    Xq, xs, xsum = oracle_rms_quant(X, g)
     assert_equal(gq, Xq, "X~ out")
     assert_equal(f32_bits(host(outs["x_scale_out"])), f32_bits(xs), "x_scale out")
     assert_equal(host(outs["x_sum_out"]).astype(np.int64), xsum, "x_sum out")
     want = O.integer_matmul(Wt, Xq)
     assert_equal(host(acc).astype(np.int64), want, "accumulators")
-    # the fused launch and the standalone normalising quantiser sum in the same
-    # order: identical codes
+    # the fused launch and the standalone normalising quantiser give the same
+    # codes (both equal the oracle's)
     q2, s2, _ = gpu_lib.bitlinear_rmsnorm_quant(dev(X), dev(g))
     assert_equal(host(q2), gq, "standalone vs fused X~")
-    # the rescale uses the absmax of the normalised row (an admissible other
-    # rounding of the mean moves it by far less than the tolerance)
     _, _, _, beta = O.quantize_activations(O.rmsnorm(X, g)[0])
     for out in ("f32", "bf16"):
         Y = gpu_lib.bitlinear_forward_rmsnorm(P, gd, dev(X), dev(g), N=N, y_dtype=out)
@@ -154,7 +131,71 @@ def test_forward_rmsnorm_grouped(gpu_lib, M, K, Ns):
     accs = gpu_lib.bitlinear_forward_rmsnorm_grouped(Ps, gds, dev(X), dev(g), y_dtype="i32", **outs)
     torch.cuda.synchronize()
     gq = host(outs["X_q_out"])
-    Xq, _, _, _ = oracle_rms_quant(X, g, gq)
+    Xq, _, _ = oracle_rms_quant(X, g)
     assert_equal(gq, Xq, "X~ out")
     for i, (Wt, a) in enumerate(zip(Wts, accs)):
         assert_equal(host(a).astype(np.int64), O.integer_matmul(Wt, Xq), f"accumulators {i}")
+
+
+def _exactness_rows(K):
+    """Rows whose mean of squares needs the exact sum: a tie between two fp32
+    values (to even), the same tie broken by one value 2^60 times smaller
+    (below the first summation window, and below any fp64 sum's resolution),
+    values spread from subnormals to 2^40 (several windows), subnormals only,
+    and one value beside zeros at the bottom of the range."""
+    a = np.float32(1.0) + np.float32(2.0 ** -12)
+    rows = np.zeros((6, K), np.float32)
+    rows[0, : K // 2] = a
+    rows[1, : K // 2] = a
+    rows[1, K // 2 + 3] = np.float32(2.0 ** -60)
+    rng = np.random.default_rng(99)
+    e = rng.integers(-149, 41, K)
+    rows[2] = (np.where(rng.random(K) < 0.5, -1.0, 1.0) * rng.uniform(1, 2, K) * 2.0 ** e).astype(np.float32)
+    rows[3] = (rng.integers(-(1 << 23), 1 << 23, K) * 2.0 ** -149).astype(np.float32)
+    rows[4, 7] = np.float32(2.0 ** -149)
+    rows[5, : K // 2] = a
+    rows[5, K // 2:] = np.float32(2.0 ** -100) * rng.standard_normal(K // 2).astype(np.float32)
+    return rows
+
+
+@pytest.mark.parametrize("K", [64, 4096, 16384, 65536])
+def test_rmsnorm_exact_mean_rows(gpu_lib, K):
+    # Rows through the first summation window only, and rows that take the
+    # further windows (values more than 2^31 below the row's largest), in the
+    # register-resident and the looped kernels.
+    X = _exactness_rows(K)
+    g = _gain(K, f"test/rms/gexact{K}")
+    q, s, t = gpu_lib.bitlinear_rmsnorm_quant(dev(X), dev(g))
+    Xq, xs, xsum = oracle_rms_quant(X, g)
+    assert_equal(host(q), Xq, "X~")
+    assert_equal(f32_bits(host(s)), f32_bits(xs), "x_scale")
+    assert_equal(host(t).astype(np.int64), xsum, "x_sum")
+    ms = O.mean_square(X)
+    assert ms[0] != ms[1]          # the tail value decides the rounding
+
+
+@pytest.mark.parametrize("K", [64, 3200, 12288])
+def test_forward_rmsnorm_exact_mean_rows_fused(gpu_lib, K):
+    # the same rows through the single-token fused launch (one row at a time)
+    import torch
+    N = 48
+    W = make_weight(0, f"test/rmsx/W{N}x{K}", N, K, 0.02)
+    gamma = O.absmean_gamma(W)
+    Wt = O.ternarize(W, gamma)
+    P = dev(O.pack_codes(Wt))
+    gd = dev(np.array([gamma], np.float32))
+    g = _gain(K, f"test/rms/gexactf{K}")
+    X = _exactness_rows(K)
+    assert gpu_lib.forward_kernel("rmsnorm", 1, [N], K) == ("k_decode_dot", True)
+    for m in range(X.shape[0]):
+        xq = torch.empty((1, K), dtype=torch.int8, device="cuda")
+        xs = torch.empty(1, dtype=torch.float32, device="cuda")
+        xsum = torch.empty(1, dtype=torch.int32, device="cuda")
+        acc = gpu_lib.bitlinear_forward_rmsnorm(P, gd, dev(X[m:m + 1]), dev(g), N=N, y_dtype="i32",
+                                                X_q_out=xq, x_scale_out=xs, x_sum_out=xsum)
+        torch.cuda.synchronize()
+        Xq, s_, t_ = oracle_rms_quant(X[m:m + 1], g)
+        assert_equal(host(xq), Xq, f"X~ row {m}")
+        assert_equal(f32_bits(host(xs)), f32_bits(s_), f"x_scale row {m}")
+        assert_equal(host(xsum).astype(np.int64), t_, f"x_sum row {m}")
+        assert_equal(host(acc).astype(np.int64), O.integer_matmul(Wt, Xq), f"accumulators row {m}")

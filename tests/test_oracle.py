@@ -522,16 +522,94 @@ def test_rmsnorm_zero_row_and_quantiser_after_it():
     assert (np.abs(Xq[np.arange(3), idx]) == 127).all()
 
 
-def test_mean_square_candidates():
-    # A mean far from any rounding boundary has one candidate.  A row whose
-    # exact mean of squares is a midpoint between two fp32 values has both:
-    # (1 + 2^-12)^2 = 1 + 2^-11 + 2^-24, half way between 1 + 2^-11 and the
-    # next fp32 value up.
-    X = np.array([[1.0, -1.0, 1.0, 1.0]], np.float32)
-    assert O.mean_square_candidates(X, 2.0 ** -40) == [[np.float32(1.0)]]
-    row = np.array([[np.float32(1.0) + np.float32(2.0 ** -12)]], np.float32)
-    c = O.mean_square_candidates(row, 2.0 ** -40)
-    assert c == [[np.float32(1 + 2.0 ** -11), np.float32(1 + 2.0 ** -11 + 2.0 ** -23)]]
-    # a hair above the midpoint (mean of two squares), only the upper one
-    # survives a tolerance smaller than the distance
-    assert O.f32_nearest((1 + Fraction(1, 2 ** 12)) ** 2) == np.float32(1 + 2.0 ** -11)   # tie: even
+def test_mean_square_ties_round_to_even_and_tails_break_them():
+    # (1 + 2^-12)^2 = 1 + 2^-11 + 2^-24 lies half way between the fp32 values
+    # 1 + 2^-11 and 1 + 2^-11 + 2^-23: the tie goes to the even significand.
+    a = np.float32(1.0) + np.float32(2.0 ** -12)
+    assert O.mean_square(np.full((1, 16), a, np.float32))[0] == np.float32(1 + 2.0 ** -11)
+    # Half of the rows at a, half zero: the mean is a^2 / 2, again a tie
+    # (between 2^-1 + 2^-12 and the next value up) and rounds down to even.
+    # One value 2^-60 among the zeros adds 2^-120 / 32 to the mean, far below
+    # any fp64 sum's resolution at this magnitude, and must round it up.
+    row = np.zeros((2, 32), np.float32)
+    row[:, :16] = a
+    row[1, 20] = np.float32(2.0 ** -60)
+    ms = O.mean_square(row)
+    assert ms[0] == np.float32(0.5 + 2.0 ** -12)
+    assert ms[1] == np.float32(0.5 + 2.0 ** -12 + 2.0 ** -24)
+    x64 = row.astype(np.float64)
+    assert np.float32((x64 * x64).sum(1)[1] / 32) == ms[0]      # what an fp64 sum gives
+    # exact mean rounded once: brute force over Fractions on mixed rows
+    rng = np.random.default_rng(13)
+    X = (rng.standard_normal((4, 48)) * np.float32(2.0) ** rng.integers(-70, 40, (4, 48))).astype(np.float32)
+    for m in range(4):
+        want = O.f32_nearest(sum(Fraction(float(v)) ** 2 for v in X[m]) / 48)
+        assert O.mean_square(X[m:m + 1])[0] == want
+
+
+def _rn32_sqrt(a: np.float32) -> np.float32:
+    """Correctly rounded fp32 square root by exact comparison: c is the
+    nearest fp32 value to sqrt(a) exactly when a lies strictly between the
+    squares of the midpoints around c (no fp32 a is the square of a midpoint)."""
+    A = Fraction(float(a))
+    c = np.sqrt(np.float32(a))
+    for cand in (np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))):
+        lo = (Fraction(float(cand)) + Fraction(float(np.nextafter(cand, np.float32(0))))) / 2
+        hi = (Fraction(float(cand)) + Fraction(float(np.nextafter(cand, np.float32(np.inf))))) / 2
+        if lo * lo < A < hi * hi:
+            return np.float32(cand)
+    raise AssertionError("no fp32 square root candidate")
+
+
+def _brute_rms_quant(x, g):
+    """X~ of one row by exact rational arithmetic with one rounding to fp32
+    after each operation, in the order of the reading: ms = RN(sum x^2 / K),
+    d = RN(sqrt(RN(ms + eps))), r = RN(1 / d), y_k = RN(RN(x_k r) g_k), then
+    the absmax quantiser (beta = max |y|, inv = RN(127 / RN(beta + eps)),
+    x~ = floor(RN(y inv) + 1/2) clipped to +-127)."""
+    F = lambda v: Fraction(float(v))
+    R = O.f32_nearest
+    K = len(x)
+    ms = R(sum(F(v) ** 2 for v in x) / K)
+    d = _rn32_sqrt(R(F(ms) + F(O.EPS)))
+    r = R(1 / F(d))
+    y = [R(F(R(F(xv) * F(r))) * F(gv)) for xv, gv in zip(x, g)]
+    beta = max(abs(F(v)) for v in y)
+    inv = R(127 / F(R(beta + F(O.EPS))))
+    out = []
+    for v in y:
+        q = F(R(F(v) * F(inv)))
+        t = (q + Fraction(1, 2)).__floor__()
+        out.append(max(-127, min(127, t)))
+    return np.array(out, np.int8)
+
+
+def test_rmsnorm_operation_order_pinned_by_exact_arithmetic():
+    # The reading fixes the per-element order fl32(fl32(x r) g).  Two other
+    # plausible orders, fl32(fl32(x / d) g) and fl32(x fl32(r g)), round
+    # differently in the last bit now and then; on the rows found here that
+    # difference flips an element of X~.  The oracle must equal the exact
+    # brute force of the reading on those rows, and differ from both
+    # alternatives, so a change of its order fails this test.
+    rng = np.random.default_rng(2024)
+    K = 64
+    rows = {"div": None, "rg": None}
+    for _ in range(200):
+        X = rng.standard_normal((512, K)).astype(np.float32)
+        g = (1 + 0.3 * rng.standard_normal((1, K))).astype(np.float32)
+        d = np.sqrt(O.mean_square(X) + O.EPS)
+        r = np.float32(1) / d
+        qa = O.quantize_activations((X * r[:, None]) * g)[0]
+        for key, y in (("div", (X / d[:, None]) * g), ("rg", X * (r[:, None] * g))):
+            bad = np.nonzero((O.quantize_activations(y)[0] != qa).any(1))[0]
+            if rows[key] is None and len(bad):
+                rows[key] = (X[bad[0]].copy(), g[0].copy(), O.quantize_activations(y)[0][bad[0]])
+        if all(v is not None for v in rows.values()):
+            break
+    assert all(v is not None for v in rows.values()), "no order-sensitive row found"
+    for x, g, q_alt in rows.values():
+        want = _brute_rms_quant(x, g)
+        Y, _ = O.rmsnorm(x[None, :], g)
+        got = O.quantize_activations(Y)[0][0]
+        assert np.array_equal(got, want)
+        assert not np.array_equal(q_alt, want)
