@@ -219,6 +219,32 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bitlinear_forward_f32 for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same computation and results, byte for byte, as
+ * bitlinear_forward_f32 with the same arguments; the workspace is not the
+ * caller's but a fixed array of BITLINEAR_NOALLOC_SCRATCH_BYTES in device
+ * memory that the library holds on each GPU it runs on, reserved when its code
+ * loads on that device and kept until the process ends.  The call allocates
+ * and frees nothing.  The caller still owns X, Y and the optional quantiser
+ * outputs (as in bitlinear_forward_f32).
+ *
+ * Every call on one GPU shares that GPU's array: two calls that overlap in
+ * time on one GPU (different streams or host threads) race on it and give
+ * unspecified results; calls in order on one stream are safe.  Nothing in the
+ * array needs clearing between calls.
+ * Errors as bitlinear_forward_f32, and BITLINEAR_ERR_WORKSPACE (before any HIP
+ * call) when bitlinear_forward_f32_workspace_bytes(M, N, K) exceeds
+ * BITLINEAR_NOALLOC_SCRATCH_BYTES (long-K prefill shapes with many tokens).
+ */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+bitlinear_status bitlinear_forward_f32_noalloc(const uint8_t* W_packed, const float* gamma,
+                                               int64_t N, int64_t K, const float* X, int64_t M,
+                                               void* Y, bitlinear_dtype y_dtype, int8_t* X_q_out,
+                                               float* x_scale_out, int32_t* x_sum_out,
+                                               void* stream);
+
+/*
  * Several projections of one activation matrix in one call: the query, key
  * and value projections of an attention block, or the gate and up
  * projections of a feed-forward block, which all read the same X~.  For

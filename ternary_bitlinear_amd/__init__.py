@@ -10,11 +10,13 @@ from .binding import (  # noqa: F401
     SIGNATURES,
     STATUS,
     MAX_GROUP,
+    NOALLOC_SCRATCH_BYTES,
     BitLinearError,
     bitlinear_base3_to_blt2,
     bitlinear_forward,
     bitlinear_forward_base3,
     bitlinear_forward_f32,
+    bitlinear_forward_f32_noalloc,
     bitlinear_forward_f32_grouped,
     bitlinear_forward_grouped,
     bitlinear_forward_rmsnorm,

@@ -35,6 +35,8 @@ SIGNATURES = {
     "bitlinear_forward_f32_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "bitlinear_forward_f32": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, ctypes.c_int,
                                              _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bitlinear_forward_f32_noalloc": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp,
+                                                     ctypes.c_int, _vp, _vp, _vp, _vp]),
     "bitlinear_forward_grouped_workspace_bytes": (_c_size, [_c_i64, ctypes.c_int, _vp, _c_i64]),
     "bitlinear_forward_grouped": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp,
                                                  _c_i64, _vp, ctypes.c_int, _vp, _c_size, _vp]),
@@ -261,6 +263,35 @@ def bitlinear_forward_f32(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None, X_
     """Quantise fp32 X [M][K] and project in one call -> Y [M][N]."""
     return _forward_f32(W_packed, gamma, X, None, N, y_dtype, Y, X_q_out, x_scale_out,
                         x_sum_out, workspace, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # BITLINEAR_NOALLOC_SCRATCH_BYTES
+
+
+def bitlinear_forward_f32_noalloc(W_packed, gamma, X, N=None, y_dtype="bf16", Y=None,
+                                  X_q_out=None, x_scale_out=None, x_sum_out=None, stream=None):
+    """bitlinear_forward_f32 with the library's own scratch array as workspace (no
+    allocation inside the library; calls overlapping on one GPU race on it).
+    Y is allocated here when not given."""
+    import torch
+    lib = load()
+    _dev(W_packed, torch.uint8, "W_packed")
+    _dev(X, torch.float32, "X")
+    M, K = X.shape
+    N = W_packed.shape[0] if N is None else N
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[y_dtype]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=tdt, device=X.device)
+    _dev(Y, tdt, "Y")
+    if X_q_out is not None:
+        _dev(X_q_out, torch.int8, "X_q_out")
+        _dev(x_scale_out, torch.float32, "x_scale_out")
+        _dev(x_sum_out, torch.int32, "x_sum_out")
+    ptr = [o.data_ptr() if o is not None else None for o in (X_q_out, x_scale_out, x_sum_out)]
+    _check(lib.bitlinear_forward_f32_noalloc(W_packed.data_ptr(), gamma.data_ptr(), N, K,
+                                             X.data_ptr(), M, Y.data_ptr(), DTYPES[y_dtype],
+                                             ptr[0], ptr[1], ptr[2], _stream(stream)))
+    return Y
 
 
 def bitlinear_forward_rmsnorm(W_packed, gamma, X, norm_g, N=None, y_dtype="bf16", Y=None,

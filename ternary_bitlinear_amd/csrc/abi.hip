@@ -166,11 +166,13 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma, 
 namespace {
 // fp32 activations in: the quantiser (after an RMS normalisation with gain
 // norm_g when that is not null) and the projection.
+// noalloc: the workspace is the library's own scratch array (workspace and
+// workspace_bytes unused); the call is refused when it needs more.
 bitlinear_status forward_f32_impl(const char* who, const uint8_t* W_packed, const float* gamma,
                                   int64_t N, int64_t K, const float* X, const float* norm_g,
                                   int64_t M, void* Y, bitlinear_dtype y_dtype, int8_t* X_q_out,
                                   float* x_scale_out, int32_t* x_sum_out, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  size_t workspace_bytes, void* stream, bool noalloc = false) {
   if (!W_packed || !gamma || !X || !Y) return fail(BITLINEAR_ERR_NULL, "%s: NULL buffer", who);
   const int given = (X_q_out != nullptr) + (x_scale_out != nullptr) + (x_sum_out != nullptr);
   if (given != 0 && given != 3)
@@ -190,6 +192,21 @@ bitlinear_status forward_f32_impl(const char* who, const uint8_t* W_packed, cons
   // projection's own part (same layout: it follows the quantiser region).
   const bool norm = norm_g != nullptr;
   const bool proj_ws = M > 16 && bl::forward_workspace_bytes(M, N, K) > 0;
+  if (noalloc) {
+    // the scratch array takes the workspace's whole layout (quantiser region,
+    // then the projection's part) whether or not the outputs are given
+    const size_t need = bl::forward_f32_workspace_bytes(M, N, K, norm);
+    if (need > bl::noalloc_scratch_bytes())
+      return fail(BITLINEAR_ERR_WORKSPACE, "%s: M=%lld N=%lld K=%lld needs %zu bytes of scratch; "
+                  "the library's array holds %zu (call bitlinear_forward_f32 with a workspace)",
+                  who, (long long)M, (long long)N, (long long)K, need, bl::noalloc_scratch_bytes());
+    bitlinear_status s = check_device();
+    if (s != BITLINEAR_OK) return s;
+    return launched(bl::launch_forward_f32_noalloc(W_packed, gamma, N, K, X, M, Y, (int)y_dtype,
+                                                   X_q_out, x_scale_out, x_sum_out,
+                                                   reinterpret_cast<hipStream_t>(stream)),
+                    "forward launch");
+  }
   const size_t need = (given && !proj_ws) ? 0 : bl::forward_f32_workspace_bytes(M, N, K, norm);
   if (need && (!workspace || workspace_bytes < need))
     return fail(BITLINEAR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu", who,
@@ -221,6 +238,15 @@ bitlinear_status bitlinear_forward_f32(const uint8_t* W_packed, const float* gam
                                        size_t workspace_bytes, void* stream) {
   return forward_f32_impl("forward_f32", W_packed, gamma, N, K, X, nullptr, M, Y, y_dtype,
                           X_q_out, x_scale_out, x_sum_out, workspace, workspace_bytes, stream);
+}
+
+bitlinear_status bitlinear_forward_f32_noalloc(const uint8_t* W_packed, const float* gamma,
+                                               int64_t N, int64_t K, const float* X, int64_t M,
+                                               void* Y, bitlinear_dtype y_dtype, int8_t* X_q_out,
+                                               float* x_scale_out, int32_t* x_sum_out,
+                                               void* stream) {
+  return forward_f32_impl("forward_f32_noalloc", W_packed, gamma, N, K, X, nullptr, M, Y, y_dtype,
+                          X_q_out, x_scale_out, x_sum_out, nullptr, 0, stream, true);
 }
 
 // ---- RMS normalisation before the quantiser -------------------------------------

@@ -62,6 +62,16 @@ hipError_t launch_forward_f32(const uint8_t* W_packed, const float* gamma, int64
                               int y_dtype, int8_t* X_q_out, float* x_scale_out,
                               int32_t* x_sum_out, void* workspace, hipStream_t stream);
 
+// launch_forward_f32 (no normalisation) with the workspace taken from the
+// library's own device array (noalloc.hip): no allocation, no caller
+// workspace.  The caller checks forward_f32_workspace_bytes(M, N, K, false)
+// <= noalloc_scratch_bytes().
+size_t noalloc_scratch_bytes();
+hipError_t launch_forward_f32_noalloc(const uint8_t* W_packed, const float* gamma, int64_t N,
+                                      int64_t K, const float* X, int64_t M, void* Y, int y_dtype,
+                                      int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
+                                      hipStream_t stream);
+
 // Base-3 weights (BLT3-v1, five per byte; rows padded to 80 weights).
 // launch_pack3 computes gamma and the codes as launch_pack does (same
 // workspace); launch_forward_b3 takes 1 <= M <= kBase3MaxTokens tokens;
