@@ -14,8 +14,12 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbitlinear.so")
+# chip-limit probes for the bench (a plain read, an int8 matrix-instruction
+# loop); a library of their own, not part of the BitLinear ABI
+PROBES_LIB = os.path.join(PKG, "libbitlinear_probes.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 SOURCES = ["abi.hip", "pack.hip", "quant.hip", "forward.hip", "base3.hip", "noalloc.hip"]
+PROBE_SOURCES = ["probes.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: no multiply-add fusion anywhere (the quantisers' rounding
@@ -43,13 +47,18 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    objs = [os.path.join(OBJ_DIR, s.replace(".hip", ".o")) for s in srcs]
-    cmds = [[HIPCC, *FLAGS, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(srcs, objs)]
+    srcs = [s for s in SOURCES + PROBE_SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    objs = {s: os.path.join(OBJ_DIR, s.replace(".hip", ".o")) for s in srcs}
+    cmds = [[HIPCC, *FLAGS, "-c", "-o", objs[s], os.path.join(CSRC, s)] for s in srcs]
     with ThreadPoolExecutor(max_workers=jobs or min(len(cmds), os.cpu_count() or 1)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
+    probe_objs = [objs[s] for s in PROBE_SOURCES if s in objs]
+    if probe_objs:
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PROBES_LIB, *probe_objs],
+             verbose)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+          *[objs[s] for s in SOURCES if s in objs]], verbose)
     # A kernel the host pass rejects silently leaves its launch stub undefined;
     # a shared library links anyway and only fails at load time.  Refuse it.
     nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)

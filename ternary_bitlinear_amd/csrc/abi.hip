@@ -32,6 +32,22 @@ bitlinear_status fail(bitlinear_status s, const char* fmt, ...) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The int a C caller passed for an enum parameter.  Any int is a valid C
+// argument, but in C++ reading a value outside the enumerators' range through
+// the enum type is undefined, so validation reads the bytes as an int.
+template <typename E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enum passed as int");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool dtype_ok(const bitlinear_dtype& d) {
+  const int v = enum_value(d);
+  return v == BITLINEAR_F32 || v == BITLINEAR_BF16 || v == BITLINEAR_I32;
+}
+
 bool shape_ok_k(int64_t K) { return K >= 16 && K % 16 == 0 && K <= BITLINEAR_MAX_K; }
 constexpr int64_t kMaxDim = 0x7fffffff;
 
@@ -143,8 +159,8 @@ bitlinear_status bitlinear_forward(const uint8_t* W_packed, const float* gamma, 
   if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K))
     return fail(BITLINEAR_ERR_SHAPE, "forward: invalid shape M=%lld N=%lld K=%lld", (long long)M,
                 (long long)N, (long long)K);
-  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
-    return fail(BITLINEAR_ERR_DTYPE, "forward: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype))
+    return fail(BITLINEAR_ERR_DTYPE, "forward: unknown y_dtype %d", enum_value(y_dtype));
   const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
   if (!aligned(W_packed, 16) || !aligned(X_q, 16) || !aligned(gamma, 4) || !aligned(x_scale, 4) ||
       !aligned(x_sum, 4) || !aligned(Y, ya))
@@ -180,8 +196,8 @@ bitlinear_status forward_f32_impl(const char* who, const uint8_t* W_packed, cons
   if (M < 1 || M > kMaxDim || N < 1 || N > kMaxDim || !shape_ok_k(K))
     return fail(BITLINEAR_ERR_SHAPE, "%s: invalid shape M=%lld N=%lld K=%lld", who,
                 (long long)M, (long long)N, (long long)K);
-  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
-    return fail(BITLINEAR_ERR_DTYPE, "%s: unknown y_dtype %d", who, (int)y_dtype);
+  if (!dtype_ok(y_dtype))
+    return fail(BITLINEAR_ERR_DTYPE, "%s: unknown y_dtype %d", who, enum_value(y_dtype));
   const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
   if (!aligned(W_packed, 16) || !aligned(X, 16) || !aligned(gamma, 4) || !aligned(Y, ya) ||
       (norm_g && !aligned(norm_g, 16)) ||
@@ -296,8 +312,8 @@ bitlinear_status check_group(const char* who, int G, const uint8_t* const* W_pac
   if (M < 1 || M > kMaxDim || !shape_ok_k(K))
     return fail(BITLINEAR_ERR_SHAPE, "%s: invalid shape M=%lld K=%lld", who, (long long)M,
                 (long long)K);
-  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
-    return fail(BITLINEAR_ERR_DTYPE, "%s: unknown y_dtype %d", who, (int)y_dtype);
+  if (!dtype_ok(y_dtype))
+    return fail(BITLINEAR_ERR_DTYPE, "%s: unknown y_dtype %d", who, enum_value(y_dtype));
   const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
   for (int g = 0; g < G; ++g) {
     if (!W_packed[g] || !gamma[g] || !Y[g])
@@ -462,8 +478,8 @@ bitlinear_status bitlinear_forward_base3(const uint8_t* W_packed3, const float* 
   if (M < 1 || M > BITLINEAR_BASE3_MAX_M || N < 1 || N > kMaxDim || !shape_ok_k(K))
     return fail(BITLINEAR_ERR_SHAPE, "forward_base3: invalid shape M=%lld N=%lld K=%lld (need "
                 "1<=M<=%d)", (long long)M, (long long)N, (long long)K, BITLINEAR_BASE3_MAX_M);
-  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
-    return fail(BITLINEAR_ERR_DTYPE, "forward_base3: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype))
+    return fail(BITLINEAR_ERR_DTYPE, "forward_base3: unknown y_dtype %d", enum_value(y_dtype));
   const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
   if (!aligned(W_packed3, 16) || !aligned(X_q, 16) || !aligned(gamma, 4) ||
       !aligned(x_scale, 4) || !aligned(x_sum, 4) || !aligned(Y, ya))
@@ -506,7 +522,7 @@ int bitlinear_forward_kernel(int entry, int64_t M, int G, const int64_t* N, int6
 }
 
 const char* bitlinear_status_string(bitlinear_status s) {
-  switch (s) {
+  switch (enum_value(s)) {
     case BITLINEAR_OK: return "ok";
     case BITLINEAR_ERR_NULL: return "null pointer";
     case BITLINEAR_ERR_SHAPE: return "invalid shape";

@@ -1,0 +1,103 @@
+// Chip-limit probes for the bench (not part of the BitLinear ABI; built into
+// libbitlinear_probes.so and loaded only by bench.py): a plain streaming read
+// of a buffer, the floor any kernel that must read the same bytes can reach,
+// and a loop of int8 matrix instructions on register operands with the value
+// distributions of the projection (codes in {0, 1, 2}, quantised activations),
+// the ceiling of the matrix cores for those operands.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+// Grid-stride read of n16 16-byte pieces, UNROLL loads in flight per thread;
+// the XOR of everything read is stored only if it equals an unlikely value, so
+// the loads cannot be removed and nothing is written.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p, int64_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  uint32_t a = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) a ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = p[i];
+    a ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (a == 0x9e3779b9u) sink[0] = a;
+}
+
+// iters x 16 independent v_mfma_i32_32x32x32_i8 per wave (4 accumulator
+// sets), operands from registers: with `real` set, A holds codes in {0, 1, 2}
+// and B int8 values spread like quantised activations (a triangular spread,
+// |x| < 64); otherwise both are zero (the matrix cores draw less power on
+// constant operands).  The accumulators are stored only if their sum equals
+// an unlikely value.
+__global__ __launch_bounds__(256) void k_mfma_loop(int iters, int real, int32_t* __restrict__ sink) {
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t h = (blockIdx.x * 4 + wave) * 64 + lane;
+  auto next = [&]() {
+    h ^= h << 13; h ^= h >> 17; h ^= h << 5;
+    return h;
+  };
+  i32x4 a[4], b[4];
+  for (int s = 0; s < 4; ++s) {
+    for (int d = 0; d < 4; ++d) {
+      uint32_t ca = 0, xb = 0;
+      for (int byte = 0; byte < 4; ++byte) {
+        uint32_t r = next();
+        ca |= (r % 3u) << (8 * byte);
+        // a sum of two small uniforms: a triangular spread around 0
+        const int x = (int)((r >> 8) & 63u) - (int)((r >> 16) & 63u);
+        xb |= ((uint32_t)x & 0xffu) << (8 * byte);
+      }
+      a[s][d] = real ? (int32_t)ca : 0;
+      b[s][d] = real ? (int32_t)xb : 0;
+    }
+  }
+  i32x16 acc[4];
+  for (int s = 0; s < 4; ++s)
+    for (int e = 0; e < 16; ++e) acc[s][e] = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[(s + r) & 3], b[s], acc[s], 0, 0, 0);
+  }
+  int32_t t = 0;
+  for (int s = 0; s < 4; ++s)
+    for (int e = 0; e < 16; ++e) t += acc[s][e];
+  if (t == 0x7eadbeef) sink[0] = t;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Plain read of `bytes` (a multiple of 16, 16-byte aligned) at `p` with
+// `grid` workgroups of 256 threads.  Returns a hipError_t.
+int probe_stream_read(const void* p, size_t bytes, int grid, void* sink, void* stream) {
+  k_stream_read<4><<<dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const uint4*>(p), (int64_t)(bytes / 16), reinterpret_cast<uint32_t*>(sink));
+  return (int)hipGetLastError();
+}
+
+// int8 matrix-instruction loop: grid x 4 waves x iters x 16 instructions of
+// 2 * 32 * 32 * 32 operations each, on the projection's operand values (real
+// != 0) or on zeros.  Returns a hipError_t.
+int probe_mfma_loop(int iters, int real, int grid, void* sink, void* stream) {
+  k_mfma_loop<<<dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      iters, real, reinterpret_cast<int32_t*>(sink));
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

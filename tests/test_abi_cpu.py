@@ -305,3 +305,58 @@ def test_quant_bits_validation_without_gpu_calls(lib):
     assert lib.bitlinear_quant_acts_bits(FAKE, 2, 64, 16, FAKE, FAKE, FAKE, None) == 4
     assert lib.bitlinear_quant_acts_bits(None, 2, 64, 4, FAKE, FAKE, FAKE, None) == 1
     assert lib.bitlinear_quant_acts_bits(FAKE, 2, 40, 4, FAKE, FAKE, FAKE, None) == 2
+
+
+def _gpu_visible():
+    """True when a HIP device is visible (counting does not initialise it)."""
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a host without a GPU: the calls below pass "
+                                            "validation and would launch on placeholder pointers")
+def test_every_entry_point_reports_no_device(lib):
+    # Valid arguments (aligned placeholder addresses that are never touched):
+    # validation passes and the first HIP call finds no device, so every entry
+    # point returns BITLINEAR_ERR_NO_DEVICE (5) and sets a last-error message.
+    C = ctypes
+    P = C.c_void_p(1 << 20)                      # 16-byte aligned, never dereferenced
+    M, N, K = 2, 64, 128
+    arr = lambda vals, t=C.c_void_p: (t * len(vals))(*vals)
+    Ps, Ns = arr([P.value, P.value]), arr([N, N], C.c_int64)
+    NO_DEVICE = 5
+    calls = {
+        "pack_weights": lambda: lib.bitlinear_pack_weights(P, N, K, P, P, P, 1 << 20, None),
+        "pack_weights_base3": lambda: lib.bitlinear_pack_weights_base3(P, N, K, P, P, P, 1 << 20,
+                                                                       None),
+        "quant_acts": lambda: lib.bitlinear_quant_acts(P, M, K, P, P, P, None),
+        "quant_acts_bits": lambda: lib.bitlinear_quant_acts_bits(P, M, K, 4, P, P, P, None),
+        "rmsnorm_quant": lambda: lib.bitlinear_rmsnorm_quant(P, P, M, K, P, P, P, None),
+        "forward": lambda: lib.bitlinear_forward(P, P, N, K, P, P, P, M, P, 1, P, 1 << 20, None),
+        "forward_f32": lambda: lib.bitlinear_forward_f32(P, P, N, K, P, M, P, 1, None, None,
+                                                         None, P, 1 << 20, None),
+        "forward_f32_noalloc": lambda: lib.bitlinear_forward_f32_noalloc(P, P, N, K, P, M, P, 1,
+                                                                         None, None, None, None),
+        "forward_rmsnorm": lambda: lib.bitlinear_forward_rmsnorm(P, P, N, K, P, P, M, P, 1, None,
+                                                                 None, None, P, 1 << 20, None),
+        "forward_grouped": lambda: lib.bitlinear_forward_grouped(2, Ps, Ps, Ns, K, P, P, P, M, Ps,
+                                                                 1, P, 1 << 20, None),
+        "forward_f32_grouped": lambda: lib.bitlinear_forward_f32_grouped(
+            2, Ps, Ps, Ns, K, P, M, Ps, 1, None, None, None, P, 1 << 20, None),
+        "forward_rmsnorm_grouped": lambda: lib.bitlinear_forward_rmsnorm_grouped(
+            2, Ps, Ps, Ns, K, P, P, M, Ps, 1, None, None, None, P, 1 << 20, None),
+        "forward_base3": lambda: lib.bitlinear_forward_base3(P, P, N, K, P, P, P, M, P, 1, None),
+        "base3_to_blt2": lambda: lib.bitlinear_base3_to_blt2(P, N, K, P, None),
+    }
+    for name, call in calls.items():
+        assert call() == NO_DEVICE, name
+        assert b"device" in lib.bitlinear_last_error(), name
+    # every status-returning entry point of the header is covered
+    status_fns = {n for n in declared_functions()
+                  if n.startswith("bitlinear_") and n not in (
+                      "bitlinear_abi_version", "bitlinear_status_string", "bitlinear_last_error",
+                      "bitlinear_forward_kernel") and not n.endswith("_bytes")}
+    assert {"bitlinear_" + n for n in calls} == status_fns
