@@ -13,8 +13,15 @@ inference; that step is timed separately and reported under "rows", as are
 the standalone quantiser and the projection on pre-quantised activations.
 Packed weights are replicated into enough copies (>= 512 MB per projection)
 that successive steps read them from HBM rather than from the 256 MB
-Infinity Cache.  Steps are replayed from a HIP graph so that host launch
-overhead does not hide the device time.
+Infinity Cache.  The timed steps are one HIP graph of exactly K steps,
+uploaded before the timed region; W untimed steps run first, then (not
+counted as steps) at least 0.5 s of the same launches writing to scratch
+outputs, so that the GPU clocks have ramped up.
+
+The default workload is the 70B-shaped FFN (8192 -> 28672 and 28672 -> 8192):
+"value" is its single-token decode step (weight GB/s), and "prefill" holds
+the same two projections at 1024 tokens (int8 TOP/s), each with its own
+roofline and CPU-oracle baseline.
 
 Prints one JSON line: the whole-step throughput ("value"), the roofline of the
 dominant kernel, the CPU oracle timed on a bounded sample, and one entry per
@@ -41,19 +48,25 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 ROTATE_BYTES = 512 << 20     # weight copies rotated per step: beyond the 256 MB MALL
 OUT_BYTES = {"f32": 4, "bf16": 2}
+STEP_GRAPH_MAX = 4096        # steps captured in one graph (more: replays of a cycle)
+RAMP_SECONDS = 0.5           # clock ramp before the timed region (not counted as steps)
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps before the timed ones (default: at least 200 steps and "
-                         "0.5 s, so the GPU clocks have ramped up; the count is reported)")
-    ap.add_argument("--workload", default="decode-3b")
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before the timed ones; then, not counted as steps, "
+                         "at least 0.5 s of the same launches writing to scratch outputs")
+    ap.add_argument("--workload", default="ffn-70b")
     ap.add_argument("--tokens", type=int, default=None, help="M; default: the workload's first")
+    ap.add_argument("--prefill-tokens", type=int, default=None,
+                    help="M of the prefill object; default: the workload's token count above "
+                         "64, if any (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-step rows")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one plain copy of known size, then bitlinear_forward once per "
                          "projection and weight copy, and exit (for rocprofv3 --pmc runs)")
@@ -86,160 +99,235 @@ class Timer:
         return a.elapsed_time(b) * 1e-3   # seconds
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        traffic_from(args)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode)", file=sys.stderr)
-        sys.exit(2)
+def hip_runtime(torch):
+    """The HIP runtime torch loaded (its own bundled library, the same instance
+    the BitLinear library binds to), for hipGraphUpload."""
+    import ctypes
+    lib = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    hip = ctypes.CDLL(lib if os.path.exists(lib) else "libamdhip64.so")
+    hip.hipGraphUpload.restype = ctypes.c_int
+    hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    return hip
 
-    import numpy as np
-    import torch
 
-    import ternary_bitlinear_amd as tb
-    from synth import WORKLOADS
+def graph_upload(hip, g, stream):
+    """Upload an instantiated graph to the device ahead of its first replay."""
+    rc = hip.hipGraphUpload(g.raw_cuda_graph_exec(), stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({rc})")
 
-    wl = WORKLOADS[args.workload]
-    M = args.tokens or wl.tokens[0]
-    out = wl.out_dtype
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    tb.load()
-    stream = torch.cuda.Stream()
-    timer = Timer(torch, stream)
 
-    # ---------------- set-up: inputs resident in HBM, weights packed once
-    projs = []
-    for p in wl.projections:
-        W = wl.weight(p)
-        X = wl.acts(p, M)
-        Wd = torch.from_numpy(W).to(dev)
-        Wp, g = tb.bitlinear_pack_weights(Wd)
+class Ctx:
+    """Set-up shared by the decode and prefill measurements: device, stream,
+    timer, packed weights and their rotated copies."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import ternary_bitlinear_amd as tb
+        from synth import WORKLOADS
+        self.np, self.torch, self.tb = np, torch, tb
+        self.wl = WORKLOADS[args.workload]
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        tb.load()
+        self.stream = torch.cuda.Stream()
+        self.timer = Timer(torch, self.stream)
+        self.hip = hip_runtime(torch)
+        self.out = self.wl.out_dtype
+        self.grouped = self.wl.shared_input
+        self.weights = []
+        for p in self.wl.projections:
+            W = self.wl.weight(p)
+            Wd = torch.from_numpy(W).to(self.dev)
+            Wp, g = tb.bitlinear_pack_weights(Wd)
+            torch.cuda.synchronize()
+            self.weights.append(dict(p=p, W_host=W, Wd=Wd, Wp=Wp, g=g))
+        # every projection alone cycles through >= ROTATE_BYTES of copies
+        self.copies = max(1, math.ceil(ROTATE_BYTES / min(w["p"].N * w["p"].K // 4
+                                                          for w in self.weights)))
+        for w in self.weights:
+            w["Wc"] = [w["Wp"]] + [w["Wp"].clone() for _ in range(self.copies - 1)]
         torch.cuda.synchronize()
-        projs.append(dict(p=p, W_host=W, X_host=X, Wd=Wd, Wp=Wp, g=g,
-                          X=torch.from_numpy(X).to(dev),
-                          Xq=torch.empty((M, p.K), dtype=torch.int8, device=dev),
-                          s=torch.empty(M, dtype=torch.float32, device=dev),
-                          xs=torch.empty(M, dtype=torch.int32, device=dev),
-                          Y=torch.empty((M, p.N), dtype=getattr(torch, {"f32": "float32", "bf16": "bfloat16"}[out]),
-                                        device=dev)))
-    grouped = wl.shared_input
-    if grouped:
-        # every projection reads one X (and, after quantisation, one X~)
-        for q in projs[1:]:
-            for key in ("X", "Xq", "s", "xs"):
-                q[key] = projs[0][key]
-    wbytes_step = sum(q["p"].N * q["p"].K // 4 for q in projs)
-    # every projection alone cycles through >= ROTATE_BYTES of copies
-    copies = max(1, math.ceil(ROTATE_BYTES / min(q["p"].N * q["p"].K // 4 for q in projs)))
-    for q in projs:
-        q["Wc"] = [q["Wp"]] + [q["Wp"].clone() for _ in range(copies - 1)]
-    torch.cuda.synchronize()
 
-    for q in projs:
-        need = tb.forward_f32_workspace_bytes(M, q["p"].N, q["p"].K)
-        q["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-        q["fused"] = need == 0
-    Ns = [q["p"].N for q in projs]
-    g_need = tb.forward_f32_grouped_workspace_bytes(M, Ns, projs[0]["p"].K) if grouped else 0
-    ws_group = torch.empty(max(g_need, 16), dtype=torch.uint8, device=dev)
-
-    def step_separate(r):
-        # quantise + project; one launch when the shape fuses, else two
-        for q in projs:
-            tb.bitlinear_forward_f32(q["Wc"][r % copies], q["g"], q["X"], N=q["p"].N,
-                                     y_dtype=out, Y=q["Y"], workspace=q["ws"], stream=stream)
-
-    def step_grouped(r):
-        # quantise once, then every projection in one launch (decode shapes)
-        tb.bitlinear_forward_f32_grouped([q["Wc"][r % copies] for q in projs],
-                                         [q["g"] for q in projs], projs[0]["X"], Ns=Ns,
-                                         y_dtype=out, Y=[q["Y"] for q in projs],
-                                         workspace=ws_group, stream=stream)
-
-    step = step_grouped if grouped else step_separate
-    fused_step = step_is_fused(tb, [q["p"] for q in projs], M, grouped)
-
-    if args.traffic_probe:
-        traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped,
-                      step if fused_step else None, reps=args.probe_reps)
-        return
-
-    def graph_of(fn_list):
+    def graph_of(self, fn_list):
+        torch = self.torch
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            with torch.cuda.graph(g, stream=stream):
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(g, stream=self.stream):
                 for fn in fn_list:
                     fn()
         return g
 
-    # ---------------- warm-up: eager steps, then the step graph replayed (by
-    # default until 0.5 s have passed, so that the clocks have ramped up)
-    w_eager = min(args.warmup, 200) if args.warmup is not None else 200
+    def projections(self, M):
+        """Per-projection buffers for M tokens (activations resident in HBM)."""
+        torch, wl, dev = self.torch, self.wl, self.dev
+        ydt = {"f32": torch.float32, "bf16": torch.bfloat16}[self.out]
+        projs = []
+        for w in self.weights:
+            p = w["p"]
+            X = wl.acts(p, M)
+            q = dict(w)
+            q.update(X_host=X, X=torch.from_numpy(X).to(dev),
+                     Xq=torch.empty((M, p.K), dtype=torch.int8, device=dev),
+                     s=torch.empty(M, dtype=torch.float32, device=dev),
+                     xs=torch.empty(M, dtype=torch.int32, device=dev),
+                     Y=torch.empty((M, p.N), dtype=ydt, device=dev),
+                     Y_scratch=torch.empty((M, p.N), dtype=ydt, device=dev))
+            projs.append(q)
+        if self.grouped:
+            # every projection reads one X (and, after quantisation, one X~)
+            for q in projs[1:]:
+                for key in ("X", "X_host", "Xq", "s", "xs"):
+                    q[key] = projs[0][key]
+        for q in projs:
+            need = self.tb.forward_f32_workspace_bytes(M, q["p"].N, q["p"].K)
+            q["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            q["fused"] = need == 0
+        torch.cuda.synchronize()
+        return projs
+
+
+def make_step(ctx, projs, M, grouped):
+    """step(r, scratch=False): quantise + project every projection once, on
+    weight copy r (one launch per projection where the shape fuses, else two;
+    one launch for all of them where a grouped decode applies)."""
+    tb, out, stream = ctx.tb, ctx.out, ctx.stream
+    Ns = [q["p"].N for q in projs]
+    if grouped:
+        g_need = tb.forward_f32_grouped_workspace_bytes(M, Ns, projs[0]["p"].K)
+        ws_group = ctx.torch.empty(max(g_need, 16), dtype=ctx.torch.uint8, device=ctx.dev)
+
+        def step(r, scratch=False):
+            tb.bitlinear_forward_f32_grouped([q["Wc"][r % ctx.copies] for q in projs],
+                                             [q["g"] for q in projs], projs[0]["X"], Ns=Ns,
+                                             y_dtype=out,
+                                             Y=[q["Y_scratch" if scratch else "Y"] for q in projs],
+                                             workspace=ws_group, stream=stream)
+        return step
+
+    def step(r, scratch=False):
+        for q in projs:
+            tb.bitlinear_forward_f32(q["Wc"][r % ctx.copies], q["g"], q["X"], N=q["p"].N,
+                                     y_dtype=out, Y=q["Y_scratch" if scratch else "Y"],
+                                     workspace=q["ws"], stream=stream)
+    return step
+
+
+def time_steps(ctx, step, steps, warmup):
+    """W eager steps, then >= RAMP_SECONDS of the same launches on scratch
+    outputs (not steps), then exactly `steps` steps from one uploaded graph
+    (or, beyond STEP_GRAPH_MAX, replays of a cycle graph), timed with HIP
+    events on the launch stream.  Returns (seconds, warm-up details)."""
+    torch, stream = ctx.torch, ctx.stream
     with torch.cuda.stream(stream):
-        for r in range(w_eager):
+        for r in range(warmup):
             step(r)
     torch.cuda.synchronize()
-    cycle = min(copies, args.steps)
-    g_cycle = graph_of([lambda r=r: step(r) for r in range(cycle)])
-    rem = args.steps % cycle
-    g_rem = graph_of([lambda r=r: step(r) for r in range(rem)]) if rem else None
-    warmup = w_eager
-    t_w0 = time.perf_counter()
-    while True:
-        if args.warmup is not None:
-            if warmup >= args.warmup:
-                break
-            if args.warmup - warmup < cycle:      # exactly W: finish eagerly
-                with torch.cuda.stream(stream):
-                    for r in range(args.warmup - warmup):
-                        step(r)
-                warmup = args.warmup
-                break
-        elif time.perf_counter() - t_w0 >= 0.5:
-            break
-        g_cycle.replay()
-        warmup += cycle
+    cycle = min(ctx.copies, steps)
+    g_ramp = ctx.graph_of([lambda r=r: step(r, scratch=True) for r in range(cycle)])
+    if steps <= STEP_GRAPH_MAX:
+        g_steps = ctx.graph_of([lambda r=r: step(r) for r in range(steps)])
+        timed_graphs = [g_steps]
+    else:
+        g_cyc = ctx.graph_of([lambda r=r: step(r) for r in range(cycle)])
+        rem = steps % cycle
+        timed_graphs = [g_cyc] * (steps // cycle)
+        if rem:
+            timed_graphs.append(ctx.graph_of([lambda r=r: step(r) for r in range(rem)]))
+    for g in {id(g): g for g in timed_graphs}.values():
+        graph_upload(ctx.hip, g, stream)
+    graph_upload(ctx.hip, g_ramp, stream)
+    torch.cuda.synchronize()
+    ramp_replays = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < RAMP_SECONDS or ramp_replays < 3:
+        with torch.cuda.stream(stream):
+            for _ in range(8):
+                g_ramp.replay()
+        ramp_replays += 8
         torch.cuda.synchronize()
+    ramp_s = time.perf_counter() - t0
+    # The start event is queued behind one more batch of ramp replays, so the
+    # GPU is busy (not waiting on the host) when it and the first timed launch
+    # come up; the events bracket exactly the timed graphs.
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for _ in range(8):
+            g_ramp.replay()
+        a.record(stream)
+        for g in timed_graphs:
+            g.replay()
+        b.record(stream)
+    ramp_replays += 8
+    b.synchronize()
     torch.cuda.synchronize()
+    elapsed = a.elapsed_time(b) * 1e-3
+    info = {"warmup_steps": warmup, "clock_ramp_s": round(ramp_s, 3),
+            "clock_ramp_launch_sets": ramp_replays * cycle,
+            "timed_graphs": len(timed_graphs), "graphs_uploaded": True}
+    return elapsed, info
 
-    # ---------------- timed region: exactly K steps
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
 
-    def timed():
-        for _ in range(args.steps // cycle):
-            g_cycle.replay()
-        if g_rem is not None:
-            g_rem.replay()
-    elapsed = timer(timed)
-    t_wall = time.perf_counter() - t_wall0
-    ms_per_step = elapsed / args.steps * 1e3
-
+def measure(ctx, M, steps, warmup, args, rows=True, cpu_tokens=None):
+    """One JSON object for the workload at M tokens: the step throughput, the
+    roofline of the dominant kernel, optional rows and the CPU baseline."""
+    torch, tb, out, stream = ctx.torch, ctx.tb, ctx.out, ctx.stream
+    projs = ctx.projections(M)
+    grouped = ctx.grouped
+    step = make_step(ctx, projs, M, grouped)
+    fused_step = step_is_fused(tb, [q["p"] for q in projs], M, grouped)
+    elapsed, warm_info = time_steps(ctx, step, steps, warmup)
+    ms_per_step = elapsed / steps * 1e3
+    wbytes_step = sum(q["p"].N * q["p"].K // 4 for q in projs)
     prefill = M > 64
     if prefill:
         ops_step = sum(2 * M * q["p"].N * q["p"].K for q in projs)
-        value, unit = ops_step / (elapsed / args.steps) / 1e12, "TOP/s"
+        value, unit = ops_step / (elapsed / steps) / 1e12, "TOP/s"
     else:
-        value, unit = wbytes_step / (elapsed / args.steps) / 1e9, "GB/s"
+        value, unit = wbytes_step / (elapsed / steps) / 1e9, "GB/s"
 
-    # ---------------- the dominant kernel.  The projection on pre-quantised
-    # activations (bitlinear_forward) over every projection of the workload,
-    # back to back over the rotated weight copies; when the step is nothing but
-    # fused launches (decode shapes), the step's own launch is the dominant
-    # kernel and is timed the same way.
+    # the dominant kernel (see roofline)
     with torch.cuda.stream(stream):
         for q in projs:
             tb.bitlinear_quant_acts(q["X"], q["Xq"], q["s"], q["xs"], stream=stream)
-    proj_roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
-                            grouped)
+    proj_roof, _ = roofline(tb, torch, ctx.timer, ctx.graph_of, projs, M, out, ctx.copies,
+                            prefill, stream, grouped)
     roof = proj_roof
     if fused_step:
-        roof, _ = roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
-                           grouped, fused_step=step)
+        roof, _ = roofline(tb, torch, ctx.timer, ctx.graph_of, projs, M, out, ctx.copies,
+                           prefill, stream, grouped, fused_step=step)
+    res = {
+        "value": round(value, 3), "unit": unit, "tokens": M, "steps": steps,
+        "ms_per_step": round(ms_per_step, 6), "warmup": warmup, "timed_region": warm_info,
+        "projections": [f"{q['p'].K}->{q['p'].N}" for q in projs],
+        "roofline": roof,
+        # tokens through every projection of the step (one layer) per second
+        "tokens_per_s": round(M / (elapsed / steps), 1),
+    }
+    if rows:
+        res["rows"] = side_rows(ctx, projs, M, proj_roof, step, grouped)
+    if not args.no_cpu_baseline:
+        # the timed step once more, its outputs for the oracle leg to check
+        with torch.cuda.stream(stream):
+            step(0)
+        stream.synchronize()
+        y_gpu = [q["Y"].float().cpu().numpy() for q in projs]
+        res["cpu_baseline"] = cpu_baseline(projs, M, args.cpu_seconds, wbytes_step, prefill,
+                                           grouped, y_gpu, out, cpu_tokens)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def side_rows(ctx, projs, M, proj_roof, step, grouped):
+    """Every step of the path timed on its own, and two chip figures."""
+    np, torch, tb, out, stream, timer = ctx.np, ctx.torch, ctx.tb, ctx.out, ctx.stream, ctx.timer
+    graph_of, copies, wl, dev = ctx.graph_of, ctx.copies, ctx.wl, ctx.dev
+    prefill = M > 64
+    rows = {}
     dom = max(projs, key=lambda q: q["p"].N * q["p"].K)
     P = dom["p"]
 
@@ -252,8 +340,6 @@ def main():
     reps = max(1, (2000 if not prefill else 200) // copies)
     t_fwd = timer(g_fwd.replay, reps) / (reps * copies)
 
-    # ---------------- every step of the path, timed on its own
-    rows = {}
     q0 = projs[0]
     ws = torch.empty(tb.pack_workspace_bytes(q0["p"].N, q0["p"].K), dtype=torch.uint8, device=dev)
     Wp_tmp = torch.empty_like(q0["Wp"])
@@ -299,6 +385,7 @@ def main():
     rows["forward_f32_warm_cache"] = {"shape": f"M{M} {P.K}->{P.N}", "us": round(t_warm * 1e6, 3),
                                       "note": "one weight copy, cache-resident: not an HBM number"}
     del g_warm
+    rows.update(chip_rows(ctx, projs))
 
     # base-3 weights (1.6 bits per weight, up to 16 tokens): each projection
     # on the same quantised activations in both formats, back to back over
@@ -381,13 +468,18 @@ def main():
 
     if grouped:
         # the same step as one call per projection, for comparison
+        Ns = [q["p"].N for q in projs]
+        cycle = copies
+
+        def step_separate(r):
+            for q in projs:
+                tb.bitlinear_forward_f32(q["Wc"][r % copies], q["g"], q["X"], N=q["p"].N,
+                                         y_dtype=out, Y=q["Y"], workspace=q["ws"], stream=stream)
         g_sep = graph_of([lambda r=r: step_separate(r) for r in range(cycle)])
         g_sep.replay()
         t_sep = timer(g_sep.replay, max(1, 2000 // cycle)) / (max(1, 2000 // cycle) * cycle)
         rows["step_separate_calls"] = {"us": round(t_sep * 1e6, 3),
                                        "note": "one bitlinear_forward_f32 per projection"}
-        rows["step_grouped"] = {"us": round(ms_per_step * 1e3, 3),
-                                "note": "one bitlinear_forward_f32_grouped"}
         gn_need = tb.forward_rmsnorm_grouped_workspace_bytes(M, Ns, projs[0]["p"].K)
         gn_ws = torch.empty(max(gn_need, 16), dtype=torch.uint8, device=dev)
 
@@ -402,31 +494,154 @@ def main():
         rows["step_grouped_rmsnorm"] = {"us": round(t_gr * 1e6, 3), "fused": gn_need == 0,
                                         "note": "one bitlinear_forward_rmsnorm_grouped: RMS "
                                                 "normalisation, quantiser and every projection"}
+    return rows
 
-    # ---------------- CPU oracle on a bounded sample of the same step
-    cpu = None
-    if not args.no_cpu_baseline:
-        # the timed step once more, its outputs for the oracle leg to check
-        with torch.cuda.stream(stream):
-            step(0)
-        stream.synchronize()
-        y_gpu = [q["Y"].float().cpu().numpy() for q in projs]
-        cpu = cpu_baseline(projs, M, args.cpu_seconds, wbytes_step, prefill, grouped, y_gpu,
-                           out)
 
+def probes(torch):
+    """The chip-limit probe library (libbitlinear_probes.so, built beside the
+    BitLinear library), or None when it is not built."""
+    import ctypes
+    from ternary_bitlinear_amd.build import PROBES_LIB
+    if not os.path.exists(PROBES_LIB):
+        return None
+    lib = ctypes.CDLL(PROBES_LIB)
+    lib.probe_stream_read.restype = ctypes.c_int
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_mfma_loop.restype = ctypes.c_int
+    lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    return lib
+
+
+def chip_rows(ctx, projs):
+    """Figures of the chip that frame the decode numbers, measured here: a
+    plain streaming read of the same packed bytes (probe kernel, rotated
+    copies, graph replay), and the library's smallest launch (the quantiser on
+    one token of 16 values) back to back in a graph, a floor for any single
+    launch."""
+    torch, tb, stream, timer, copies = ctx.torch, ctx.tb, ctx.stream, ctx.timer, ctx.copies
+    rows = {}
+    pr = probes(torch)
+    dom = max(projs, key=lambda q: q["p"].N * q["p"].K)
+    nbytes = dom["p"].N * dom["p"].K // 4
+    if pr is not None:
+        sink = torch.zeros(16, dtype=torch.int32, device=ctx.dev)
+        cus = torch.cuda.get_device_properties(ctx.dev).multi_processor_count
+        best = None
+        for grid in (cus, 2 * cus, 3 * cus):
+            def rd(w, grid=grid):
+                rc = pr.probe_stream_read(w.data_ptr(), nbytes, grid, sink.data_ptr(),
+                                          stream.cuda_stream)
+                if rc:
+                    raise RuntimeError(f"probe_stream_read failed ({rc})")
+            g_read = ctx.graph_of([lambda w=w: rd(w) for w in dom["Wc"]])
+            g_read.replay()
+            reps = max(1, 400 // copies)
+            t = timer(g_read.replay, reps) / (reps * copies)
+            if best is None or t < best[0]:
+                best = (t, grid)
+            del g_read
+        t_read, grid = best
+        rows["plain_read"] = {"bytes": nbytes, "us": round(t_read * 1e6, 3),
+                              "GB/s": round(nbytes / t_read / 1e9, 1),
+                              "frac_of_hbm": round(nbytes / t_read / 1e9 / HBM_PEAK_GBS, 4),
+                              "grid": grid,
+                              "note": "probe_stream_read (16-byte loads, 4 in flight per thread, "
+                                      "best of 1-3 workgroups of 256 per CU) over the dominant "
+                                      "projection's packed bytes, rotated copies: the floor of a "
+                                      "kernel that reads the same bytes"}
+    x = torch.zeros((1, 16), dtype=torch.float32, device=ctx.dev)
+    xq = torch.empty((1, 16), dtype=torch.int8, device=ctx.dev)
+    s = torch.empty(1, dtype=torch.float32, device=ctx.dev)
+    xs = torch.empty(1, dtype=torch.int32, device=ctx.dev)
+    g_small = ctx.graph_of([lambda: tb.bitlinear_quant_acts(x, xq, s, xs, stream=stream)] * 200)
+    g_small.replay()
+    t_small = timer(g_small.replay, 10) / 2000
+    rows["launch_floor"] = {"us": round(t_small * 1e6, 3),
+                            "note": "bitlinear_quant_acts on one token of 16 values, 200 back to "
+                                    "back in a graph: the per-launch floor of a graph replay"}
+    return rows
+
+
+def mfma_ceiling(ctx):
+    """int8 matrix-instruction throughput of a register-only loop with the
+    projection's operand distributions (probe_mfma_loop), against the 5.0
+    POPS peak: the ceiling the prefill GEMM works under on this chip."""
+    torch = ctx.torch
+    pr = probes(torch)
+    if pr is None:
+        return None
+    sink = torch.zeros(16, dtype=torch.int32, device=ctx.dev)
+    cus = torch.cuda.get_device_properties(ctx.dev).multi_processor_count
+    grid, iters = 2 * cus, 2000
+    out = {"grid": grid,
+           "note": "probe_mfma_loop: v_mfma_i32_32x32x32_i8 on register operands, 2 workgroups "
+                   "of 4 waves per CU, 16 independent instructions per wave per iteration; "
+                   "'operands' = codes in {0,1,2} x activations spread like quantised values, "
+                   "'zeros' = all-zero operands (the matrix cores' draw, and with it the clock, "
+                   "depends on the operand values)"}
+    for key, real in (("operands", 1), ("zeros", 0)):
+        def run(real=real):
+            rc = pr.probe_mfma_loop(iters, real, grid, sink.data_ptr(), ctx.stream.cuda_stream)
+            if rc:
+                raise RuntimeError(f"probe_mfma_loop failed ({rc})")
+        run()
+        ctx.timer(run, 20)
+        t = ctx.timer(run, 20) / 20
+        ops = grid * 4 * iters * 16 * 2 * 32 * 32 * 32
+        tops = ops / t / 1e12
+        out[key] = {"us": round(t * 1e6, 2), "TOP/s": round(tops, 1),
+                    "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    return out
+
+
+def prefill_tokens(args, wl, M):
+    if args.prefill_tokens is not None:
+        return args.prefill_tokens
+    big = [m for m in wl.tokens if m > 64]
+    return big[0] if big and M <= 64 else 0
+
+
+def main():
+    args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    ctx = Ctx(args)
+    wl = ctx.wl
+    M = args.tokens or wl.tokens[0]
+    if args.traffic_probe:
+        projs = ctx.projections(M)
+        step = make_step(ctx, projs, M, ctx.grouped)
+        fused_step = step_is_fused(ctx.tb, [q["p"] for q in projs], M, ctx.grouped)
+        traffic_probe(ctx.tb, ctx.torch, projs, M, ctx.out, ctx.copies, ctx.stream, ctx.dev, wl,
+                      ctx.grouped, step if fused_step else None, reps=args.probe_reps)
+        return
+    res = measure(ctx, M, args.steps, args.warmup, args, rows=not args.no_rows)
     line = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": M,
-                   "projections": [f"{q['p'].K}->{q['p'].N}" for q in projs],
-                   "out": out, "weight_copies": copies, "seed": wl.seed, "graph": True},
-        "roofline": roof, "cpu_baseline": cpu, "rows": rows,
-        # tokens through every projection of the step (one layer) per second
-        "tokens_per_s": round(M / (elapsed / args.steps), 1),
-        "wall_s_timed": round(t_wall, 3),
+        "config": {"workload": wl.name, "tokens": M, "projections": res["projections"],
+                   "out": ctx.out, "weight_copies": ctx.copies, "seed": wl.seed, "graph": True},
+        "roofline": res["roofline"], "cpu_baseline": res["cpu_baseline"],
+        "timed_region": res["timed_region"], "tokens_per_s": res["tokens_per_s"],
     }
+    if "rows" in res:
+        line["rows"] = res["rows"]
+    pm = prefill_tokens(args, wl, M)
+    if pm:
+        # the same projections at prefill size: int8 TOP/s on the matrix cores
+        pre = measure(ctx, pm, min(args.steps, 200), min(args.warmup, 20), args, rows=False,
+                      cpu_tokens=16)
+        line["prefill"] = {"metric": "prefill int8 TOP/s", **pre}
+        line["prefill"]["mfma_ceiling"] = mfma_ceiling(ctx)
     print(json.dumps(line), flush=True)
 
 
@@ -748,25 +963,23 @@ def load_traffic(kernel, projs, M, out, fused=False):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(projs, M, seconds, wbytes_step, prefill, grouped, y_gpu, out):
+def cpu_baseline(projs, M, seconds, wbytes_step, prefill, grouped, y_gpu, out, tokens=None):
     """The oracle's per-step work (quantise, integer product, rescale) for every
-    projection, repeated on the host for about `seconds`; its last step's
-    outputs are compared element by element with the GPU step's (y_gpu):
-    |y - y_oracle| <= tol |y_oracle| (1e-5 fp32, 1e-2 bf16), and exactly 0
-    where the accumulator is 0."""
+    projection, on one host thread (its float64 BLAS pool limited to 1), repeated
+    for about `seconds`.  With `tokens`, each step covers only the first `tokens`
+    of the M tokens (a bounded sample of a prefill step); the rate is scaled
+    to the work actually done.  Its last step's outputs are compared element
+    by element with the GPU step's (y_gpu, the same rows): |y - y_oracle| <=
+    tol |y_oracle| (1e-5 fp32, 1e-2 bf16), and exactly 0 where the
+    accumulator is 0."""
     import numpy as np
     from oracle import bitlinear_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    from threadpoolctl import threadpool_limits
+    T = M if tokens is None else min(tokens, M)
     prep = []
     for q in projs:
         gamma = O.absmean_gamma(q["W_host"])
-        # a grouped step feeds every projection the first one's activations
-        X = projs[0]["X_host"] if grouped else q["X_host"]
-        prep.append((O.ternarize(q["W_host"], gamma), gamma, X))
+        prep.append((O.ternarize(q["W_host"], gamma), gamma, q["X_host"][:T]))
 
     def one_step():
         ys = []
@@ -774,38 +987,21 @@ def cpu_baseline(projs, M, seconds, wbytes_step, prefill, grouped, y_gpu, out):
             Xq, _, _, beta = O.quantize_activations(X)
             ys.append(O.rescale(O.integer_matmul(Wt, Xq), gamma, beta))
         return ys
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        ys = one_step()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or (n >= 1 and el * (n + 1) / n > 3 * seconds):
-            break
+    with threadpool_limits(limits=1):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            ys = one_step()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or (n >= 1 and el * (n + 1) / n > 3 * seconds):
+                break
     per = el / n
-    macs = sum(M * q["p"].N * q["p"].K for q in projs)
+    macs = sum(T * q["p"].N * q["p"].K for q in projs)
     if prefill:
         v, unit = 2 * macs / per / 1e12, "TOP/s"
     else:
         v, unit = wbytes_step / per / 1e9, "GB/s"
-    # the same step on one thread (decode shapes only: a prefill step takes
-    # tens of seconds there), for about a third of the time
-    single = None
-    if not prefill:
-        try:
-            from threadpoolctl import threadpool_limits
-            with threadpool_limits(limits=1):
-                n1, t1 = 0, time.perf_counter()
-                while True:
-                    one_step()
-                    n1 += 1
-                    e1 = time.perf_counter() - t1
-                    if e1 >= seconds / 3:
-                        break
-            single = {"value": round(wbytes_step / (e1 / n1) / 1e9, 6), "unit": "GB/s",
-                      "ms_per_step": round(e1 / n1 * 1e3, 3), "sample": f"{n1} steps ({e1:.1f} s)"}
-        except Exception:  # pragma: no cover
-            single = None
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -815,15 +1011,17 @@ def cpu_baseline(projs, M, seconds, wbytes_step, prefill, grouped, y_gpu, out):
     tol = {"f32": 1e-5, "bf16": 1e-2}[out]
     bad = 0
     for y, yg in zip(ys, y_gpu):
+        yg = yg[:T]
         zero = y == 0
         bad += int((yg[zero] != 0).sum())
         bad += int((np.abs(yg - y) > tol * np.abs(y))[~zero].sum())
-    return {"value": round(v, 6), "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{n} full steps of the same workload ({el:.1f} s)",
-            "ms_per_step": round(per * 1e3, 3),
-            "gmac_per_s": round(macs / per / 1e9, 3),
+    sample = (f"{n} full steps of the same workload ({el:.1f} s)" if T == M else
+              f"{n} steps over the first {T} of the {M} tokens of each projection ({el:.1f} s); "
+              f"rate scaled to those tokens")
+    return {"value": round(v, 6), "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
+            "ms_per_step": round(per * 1e3, 3), "gmac_per_s": round(macs / per / 1e9, 3),
+            "threads": "one (BLAS pool limited to 1 thread)",
             "cpu_model": cpu_model, "nproc": os.cpu_count(),
-            "single_core": single,
             "timed_outputs_checked": int(sum(y.size for y in ys)),
             "timed_outputs_mismatched": bad,
             "timed_outputs_tolerance": f"{tol:g} relative ({out}); exact 0 for a zero accumulator"}
