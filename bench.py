@@ -189,12 +189,31 @@ class Ctx:
         return projs
 
 
-def make_step(ctx, projs, M, grouped):
+def multi_step(tb, projs, M, grouped):
+    """True when the step's projections (separate inputs) run as one
+    bitlinear_forward_f32_multi launch (its kernel query says so)."""
+    if grouped or len(projs) < 2:
+        return False
+    return tb.forward_f32_multi_kernel(M, [q["p"].N for q in projs],
+                                       [q["p"].K for q in projs]) is not None
+
+
+def make_step(ctx, projs, M, grouped, separate=False):
     """step(r, scratch=False): quantise + project every projection once, on
-    weight copy r (one launch per projection where the shape fuses, else two;
-    one launch for all of them where a grouped decode applies)."""
+    weight copy r: one launch for all of them where the multi-projection call
+    (separate inputs) or a grouped decode (one shared input) applies, else one
+    launch per projection where the shape fuses, two where it does not
+    (`separate`: always one bitlinear_forward_f32 per projection)."""
     tb, out, stream = ctx.tb, ctx.out, ctx.stream
     Ns = [q["p"].N for q in projs]
+    if not separate and multi_step(tb, projs, M, grouped):
+        def step(r, scratch=False):
+            tb.bitlinear_forward_f32_multi([q["Wc"][r % ctx.copies] for q in projs],
+                                           [q["g"] for q in projs], [q["X"] for q in projs],
+                                           Ns=Ns, y_dtype=out,
+                                           Y=[q["Y_scratch" if scratch else "Y"] for q in projs],
+                                           stream=stream)
+        return step
     if grouped:
         g_need = tb.forward_f32_grouped_workspace_bytes(M, Ns, projs[0]["p"].K)
         ws_group = ctx.torch.empty(max(g_need, 16), dtype=ctx.torch.uint8, device=ctx.dev)
@@ -278,7 +297,8 @@ def measure(ctx, M, steps, warmup, args, rows=True, cpu_tokens=None):
     projs = ctx.projections(M)
     grouped = ctx.grouped
     step = make_step(ctx, projs, M, grouped)
-    fused_step = step_is_fused(tb, [q["p"] for q in projs], M, grouped)
+    multi = multi_step(tb, projs, M, grouped)
+    fused_step = multi or step_is_fused(tb, [q["p"] for q in projs], M, grouped)
     elapsed, warm_info = time_steps(ctx, step, steps, warmup)
     ms_per_step = elapsed / steps * 1e3
     wbytes_step = sum(q["p"].N * q["p"].K // 4 for q in projs)
@@ -298,7 +318,7 @@ def measure(ctx, M, steps, warmup, args, rows=True, cpu_tokens=None):
     roof = proj_roof
     if fused_step:
         roof, _ = roofline(tb, torch, ctx.timer, ctx.graph_of, projs, M, out, ctx.copies,
-                           prefill, stream, grouped, fused_step=step)
+                           prefill, stream, grouped, fused_step=step, multi=multi)
     res = {
         "value": round(value, 3), "unit": unit, "tokens": M, "steps": steps,
         "ms_per_step": round(ms_per_step, 6), "warmup": warmup, "timed_region": warm_info,
@@ -309,6 +329,18 @@ def measure(ctx, M, steps, warmup, args, rows=True, cpu_tokens=None):
     }
     if rows:
         res["rows"] = side_rows(ctx, projs, M, proj_roof, step, grouped)
+        if multi:
+            # the same step as one bitlinear_forward_f32 per projection
+            sep = make_step(ctx, projs, M, grouped, separate=True)
+            g_sep = ctx.graph_of([lambda r=r: sep(r) for r in range(ctx.copies)])
+            g_sep.replay()
+            reps = max(1, 2000 // ctx.copies)
+            t_sep = ctx.timer(g_sep.replay, reps) / (reps * ctx.copies)
+            res["rows"]["step_separate_calls"] = {
+                "us": round(t_sep * 1e6, 3),
+                "GB/s": round(wbytes_step / t_sep / 1e9, 1),
+                "note": "one bitlinear_forward_f32 per projection, one launch each (the step "
+                        "runs them as one bitlinear_forward_f32_multi launch)"}
     if not args.no_cpu_baseline:
         # the timed step once more, its outputs for the oracle leg to check
         with torch.cuda.stream(stream):
@@ -618,9 +650,11 @@ def main():
     if args.traffic_probe:
         projs = ctx.projections(M)
         step = make_step(ctx, projs, M, ctx.grouped)
-        fused_step = step_is_fused(ctx.tb, [q["p"] for q in projs], M, ctx.grouped)
+        multi = multi_step(ctx.tb, projs, M, ctx.grouped)
+        fused_step = multi or step_is_fused(ctx.tb, [q["p"] for q in projs], M, ctx.grouped)
         traffic_probe(ctx.tb, ctx.torch, projs, M, ctx.out, ctx.copies, ctx.stream, ctx.dev, wl,
-                      ctx.grouped, step if fused_step else None, reps=args.probe_reps)
+                      ctx.grouped, step if fused_step else None, reps=args.probe_reps,
+                      multi=multi)
         return
     res = measure(ctx, M, args.steps, args.warmup, args, rows=not args.no_rows)
     line = {
@@ -693,13 +727,16 @@ def vendor_int8_mm(tb, torch, timer, stream, q, M):
                     "calibration, not the path"}
 
 
-def launch_alg_bytes(shapes, M, out, fused, grouped):
+def launch_alg_bytes(shapes, M, out, fused, grouped, multi=False):
     """Algorithmic bytes per launch of the dominant kernel: one grouped launch
-    reads the shared activations once; separate launches are averaged."""
+    reads the shared activations once; one multi-projection launch reads every
+    projection's own activations; separate launches are averaged."""
     f = alg_bytes_f32 if fused else alg_bytes
     shared = 4 * M * shapes[0].K if fused else M * shapes[0].K + 8 * M
     if grouped:
         return sum(f(P, M, out) for P in shapes) - (len(shapes) - 1) * shared
+    if multi:
+        return sum(f(P, M, out) for P in shapes)
     return sum(f(P, M, out) for P in shapes) / len(shapes)
 
 
@@ -716,12 +753,14 @@ def step_is_fused(tb, shapes, M, grouped):
 # Kernel names as the library reports them (bitlinear_forward_kernel), and the
 # symbols they appear under in a profile.
 KERNEL_SYMBOLS = {"k_decode_dot": ("k_decode_dot",), "k_decode": ("k_decode_lds", "k_decode_reg"),
-                  "k_skinny": ("k_skinny",), "k_gemm": ("k_gemm",)}
+                  "k_skinny": ("k_skinny",), "k_gemm": ("k_gemm",), "k_stream": ("k_stream",)}
 
 
-def step_kernels(tb, shapes, M, grouped, fused):
+def step_kernels(tb, shapes, M, grouped, fused, multi=False):
     """The kernel(s) the step's projection launches run, '+'-joined when the
     projections of a step differ."""
+    if multi:
+        return "k_stream"
     entry = "f32" if fused else "forward"
     if grouped:
         names = {tb.forward_kernel(entry, M, [P.N for P in shapes], shapes[0].K)[0]}
@@ -736,7 +775,7 @@ def kernel_matches(kernels, name):
 
 
 def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream, grouped=False,
-             fused_step=None):
+             fused_step=None, multi=False):
     """Average launch of the dominant kernel, timed with HIP events on the
     launch stream around a graph of back-to-back launches over the rotated
     weight copies.  With fused_step (the step's own function, every launch of
@@ -762,7 +801,7 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
                                  N=q["p"].N, K=q["p"].K, y_dtype=out, Y=q["Y"], stream=stream)
     g = graph_of([lambda r=r: fwd_all(r) for r in range(copies)])
     g.replay()
-    per_replay = 1 if grouped else len(projs)
+    per_replay = 1 if grouped or multi else len(projs)
     launches_per_replay = copies * per_replay
     # the replays in ROOF_GROUPS timed groups; the median group's mean launch
     # is reported, with the spread of the group means
@@ -772,8 +811,8 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
     n_launch = ROOF_GROUPS * reps * launches_per_replay
     t_launch = per_group[ROOF_GROUPS // 2]
     shapes = [q["p"] for q in projs]
-    bytes_launch = launch_alg_bytes(shapes, M, out, fused, grouped)
-    ops_launch = sum(2 * M * P.N * P.K for P in shapes) / (1 if grouped else len(shapes))
+    bytes_launch = launch_alg_bytes(shapes, M, out, fused, grouped, multi)
+    ops_launch = sum(2 * M * P.N * P.K for P in shapes) / (1 if grouped or multi else len(shapes))
     if prefill:
         achieved = ops_launch / t_launch / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
@@ -782,8 +821,9 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
         achieved = bytes_launch / t_launch / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    api = ("bitlinear_forward_f32" if fused else "bitlinear_forward") + ("_grouped" if grouped else "")
-    kern = step_kernels(tb, shapes, M, grouped, fused)
+    api = ("bitlinear_forward_f32" if fused else "bitlinear_forward") + (
+        "_grouped" if grouped else "_multi" if multi else "")
+    kern = step_kernels(tb, shapes, M, grouped, fused, multi)
     roof.update({
         "traffic": load_traffic(kern, projs, M, out, fused),
         "kernel": kern, "entry_point": api,
@@ -792,10 +832,10 @@ def roofline(tb, torch, timer, graph_of, projs, M, out, copies, prefill, stream,
         "us_per_launch_min_max": [round(per_group[0] * 1e6, 3), round(per_group[-1] * 1e6, 3)],
         "algorithmic_bytes_per_launch": int(bytes_launch),
         "ops_per_launch": int(ops_launch),
-        "grouped": grouped, "fused_quantiser": fused,
+        "grouped": grouped, "multi": multi, "fused_quantiser": fused,
         "timing": f"HIP events on the launch stream around replays of a graph of back-to-back "
                   f"{api} launches ("
-                  + ("all projections in one, " if grouped else "every projection, ")
+                  + ("all projections in one, " if grouped or multi else "every projection, ")
                   + f"rotated weight copies), in {ROOF_GROUPS} timed groups: the median "
                   "group's mean launch"})
     return roof, t_launch
@@ -806,7 +846,7 @@ ROOF_GROUPS = 9              # timed groups of the roofline's graph replays
 
 
 def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=False,
-                  fused_step=None, reps=1):
+                  fused_step=None, reps=1, multi=False):
     """One elementwise copy of CAL_BYTES (torch.neg on int32: reads and writes
     CAL_BYTES), then the dominant kernel `reps` times per weight copy: the
     step's own fused launches when it has nothing else (fused_step), else
@@ -853,10 +893,11 @@ def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=Fal
                 launch(r)
     torch.cuda.synchronize()
     shapes = [q["p"] for q in projs]
-    kern = step_kernels(tb, shapes, M, grouped, fused_step is not None)
+    kern = step_kernels(tb, shapes, M, grouped, fused_step is not None, multi)
     print(json.dumps({"traffic_probe": traffic_key(kern, shapes, M, out, fused_step is not None),
                       "workload": wl.name, "calibration_bytes": CAL_BYTES,
-                      "launches": copies * reps * (1 if grouped else len(projs))}), flush=True)
+                      "launches": copies * reps * (1 if grouped or multi else len(projs))}),
+          flush=True)
 
 
 def _counters(d, name):
@@ -888,8 +929,10 @@ def traffic_from(args):
     shapes = list(wl.projections)
     import ternary_bitlinear_amd as tb   # size queries only: no GPU
     tb.load()
-    fused = step_is_fused(tb, shapes, M, wl.shared_input)
-    fam = step_kernels(tb, shapes, M, wl.shared_input, fused)
+    multi = (not wl.shared_input and len(shapes) > 1 and tb.forward_f32_multi_kernel(
+        M, [P.N for P in shapes], [P.K for P in shapes]) is not None)
+    fused = multi or step_is_fused(tb, shapes, M, wl.shared_input)
+    fam = step_kernels(tb, shapes, M, wl.shared_input, fused, multi)
     key = traffic_key(fam, shapes, M, wl.out_dtype, fused)
     out = {}
     for what, d, cname in (("fetch", args.traffic_from[0], "FETCH_SIZE"),
@@ -908,7 +951,7 @@ def traffic_from(args):
                      "kernel_kib_per_dispatch": round(kib, 2), "dispatches": len(ker),
                      "reduce_dispatches": len(red),
                      "bytes_per_launch": kib * 1024.0 * factor}
-    alg = launch_alg_bytes(shapes, M, wl.out_dtype, fused, wl.shared_input)
+    alg = launch_alg_bytes(shapes, M, wl.out_dtype, fused, wl.shared_input, multi)
     total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
     ent = {"bytes_per_launch": int(total), "algorithmic_bytes_per_launch": int(alg),
            "ratio_to_algorithmic": round(total / alg, 4),

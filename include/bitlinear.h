@@ -298,6 +298,41 @@ bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_pa
                                                size_t workspace_bytes, void* stream);
 
 /*
+ * Several projections, each with its own activations and its own K, in one
+ * call: the projections of a decode step that do not share an input (two
+ * feed-forward projections on separate inputs, the experts of a
+ * mixture-of-experts layer with their own tokens).  For g < G this computes
+ * exactly what bitlinear_forward_f32(W_packed[g], gamma[g], N[g], K[g], X[g],
+ * M, Y[g], y_dtype, ...) computes (page section 2, absmax activation
+ * quantiser and the linear transformation; same X~, accumulators and output
+ * bytes).  One token (M = 1) with every K[g] a multiple of 64 up to 32768
+ * runs as ONE launch that streams the weights of all G matrices (page section
+ * 4: decode time is the time to read the weights, so the projections share
+ * one pass instead of paying a launch each): each workgroup quantises its
+ * projection's X once and reads its share of the rows.  Other shapes run the
+ * projections one after another.
+ *
+ * G          1 .. BITLINEAR_MAX_GROUP.
+ * W_packed, gamma, N, K, X, Y   HOST arrays of G entries (read during the call,
+ *            not kept); the buffers are device memory laid out and aligned as
+ *            for bitlinear_forward_f32 (X[g] is [M][K[g]] fp32, 16-byte
+ *            aligned; W_packed[g] is [N[g]][K[g]/4] BLT2-v1 bytes).
+ * workspace  >= bitlinear_forward_f32_multi_workspace_bytes(M, G, N, K) bytes
+ *            (16-byte aligned), scratch after the call; may be NULL when that is
+ *            0 (it is 0 for the single launch, and for single-token calls that
+ *            fall back to one call per projection).
+ * bitlinear_forward_f32_multi_kernel tells which way a call runs.
+ */
+size_t bitlinear_forward_f32_multi_workspace_bytes(int64_t M, int G, const int64_t* N,
+                                                   const int64_t* K);
+bitlinear_status bitlinear_forward_f32_multi(int G, const uint8_t* const* W_packed,
+                                             const float* const* gamma, const int64_t* N,
+                                             const int64_t* K, const float* const* X, int64_t M,
+                                             void* const* Y, bitlinear_dtype y_dtype,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
+/*
  * RMS normalisation before the quantiser.  Page section 2 (activations are
  * normalised with RMSNorm before they are quantised to int8; the page cites
  * Zhang and Sennrich, "Root Mean Square Layer Normalization"):
@@ -421,6 +456,8 @@ typedef enum bitlinear_kernel {
   BITLINEAR_KERNEL_SKINNY = 3,     /* 2-64 tokens: activations and codes through an LDS ring
                                       (K split over workgroups on long-K shapes) */
   BITLINEAR_KERNEL_GEMM = 4,       /* tiled matrix product (K split over workgroups when tiles are few) */
+  BITLINEAR_KERNEL_STREAM = 5,     /* one token, several projections with their own activations
+                                      in one persistent launch (bitlinear_forward_f32_multi) */
   BITLINEAR_KERNEL_FUSED_QUANT = 16 /* or'ed in: the activation quantiser runs in the same launch */
 } bitlinear_kernel;
 
@@ -438,6 +475,17 @@ typedef enum bitlinear_kernel {
  * than 0, 1, 2).
  */
 int bitlinear_forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K);
+
+/*
+ * How a bitlinear_forward_f32_multi call with these sizes runs (host only, no
+ * GPU call): BITLINEAR_KERNEL_STREAM | BITLINEAR_KERNEL_FUSED_QUANT when all G
+ * projections run as one launch (one token, every K[g] a multiple of 64 up to
+ * 32768, and rows few enough per workgroup), 0 when they run one
+ * bitlinear_forward_f32 call after another (bitlinear_forward_kernel with
+ * entry 1 then names each call's kernel), -BITLINEAR_ERR_SHAPE for sizes the
+ * call would reject.
+ */
+int bitlinear_forward_f32_multi_kernel(int64_t M, int G, const int64_t* N, const int64_t* K);
 
 /* Static English name of a status. */
 const char* bitlinear_status_string(bitlinear_status s);

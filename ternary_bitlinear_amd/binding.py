@@ -37,6 +37,10 @@ SIGNATURES = {
                                              _vp, _vp, _vp, _vp, _c_size, _vp]),
     "bitlinear_forward_f32_noalloc": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp,
                                                      ctypes.c_int, _vp, _vp, _vp, _vp]),
+    "bitlinear_forward_f32_multi_workspace_bytes": (_c_size, [_c_i64, ctypes.c_int, _vp, _vp]),
+    "bitlinear_forward_f32_multi_kernel": (ctypes.c_int, [_c_i64, ctypes.c_int, _vp, _vp]),
+    "bitlinear_forward_f32_multi": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _c_i64,
+                                                   _vp, ctypes.c_int, _vp, _c_size, _vp]),
     "bitlinear_forward_grouped_workspace_bytes": (_c_size, [_c_i64, ctypes.c_int, _vp, _c_i64]),
     "bitlinear_forward_grouped": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp,
                                                  _c_i64, _vp, ctypes.c_int, _vp, _c_size, _vp]),
@@ -555,7 +559,7 @@ def forward_rmsnorm_grouped_workspace_bytes(M: int, Ns, K: int) -> int:
     return load().bitlinear_forward_rmsnorm_grouped_workspace_bytes(M, len(Ns), _i64_array(Ns), K)
 
 
-KERNELS = {1: "k_decode_dot", 2: "k_decode", 3: "k_skinny", 4: "k_gemm"}
+KERNELS = {1: "k_decode_dot", 2: "k_decode", 3: "k_skinny", 4: "k_gemm", 5: "k_stream"}
 ENTRIES = {"forward": 0, "f32": 1, "rmsnorm": 2}
 
 
@@ -602,3 +606,57 @@ def _forward_f32_grouped(W_packed, gamma, X, norm_g, Ns, y_dtype, Y, X_q_out, x_
                                                      ptr[1], ptr[2], ws_ptr, ws_bytes,
                                                      _stream(stream)))
     return Y
+
+
+def forward_f32_multi_workspace_bytes(M: int, Ns, Ks) -> int:
+    return load().bitlinear_forward_f32_multi_workspace_bytes(M, len(Ns), _i64_array(Ns),
+                                                             _i64_array(Ks))
+
+
+def bitlinear_forward_f32_multi(W_packed, gamma, X, Ns=None, y_dtype="bf16", Y=None,
+                                workspace=None, stream=None):
+    """Several projections, each with its own fp32 activations X[g] [M][K_g] and
+    packed weights W_packed[g] [N_g][K_g/4]: quantise and project every one ->
+    list of Y [M][N_g] (one launch for a single token)."""
+    import torch
+    lib = load()
+    G = len(W_packed)
+    if not 1 <= G <= MAX_GROUP:
+        raise ValueError(f"1 to {MAX_GROUP} projections per call, got {G}")
+    if len(gamma) != G or len(X) != G:
+        raise ValueError("one gamma and one X per projection")
+    shapes = [_acts_f32(x) for x in X]
+    Ms = {m for m, _ in shapes}
+    if len(Ms) != 1:
+        raise ValueError(f"every X must have the same number of tokens, got {sorted(Ms)}")
+    M = shapes[0][0]
+    Ks = [k for _, k in shapes]
+    for i, w in enumerate(W_packed):
+        _t(w, torch.uint8, f"W_packed[{i}]")
+    Ns = [w.shape[0] for w in W_packed] if Ns is None else list(Ns)
+    if len(Ns) != G:
+        raise ValueError("one N per projection")
+    for i, (w, g, n, k) in enumerate(zip(W_packed, gamma, Ns, Ks)):
+        _t(w, torch.uint8, f"W_packed[{i}]", numel=n * (k // 4))
+        _t(g, torch.float32, f"gamma[{i}]", numel=1)
+    Y = _outputs(Ns, M, y_dtype, X[0].device, Y)
+    n_arr, k_arr = _i64_array(Ns), _i64_array(Ks)
+    need = lib.bitlinear_forward_f32_multi_workspace_bytes(M, G, n_arr, k_arr)
+    workspace = _ws(need, workspace, X[0].device)
+    _on_device(("workspace", workspace), *[(f"X[{i}]", x) for i, x in enumerate(X)],
+               *_group_named(W_packed, gamma, Y))
+    _check(lib.bitlinear_forward_f32_multi(G, _ptr_array(W_packed), _ptr_array(gamma), n_arr,
+                                           k_arr, _ptr_array(X), M, _ptr_array(Y),
+                                           DTYPES[y_dtype], *_ws_args(workspace),
+                                           _stream(stream)))
+    return Y
+
+
+def forward_f32_multi_kernel(M: int, Ns, Ks):
+    """("k_stream", True) when bitlinear_forward_f32_multi runs these sizes as
+    one launch, None when it runs one bitlinear_forward_f32 per projection."""
+    r = load().bitlinear_forward_f32_multi_kernel(M, len(Ns), _i64_array(Ns), _i64_array(Ks))
+    if r < 0:
+        raise BitLinearError(-r, f"forward_f32_multi_kernel: invalid sizes M={M} Ns={list(Ns)} "
+                                 f"Ks={list(Ks)}")
+    return (KERNELS[r & 15], bool(r & 16)) if r else None

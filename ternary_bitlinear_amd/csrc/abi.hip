@@ -441,6 +441,69 @@ bitlinear_status bitlinear_forward_rmsnorm_grouped(int G, const uint8_t* const* 
                                   workspace_bytes, stream);
 }
 
+// ---- several projections with their own activations ----------------------------
+
+namespace {
+bool multi_shapes_ok(int64_t M, int G, const int64_t* N, const int64_t* K) {
+  if (G < 1 || G > BITLINEAR_MAX_GROUP || !N || !K || M < 1 || M > kMaxDim) return false;
+  for (int g = 0; g < G; ++g)
+    if (N[g] < 1 || N[g] > kMaxDim || !shape_ok_k(K[g])) return false;
+  return true;
+}
+}  // namespace
+
+int bitlinear_forward_f32_multi_kernel(int64_t M, int G, const int64_t* N, const int64_t* K) {
+  if (!multi_shapes_ok(M, G, N, K)) return -BITLINEAR_ERR_SHAPE;
+  static_assert(BITLINEAR_KERNEL_STREAM == bl::kKernelStream, "kernel ids");
+  return bl::stream_multi_ok(M, G, N, K) ? (BITLINEAR_KERNEL_STREAM | BITLINEAR_KERNEL_FUSED_QUANT)
+                                         : 0;
+}
+
+size_t bitlinear_forward_f32_multi_workspace_bytes(int64_t M, int G, const int64_t* N,
+                                                   const int64_t* K) {
+  if (!multi_shapes_ok(M, G, N, K)) return 0;
+  return bl::forward_f32_multi_workspace_bytes(M, G, N, K);
+}
+
+bitlinear_status bitlinear_forward_f32_multi(int G, const uint8_t* const* W_packed,
+                                             const float* const* gamma, const int64_t* N,
+                                             const int64_t* K, const float* const* X, int64_t M,
+                                             void* const* Y, bitlinear_dtype y_dtype,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (G < 1 || G > BITLINEAR_MAX_GROUP)
+    return fail(BITLINEAR_ERR_SHAPE, "forward_f32_multi: G=%d outside 1..%d", G,
+                BITLINEAR_MAX_GROUP);
+  if (!W_packed || !gamma || !N || !K || !X || !Y)
+    return fail(BITLINEAR_ERR_NULL, "forward_f32_multi: NULL array");
+  if (!multi_shapes_ok(M, G, N, K))
+    return fail(BITLINEAR_ERR_SHAPE, "forward_f32_multi: invalid shape (M=%lld; every N >= 1, "
+                "K %% 16 == 0, 16 <= K <= %d)", (long long)M, BITLINEAR_MAX_K);
+  if (!dtype_ok(y_dtype))
+    return fail(BITLINEAR_ERR_DTYPE, "forward_f32_multi: unknown y_dtype %d", enum_value(y_dtype));
+  const uintptr_t ya = y_dtype == BITLINEAR_BF16 ? 2 : 4;
+  for (int g = 0; g < G; ++g) {
+    if (!W_packed[g] || !gamma[g] || !X[g] || !Y[g])
+      return fail(BITLINEAR_ERR_NULL, "forward_f32_multi: NULL buffer of projection %d", g);
+    if (!aligned(W_packed[g], 16) || !aligned(X[g], 16) || !aligned(gamma[g], 4) ||
+        !aligned(Y[g], ya))
+      return fail(BITLINEAR_ERR_ALIGN, "forward_f32_multi: projection %d: W_packed and X need "
+                  "16-byte alignment, Y its element size", g);
+  }
+  const size_t need = bl::forward_f32_multi_workspace_bytes(M, G, N, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "forward_f32_multi: workspace of %zu bytes needed, got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned(workspace, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "forward_f32_multi: workspace alignment");
+  bitlinear_status s = check_device();
+  if (s != BITLINEAR_OK) return s;
+  return launched(bl::launch_forward_f32_multi(G, W_packed, gamma, N, K, X, M, Y, (int)y_dtype,
+                                               need ? workspace : nullptr,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                  "forward_f32_multi launch");
+}
+
 size_t bitlinear_packed3_bytes(int64_t N, int64_t K) {
   if (N < 1 || N > kMaxDim || !shape_ok_k(K)) return 0;
   return (size_t)N * bl::packed3_row_bytes(K);

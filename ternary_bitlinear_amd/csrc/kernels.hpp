@@ -72,6 +72,17 @@ hipError_t launch_forward_f32_noalloc(const uint8_t* W_packed, const float* gamm
                                       int8_t* X_q_out, float* x_scale_out, int32_t* x_sum_out,
                                       hipStream_t stream);
 
+// Several projections with their own activations and K (G <= 4; all arrays
+// on the host): one persistent launch for a single token (stream_multi_ok),
+// else one launch_forward_f32 per projection (the workspace reused in stream
+// order).
+bool stream_multi_ok(int64_t M, int G, const int64_t* N, const int64_t* K);
+size_t forward_f32_multi_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K);
+hipError_t launch_forward_f32_multi(int G, const uint8_t* const* W_packed,
+                                   const float* const* gamma, const int64_t* N, const int64_t* K,
+                                   const float* const* X, int64_t M, void* const* Y, int y_dtype,
+                                   void* workspace, hipStream_t stream);
+
 // Base-3 weights (BLT3-v1, five per byte; rows padded to 80 weights).
 // launch_pack3 computes gamma and the codes as launch_pack does (same
 // workspace); launch_forward_b3 takes 1 <= M <= kBase3MaxTokens tokens;
@@ -89,7 +100,8 @@ hipError_t launch_b3_to_b2(const uint8_t* W_packed3, int64_t N, int64_t K, uint8
 // The kernel a forward call launches for these sizes (host only): entry 0
 // for the pre-quantised projection, 1 for the fp32 one, 2 with the RMS
 // normalisation; kKernel* or'ed with 16 when the quantiser runs inside it.
-constexpr int kKernelDecodeDot = 1, kKernelDecode = 2, kKernelSkinny = 3, kKernelGemm = 4;
+constexpr int kKernelDecodeDot = 1, kKernelDecode = 2, kKernelSkinny = 3, kKernelGemm = 4,
+              kKernelStream = 5;
 int forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K);
 
 }  // namespace bl

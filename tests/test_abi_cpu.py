@@ -348,6 +348,8 @@ def test_every_entry_point_reports_no_device(lib):
             2, Ps, Ps, Ns, K, P, M, Ps, 1, None, None, None, P, 1 << 20, None),
         "forward_rmsnorm_grouped": lambda: lib.bitlinear_forward_rmsnorm_grouped(
             2, Ps, Ps, Ns, K, P, P, M, Ps, 1, None, None, None, P, 1 << 20, None),
+        "forward_f32_multi": lambda: lib.bitlinear_forward_f32_multi(
+            2, Ps, Ps, Ns, arr([K, 2 * K], C.c_int64), Ps, M, Ps, 1, P, 1 << 20, None),
         "forward_base3": lambda: lib.bitlinear_forward_base3(P, P, N, K, P, P, P, M, P, 1, None),
         "base3_to_blt2": lambda: lib.bitlinear_base3_to_blt2(P, N, K, P, None),
     }
@@ -358,5 +360,24 @@ def test_every_entry_point_reports_no_device(lib):
     status_fns = {n for n in declared_functions()
                   if n.startswith("bitlinear_") and n not in (
                       "bitlinear_abi_version", "bitlinear_status_string", "bitlinear_last_error",
-                      "bitlinear_forward_kernel") and not n.endswith("_bytes")}
+                      "bitlinear_forward_kernel", "bitlinear_forward_f32_multi_kernel")
+                  and not n.endswith("_bytes")}
     assert {"bitlinear_" + n for n in calls} == status_fns
+
+
+def test_multi_kernel_query(lib):
+    # one launch exactly for one token with every K a multiple of 64 up to
+    # 32768; else one call per projection (0); invalid sizes are refused
+    C = ctypes
+    q = lambda M, Ns, Ks: lib.bitlinear_forward_f32_multi_kernel(
+        M, len(Ns), (C.c_int64 * len(Ns))(*Ns), (C.c_int64 * len(Ks))(*Ks))
+    STREAM_FUSED = 5 | 16
+    assert q(1, [28672, 8192], [8192, 28672]) == STREAM_FUSED
+    assert q(1, [8640, 3200], [3200, 8640]) == STREAM_FUSED
+    assert q(1, [1, 7], [64, 32768]) == STREAM_FUSED
+    assert q(1, [100], [1040]) == 0          # K % 64 != 0
+    assert q(1, [100], [32768 + 64]) == 0    # K beyond the kernel's LDS row
+    assert q(2, [100, 200], [512, 512]) == 0  # two tokens
+    assert q(1, [100] * 5, [512] * 5) == -2   # G > 4
+    assert q(1, [0], [512]) == -2
+    assert q(1, [100], [40]) == -2            # K % 16 != 0

@@ -39,3 +39,13 @@ def test_fused_and_grouped_counting():
     ffn = list(WORKLOADS["decode-3b"].projections)
     want = sum(bench.alg_bytes_f32(Q, 1, "bf16") for Q in ffn) / 2
     assert bench.launch_alg_bytes(ffn, 1, "bf16", True, False) == want
+
+
+def test_multi_launch_bytes_ffn70b():
+    # one multi-projection launch over both 70B projections, each with its own
+    # fp32 activations (one token, bf16 out), worked by hand:
+    #   8192 -> 28672: 58 720 256 packed + 32 768 X + 57 344 Y + 4 gamma = 58 810 372
+    #   28672 -> 8192: 58 720 256 packed + 114 688 X + 16 384 Y + 4 gamma = 58 851 332
+    from synth import WORKLOADS
+    shapes = list(WORKLOADS["ffn-70b"].projections)
+    assert bench.launch_alg_bytes(shapes, 1, "bf16", True, False, multi=True) == 117_661_704
