@@ -987,7 +987,7 @@ def forward_source_digest():
     """Digest of the sources the projection kernels are compiled from."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("forward.hip", "common.hpp"):
+    for name in ("forward.hip", "common.hpp", "stream.hpp"):
         h.update(open(os.path.join(ROOT, "ternary_bitlinear_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
