@@ -1,7 +1,7 @@
 """GPU parity of the K-split skinny projection (one projection, 17-64 tokens,
 K >= 2 N, M K > 256 Ki): each split writes exact int32 partial sums and a
 second launch adds them and applies the rescale.  Accumulators exact against
-the oracle (sampled rows for the largest shape), Y within tolerance, and an
+the oracle in full, Y within tolerance, and an
 unaligned Y (scalar stores in the reduction) byte-identical to an aligned one.
 """
 import numpy as np
@@ -41,10 +41,7 @@ def test_split_int32_handbuilt(gpu_lib, M, N, K):
                                     dev(Xq), dev(np.ones(M, np.float32)), dev(xsum), N=N, K=K,
                                     y_dtype="i32")
     torch.cuda.synchronize()
-    rows = np.arange(N) if N * K <= (1 << 26) else np.unique(np.concatenate(
-        [np.arange(32), N - 1 - np.arange(32), rng.integers(0, N, 64)]))
-    assert_equal(host(acc)[:, rows].astype(np.int64), O.integer_matmul(Wt[rows], Xq),
-                 "int32 accumulators")
+    assert_equal(host(acc).astype(np.int64), O.integer_matmul(Wt, Xq), "int32 accumulators")
 
 
 def test_split_extreme_accumulators(gpu_lib):
