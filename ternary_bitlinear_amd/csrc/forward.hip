@@ -1771,9 +1771,14 @@ hipError_t launch_gemm_t(GemmArgs ga, hipStream_t stream) {
 inline GemmCfg gemm_cfg(int M, int N, int K) {
   GemmCfg c{128, 128, 1};
   if (M <= 128) c = {64, 64, 1};
-  // 1024+ tokens with K <= 8192: 128 x 256 tiles at two waves per SIMD, 40 %
-  // fewer LDS bytes per matrix instruction; timed 3-6 % faster on prefill-7b
-  // (2048 x 11008 x 4096) and 1024 x 28672 x 8192, slower at K = 28672.
+  // 1024+ tokens with K <= 8192: 128 x 256 tiles at two waves per SIMD, the
+  // four waves side by side along N (a 128 x 64 sub-tile each, so every
+  // expanded code word feeds four matrix instructions).  Timed on MI355X
+  // (bench operands, same process): prefill-7b (2048 x 11008 x 4096) 92.1
+  // against 92.9 us with 2 x 2 waves, and 3-6 % faster than 128 x 128.  At
+  // K = 28672 (8192 outputs) the 256 tiles leave half the CUs' second
+  // workgroup slots idle and 128 x 128 stays ahead (215 against 218 us on
+  // the ffn-70b pair).
   else if (M >= 1024 && K <= 8192) c = {128, 256, 1};
   const int tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
   const int nk = K / kGBK;
@@ -1792,7 +1797,7 @@ hipError_t launch_gemm(const GemmCfg& c, GemmArgs ga, hipStream_t stream) {
   ga.splits = c.splits;
   if (c.bm == 128 && c.bn == 128) return launch_gemm_t<A64, OUT, 128, 128, 2, 2, 3>(ga, stream);
   if (c.bm == 128 && c.bn == 256)
-    return launch_gemm_t<A64, OUT, 128, 256, 2, 2, 3, false, 2>(ga, stream);
+    return launch_gemm_t<A64, OUT, 128, 256, 1, 4, 3, false, 2>(ga, stream);
   // 64 x 64 tiles run one workgroup per CU (a single wave per SIMD), so the
   // fragment reads are pipelined a step ahead there (timed 5-7 % faster);
   // at 128 x 128 two workgroups per CU already hide them.
