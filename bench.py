@@ -628,6 +628,17 @@ def mfma_ceiling(ctx):
     return out
 
 
+def prefill_vendor_row(ctx, M):
+    """vendor_int8_mm on the prefill object's first projection (its
+    activations quantised by the library first), for context beside the
+    GEMM's own fraction."""
+    q = ctx.projections(M)[0]
+    ctx.tb.bitlinear_quant_acts(q["X"], X_q=q["Xq"], x_scale=q["s"], x_sum=q["xs"],
+                                stream=ctx.stream)
+    ctx.stream.synchronize()
+    return vendor_int8_mm(ctx.tb, ctx.torch, ctx.timer, ctx.stream, q, M)
+
+
 def prefill_tokens(args, wl, M):
     if args.prefill_tokens is not None:
         return args.prefill_tokens
@@ -676,6 +687,8 @@ def main():
                       cpu_tokens=16)
         line["prefill"] = {"metric": "prefill int8 TOP/s", **pre}
         line["prefill"]["mfma_ceiling"] = mfma_ceiling(ctx)
+        if not args.no_rows:
+            line["prefill"]["vendor_int8_mm"] = prefill_vendor_row(ctx, pm)
     print(json.dumps(line), flush=True)
 
 
@@ -845,6 +858,24 @@ CAL_BYTES = 256 << 20        # the calibration copy reads and writes this many b
 ROOF_GROUPS = 9              # timed groups of the roofline's graph replays
 
 
+def mfma_clock_ramp(torch, stream, dev, seconds=RAMP_SECONDS):
+    """About `seconds` of the int8 matrix-instruction probe loop (a kernel of
+    its own, so a kernel trace keeps it apart) before a traced GEMM: the
+    GEMM's launches then run at the clock the bench's timed region sees."""
+    pr = probes(torch)
+    if pr is None:
+        return
+    sink = torch.zeros(16, dtype=torch.int32, device=dev)
+    grid = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            rc = pr.probe_mfma_loop(20000, 1, grid, sink.data_ptr(), stream.cuda_stream)
+            if rc:
+                raise RuntimeError(f"probe_mfma_loop failed ({rc})")
+        stream.synchronize()
+
+
 def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=False,
                   fused_step=None, reps=1, multi=False):
     """One elementwise copy of CAL_BYTES (torch.neg on int32: reads and writes
@@ -885,6 +916,8 @@ def traffic_probe(tb, torch, projs, M, out, copies, stream, dev, wl, grouped=Fal
             with torch.cuda.graph(g, stream=stream):
                 for r in range(copies):
                     launch(r)
+        if M > 64:
+            mfma_clock_ramp(torch, stream, dev)
         for _ in range(reps):
             g.replay()
     else:
