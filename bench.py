@@ -540,6 +540,9 @@ def probes(torch):
     lib.probe_stream_read.restype = ctypes.c_int
     lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_bcast_read.restype = ctypes.c_int
+    lib.probe_bcast_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
     lib.probe_mfma_loop.restype = ctypes.c_int
     lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p]
@@ -583,6 +586,26 @@ def chip_rows(ctx, projs):
                                       "best of 1-3 workgroups of 256 per CU) over the dominant "
                                       "projection's packed bytes, rotated copies: the floor of a "
                                       "kernel that reads the same bytes"}
+        M = dom["Xq"].shape[0]
+        if 2 <= M <= 64:
+            xb = dom["Xq"].numel()
+
+            def shared(xb=xb):
+                rc = pr.probe_bcast_read(dom["Xq"].data_ptr(), xb, cus, sink.data_ptr(),
+                                         stream.cuda_stream)
+                if rc:
+                    raise RuntimeError(f"probe_bcast_read failed ({rc})")
+            g_sh = ctx.graph_of([shared] * 20)
+            g_sh.replay()
+            t_sh = timer(g_sh.replay, 10) / 200
+            del g_sh
+            rows["shared_read"] = {
+                "bytes_per_cu": xb, "us": round(t_sh * 1e6, 3),
+                "GB/s_per_cu": round(xb / t_sh / 1e9, 1), "grid": cus,
+                "note": "probe_bcast_read: one workgroup of 512 threads per CU, each reading the "
+                        "dominant projection's whole X~ (M x K bytes, held by L2): the floor of "
+                        "a launch in which every CU takes in all of X~, as the skinny kernel's "
+                        "workgroups do"}
     x = torch.zeros((1, 16), dtype=torch.float32, device=ctx.dev)
     xq = torch.empty((1, 16), dtype=torch.int8, device=ctx.dev)
     s = torch.empty(1, dtype=torch.float32, device=ctx.dev)

@@ -1,7 +1,9 @@
 // Chip-limit probes for the bench (not part of the BitLinear ABI; built into
 // libbitlinear_probes.so and loaded only by bench.py): a plain streaming read
-// of a buffer, the floor any kernel that must read the same bytes can reach,
-// and a loop of int8 matrix instructions on register operands with the value
+// of a buffer, the floor any kernel that must read the same bytes can reach;
+// a read of one buffer by every workgroup, the rate at which a CU takes in
+// data all CUs share (the skinny kernels' activations); and a loop of int8
+// matrix instructions on register operands with the value
 // distributions of the projection (codes in {0, 1, 2}, quantised activations),
 // the ceiling of the matrix cores for those operands.
 #include <hip/hip_runtime.h>
@@ -29,6 +31,28 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p
     for (int u = 0; u < UNROLL; ++u) a ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
+    const uint4 v = p[i];
+    a ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (a == 0x9e3779b9u) sink[0] = a;
+}
+
+// Every workgroup reads the whole buffer (n16 16-byte pieces, UNROLL loads in
+// flight per thread): with one workgroup per CU and a buffer that L2 holds,
+// the rate at which one CU can take in data that all CUs share.
+template <int UNROLL>
+__global__ __launch_bounds__(512) void k_bcast_read(const uint4* __restrict__ p, int64_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  uint32_t a = 0;
+  int64_t i = threadIdx.x;
+  for (; i + (UNROLL - 1) * 512 < n16; i += UNROLL * 512) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = p[i + u * 512];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) a ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += 512) {
     const uint4 v = p[i];
     a ^= v.x ^ v.y ^ v.z ^ v.w;
   }
@@ -87,6 +111,14 @@ extern "C" {
 // `grid` workgroups of 256 threads.  Returns a hipError_t.
 int probe_stream_read(const void* p, size_t bytes, int grid, void* sink, void* stream) {
   k_stream_read<4><<<dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const uint4*>(p), (int64_t)(bytes / 16), reinterpret_cast<uint32_t*>(sink));
+  return (int)hipGetLastError();
+}
+
+// Shared read: `grid` workgroups of 512 threads each read all `bytes` (a
+// multiple of 16, 16-byte aligned) at `p`.  Returns a hipError_t.
+int probe_bcast_read(const void* p, size_t bytes, int grid, void* sink, void* stream) {
+  k_bcast_read<4><<<dim3(grid), dim3(512), 0, reinterpret_cast<hipStream_t>(stream)>>>(
       reinterpret_cast<const uint4*>(p), (int64_t)(bytes / 16), reinterpret_cast<uint32_t*>(sink));
   return (int)hipGetLastError();
 }

@@ -49,3 +49,17 @@ def test_multi_launch_bytes_ffn70b():
     from synth import WORKLOADS
     shapes = list(WORKLOADS["ffn-70b"].projections)
     assert bench.launch_alg_bytes(shapes, 1, "bf16", True, False, multi=True) == 117_661_704
+
+
+def test_probe_library_exports_the_bench_probes():
+    """The chip-limit probe library the bench loads (built beside the
+    BitLinear library by build()) exports every probe the bench calls; no
+    probe runs here."""
+    import ctypes
+    import os
+    from ternary_bitlinear_amd.build import PROBES_LIB
+    if not os.path.exists(PROBES_LIB):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(PROBES_LIB)
+    for name in ("probe_stream_read", "probe_bcast_read", "probe_mfma_loop"):
+        assert hasattr(lib, name), name
