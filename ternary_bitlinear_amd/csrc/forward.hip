@@ -833,10 +833,14 @@ hipError_t launch_decode_dot_t(DecodeArgs da, hipStream_t stream) {
 // lane reads its column's codes for the whole step as one 16-byte chunk
 // (words 4g .. 4g + 3) and the activation fragment of piece 4g + ks.  Each
 // packed word is expanded once and reused across the wave's row blocks.
-// Codes are the instruction's first operand and activations its second, so
-// the result is the transposed tile: a lane holds one token row and, per
-// register group, four consecutive outputs of it, which the epilogue writes
-// as one vector store with that row's scale and sum loaded once.
+// Activations are the instruction's first operand and codes its second.
+// The matrix cores' power draw depends on which operand holds which values:
+// a loop of these instructions alone on the projection's values runs about
+// 14 % faster with the low-entropy codes second than with them first, and
+// since the GEMM runs at the chip's power limit, the kernel gains about as
+// much.  A lane's results are then one weight row (its column of the block)
+// for 16 tokens; the epilogue takes each token's scale and sum from a table
+// in LDS that the workgroup fills before the K loop.
 //
 // Full steps read activations at row-clamped addresses (rows past M only feed
 // outputs that are not stored).  A K tail (K % 128 != 0) is one more step
@@ -856,7 +860,8 @@ struct GemmArgs {
   const int32_t* xsum;
   void* Y;
   int tiles_m, tiles_n;
-  int vec_out;   // store width: 2 (bf16 via LDS, 16 B), 1 (4 outputs), 0 (scalar)
+  int vec_out;   // 2: bf16 rows staged through LDS, 16-byte stores (k_gemm); 1: four
+                 // outputs per store (split-K reduction); 0: one output per store
   int band;      // tile-order band width in column tiles (see k_gemm)
   int splits;    // K splits per tile; > 1: raw int32 partial tiles into `part`
   int32_t* part; // [splits][M][N] partial accumulators (splits > 1)
@@ -963,7 +968,7 @@ __device__ __forceinline__ void gemm_mma(const GemmFrag<MB, NB>& f, i32x16 (&acc
       const i32x4 bf = expand_codes((uint32_t)f.bw[nb][ks]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        acc[ks % NA][mb][nb] = mfma_i8_32x32x32(bf, f.af[ks][mb], acc[ks % NA][mb][nb]);
+        acc[ks % NA][mb][nb] = mfma_i8_32x32x32(f.af[ks][mb], bf, acc[ks % NA][mb][nb]);
     }
   }
 }
@@ -1012,7 +1017,7 @@ __device__ __forceinline__ void gemm_step(const int8_t* __restrict__ Ac, const u
       const i32x4 bf = expand_codes((uint32_t)bw[nb][ks]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        acc[ks % NA][mb][nb] = mfma_i8_32x32x32(bf, af[ks][mb], acc[ks % NA][mb][nb]);
+        acc[ks % NA][mb][nb] = mfma_i8_32x32x32(af[ks][mb], bf, acc[ks % NA][mb][nb]);
     }
   }
 }
@@ -1044,6 +1049,8 @@ void k_gemm(GemmArgs ga) {
       BL_SB(4), BL_SB(5), BL_SB(6), BL_SB(7);
 #undef BL_SA
 #undef BL_SB
+  __shared__ __attribute__((aligned(16))) int32_t tok_sum[BM];
+  __shared__ __attribute__((aligned(16))) float tok_scale[BM];
   int8_t* const sA[8] = {sA0, sA1, sA2, sA3, sA4, sA5, sA6, sA7};
   uint8_t* const sB[8] = {sB0, sB1, sB2, sB3, sB4, sB5, sB6, sB7};
 
@@ -1126,15 +1133,13 @@ void k_gemm(GemmArgs ga) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc_sets[h][a][c][e] = 0;
 
-  // This lane's token rows in the epilogue; their sums and scales are read
-  // now so the loads are long done by then.
-  int32_t sxv[MB];
-  float scv[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = min(m0 + wm * MB * 32 + mb * 32 + r32, M - 1);
-    sxv[mb] = ga.xsum[m];
-    scv[mb] = ga.xs[m];
+  // The tile's token sums and scales for the epilogue, loaded now so that
+  // the loads are long done by then (rows past M repeat row M - 1; their
+  // outputs are not stored).
+  if (tid < BM) {
+    const int m = min(m0 + tid, M - 1);
+    tok_sum[tid] = ga.xsum[m];
+    tok_scale[tid] = ga.xs[m];
   }
 
   // Fragment rows of this lane; aswz of an activation row depends only on
@@ -1247,67 +1252,64 @@ void k_gemm(GemmArgs ga) {
         for (int e = 0; e < 16; ++e) acc[a][c][e] += acc_sets[h][a][c][e];
 
   // Epilogue: lane (r32, g2), register 4 i + j of block (mb, nb) holds the
-  // output of token m0 + (row block) + r32 and weight row
-  // n0 + (column block) + 8 i + 4 g2 + j.
+  // output of token m0 + (row block) + 8 i + 4 g2 + j and weight row
+  // n0 + (column block) + r32.  For a fixed register the 32 lanes of a half
+  // hold 32 consecutive weight rows of one token: consecutive addresses.
   if (S > 1) {
     // Raw partial accumulators of this split; the reduction kernel adds the
     // splits, subtracts the code offset and rescales.
     int32_t* P = ga.part + (int64_t)split * M * N;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + wm * MB * 32 + mb * 32 + r32;
-      if (m >= M) continue;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
+        const int n = n0 + wn * NB * 32 + nb * 32 + r32;
+        if (n >= N) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = n0 + wn * NB * 32 + nb * 32 + 8 * i + 4 * g2;
-          const int64_t idx = (int64_t)m * N + n;
-          i32x4 v;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][4 * i + j];
-          if (N % 4 == 0) {
-            if (n < N) *reinterpret_cast<i32x4*>(P + idx) = v;
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (n + j < N) P[idx + j] = v[j];
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * MB * 32 + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+          if (m < M) P[(int64_t)m * N + n] = acc[mb][nb][e];
         }
       }
     }
     return;
   }
   const float gamma = ga.gamma[0];
+  // The token table is complete, and (for the staged stores) every wave is
+  // done with the stage buffers.
+  __syncthreads();
   if constexpr (OUT == kOutBF16) {
     if (ga.vec_out == 2) {
-      // Rows of 16-byte pieces through LDS: each wave stages one 32-row block
-      // of its sub-tile at a time in a stage buffer of its own (4 KB or 2 KB),
-      // then writes whole row segments (NB * 64 bytes) with 16-byte stores.
-      // Piece c of staged row r sits at slot c ^ ((r / RPL) % CH), which
-      // keeps both the 8-byte writes and the 16-byte reads conflict-free.
+      // Rows of 16-byte pieces through LDS: each wave stages one 32-token
+      // block of its sub-tile at a time in a stage buffer of its own (4 KB or
+      // 2 KB), then writes whole row segments (NB * 64 bytes) with 16-byte
+      // stores.  Piece c of staged row r sits at slot c ^ ((r / RPL) % CH),
+      // which keeps the 16-byte reads conflict-free.
       constexpr int CH = NB * 4;            // 16-byte pieces per staged row
       constexpr int RPL = 16 / CH;          // staged rows per 256-byte bank row
       static_assert(32 * CH * 16 <= BN * 32, "a code stage holds one block");
       uint8_t* buf = wave == 0 ? reinterpret_cast<uint8_t*>(sA0)
                    : wave == 1 ? reinterpret_cast<uint8_t*>(sA1)
                    : wave == 2 ? reinterpret_cast<uint8_t*>(sA2) : sB0;
-      __syncthreads();   // every wave is done with the stage buffers
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int sw = (r32 / RPL) % CH;
+        const int t0 = wm * MB * 32 + mb * 32;   // the block's first token in the tile
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int i = 0; i < 4; ++i) {
+          const int r0 = 8 * i + 4 * g2;          // staged rows r0 .. r0 + 3
+          const i32x4 sx = *reinterpret_cast<const i32x4*>(tok_sum + t0 + r0);
+          const float4 sc = *reinterpret_cast<const float4*>(tok_scale + t0 + r0);
+          const float scj[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float y[4];
+          for (int nb = 0; nb < NB; ++nb) {
+            const int col = nb * 32 + r32;        // bf16 column of the staged row
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              y[jj] = ((float)(acc[mb][nb][4 * i + jj] - sxv[mb]) * gamma) * scv[mb];
-            const uint32_t lo = (uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16);
-            *reinterpret_cast<uint2*>(buf + r32 * (CH * 16) + 16 * ((nb * 4 + i) ^ sw) + 8 * g2) =
-                make_uint2(lo, hi);
+            for (int j = 0; j < 4; ++j) {
+              const int r = r0 + j;
+              const float y = ((float)(acc[mb][nb][4 * i + j] - sx[j]) * gamma) * scj[j];
+              *reinterpret_cast<uint16_t*>(buf + r * (CH * 16) + 16 * ((col >> 3) ^ ((r / RPL) % CH)) +
+                                           2 * (col & 7)) = f32_to_bf16_rne(y);
+            }
           }
         }
         // The wave's LDS accesses complete in order, so its reads below see
@@ -1318,7 +1320,7 @@ void k_gemm(GemmArgs ga) {
           const int c = lane % CH;
           const uint4 v = *reinterpret_cast<const uint4*>(
               buf + row * (CH * 16) + 16 * (c ^ ((row / RPL) % CH)));
-          const int m = m0 + wm * MB * 32 + mb * 32 + row;
+          const int m = m0 + t0 + row;
           const int n = n0 + wn * NB * 32 + 8 * c;
           if (m < M && n < N)
             *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ga.Y) + (int64_t)m * N + n) = v;
@@ -1329,23 +1331,22 @@ void k_gemm(GemmArgs ga) {
   }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + wm * MB * 32 + mb * 32 + r32;
-    if (m >= M) continue;
+    const int t0 = wm * MB * 32 + mb * 32;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int i = 0; i < 4; ++i) {
+      const int r0 = 8 * i + 4 * g2;
+      const i32x4 sx = *reinterpret_cast<const i32x4*>(tok_sum + t0 + r0);
+      const float4 sc = *reinterpret_cast<const float4*>(tok_scale + t0 + r0);
+      const float scj[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + wn * NB * 32 + nb * 32 + 8 * i + 4 * g2;
-        const int64_t idx = (int64_t)m * N + n;
-        i32x4 v;
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + t0 + r0 + j;
+        if (m >= M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][4 * i + j] - sxv[mb];
-        if (ga.vec_out) {
-          if (n < N) store_out4<OUT>(ga.Y, idx, v, gamma, scv[mb]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (n + j < N) store_out<OUT>(ga.Y, idx + j, v[j], gamma, scv[mb]);
+        for (int nb = 0; nb < NB; ++nb) {
+          const int n = n0 + wn * NB * 32 + nb * 32 + r32;
+          if (n < N)
+            store_out<OUT>(ga.Y, (int64_t)m * N + n, acc[mb][nb][4 * i + j] - sx[j], gamma, scj[j]);
         }
       }
     }
