@@ -633,12 +633,13 @@ def mfma_ceiling(ctx):
     out = {"grid": grid,
            "note": "probe_mfma_loop: v_mfma_i32_32x32x32_i8 on register operands, 2 workgroups "
                    "of 4 waves per CU, 16 independent instructions per wave per iteration; "
-                   "'operands' = codes in {0,1,2} x activations spread like quantised values, "
-                   "'zeros' = all-zero operands (the matrix cores' draw, and with it the clock, "
-                   "depends on the operand values)"}
-    for key, real in (("operands", 1), ("zeros", 0)):
-        def run(real=real):
-            rc = pr.probe_mfma_loop(iters, real, grid, sink.data_ptr(), ctx.stream.cuda_stream)
+                   "'operands' = activations spread like quantised values (first operand) x "
+                   "codes in {0,1,2} (second), the GEMM's order; 'operands_codes_first' = the "
+                   "same values exchanged; 'zeros' = all-zero operands (the matrix cores' draw, "
+                   "and with it the clock, depends on the operand values and their order)"}
+    for key, mode in (("operands", 2), ("operands_codes_first", 1), ("zeros", 0)):
+        def run(mode=mode):
+            rc = pr.probe_mfma_loop(iters, mode, grid, sink.data_ptr(), ctx.stream.cuda_stream)
             if rc:
                 raise RuntimeError(f"probe_mfma_loop failed ({rc})")
         run()
@@ -893,7 +894,7 @@ def mfma_clock_ramp(torch, stream, dev, seconds=RAMP_SECONDS):
     t0 = time.time()
     while time.time() - t0 < seconds:
         for _ in range(8):
-            rc = pr.probe_mfma_loop(20000, 1, grid, sink.data_ptr(), stream.cuda_stream)
+            rc = pr.probe_mfma_loop(20000, 2, grid, sink.data_ptr(), stream.cuda_stream)
             if rc:
                 raise RuntimeError(f"probe_mfma_loop failed ({rc})")
         stream.synchronize()

@@ -839,8 +839,9 @@ hipError_t launch_decode_dot_t(DecodeArgs da, hipStream_t stream) {
 // 14 % faster with the low-entropy codes second than with them first, and
 // since the GEMM runs at the chip's power limit, the kernel gains about as
 // much.  A lane's results are then one weight row (its column of the block)
-// for 16 tokens; the epilogue takes each token's scale and sum from a table
-// in LDS that the workgroup fills before the K loop.
+// for 16 tokens.  Its accumulators start at minus their tokens' sums of X~
+// (so the code offset comes off inside the matrix sums), and the epilogue
+// takes each token's scale from a table in LDS filled before the K loop.
 //
 // Full steps read activations at row-clamped addresses (rows past M only feed
 // outputs that are not stored).  A K tail (K % 128 != 0) is one more step
@@ -1049,7 +1050,6 @@ void k_gemm(GemmArgs ga) {
       BL_SB(4), BL_SB(5), BL_SB(6), BL_SB(7);
 #undef BL_SA
 #undef BL_SB
-  __shared__ __attribute__((aligned(16))) int32_t tok_sum[BM];
   __shared__ __attribute__((aligned(16))) float tok_scale[BM];
   int8_t* const sA[8] = {sA0, sA1, sA2, sA3, sA4, sA5, sA6, sA7};
   uint8_t* const sB[8] = {sB0, sB1, sB2, sB3, sB4, sB5, sB6, sB7};
@@ -1132,15 +1132,27 @@ void k_gemm(GemmArgs ga) {
       for (int c = 0; c < NB; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc_sets[h][a][c][e] = 0;
-
-  // The tile's token sums and scales for the epilogue, loaded now so that
-  // the loads are long done by then (rows past M repeat row M - 1; their
-  // outputs are not stored).
-  if (tid < BM) {
-    const int m = min(m0 + tid, M - 1);
-    tok_sum[tid] = ga.xsum[m];
-    tok_scale[tid] = ga.xs[m];
+  // Without a K split, each accumulator of the first set starts at minus its
+  // token's sum of X~: the matrix sums then end at sum_k (c - 1) x~ = the
+  // exact W~ X~ product, with no subtraction per output in the epilogue.
+  // (Register 4 i + j of block (mb, nb) belongs to token row
+  // mb * 32 + 8 i + 4 g2 + j of the wave's sub-tile; rows past M repeat row
+  // M - 1, and their outputs are not stored.)
+  if (S == 1) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = min(m0 + wm * MB * 32 + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3), M - 1);
+        const int32_t sx = ga.xsum[m];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc_sets[0][mb][nb][e] = -sx;
+      }
   }
+
+  // The tile's token scales for the epilogue, loaded now so that the loads
+  // are long done by then (rows past M repeat row M - 1).
+  if (tid < BM) tok_scale[tid] = ga.xs[min(m0 + tid, M - 1)];
 
   // Fragment rows of this lane; aswz of an activation row depends only on
   // r32 (row blocks are 32 apart).
@@ -1275,7 +1287,7 @@ void k_gemm(GemmArgs ga) {
     return;
   }
   const float gamma = ga.gamma[0];
-  // The token table is complete, and (for the staged stores) every wave is
+  // The token scales are in LDS, and (for the staged stores) every wave is
   // done with the stage buffers.
   __syncthreads();
   if constexpr (OUT == kOutBF16) {
@@ -1297,7 +1309,6 @@ void k_gemm(GemmArgs ga) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r0 = 8 * i + 4 * g2;          // staged rows r0 .. r0 + 3
-          const i32x4 sx = *reinterpret_cast<const i32x4*>(tok_sum + t0 + r0);
           const float4 sc = *reinterpret_cast<const float4*>(tok_scale + t0 + r0);
           const float scj[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
@@ -1306,9 +1317,12 @@ void k_gemm(GemmArgs ga) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int r = r0 + j;
-              const float y = ((float)(acc[mb][nb][4 * i + j] - sx[j]) * gamma) * scj[j];
-              *reinterpret_cast<uint16_t*>(buf + r * (CH * 16) + 16 * ((col >> 3) ^ ((r / RPL) % CH)) +
-                                           2 * (col & 7)) = f32_to_bf16_rne(y);
+              const float y = ((float)acc[mb][nb][4 * i + j] * gamma) * scj[j];
+              // The hardware conversion (v_cvt_pk_bf16_f32) rounds to
+              // nearest even: the same bits as f32_to_bf16_rne for every
+              // non-NaN value, in one instruction.
+              *reinterpret_cast<__bf16*>(buf + r * (CH * 16) + 16 * ((col >> 3) ^ ((r / RPL) % CH)) +
+                                         2 * (col & 7)) = (__bf16)y;
             }
           }
         }
@@ -1335,7 +1349,6 @@ void k_gemm(GemmArgs ga) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r0 = 8 * i + 4 * g2;
-      const i32x4 sx = *reinterpret_cast<const i32x4*>(tok_sum + t0 + r0);
       const float4 sc = *reinterpret_cast<const float4*>(tok_scale + t0 + r0);
       const float scj[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
@@ -1346,7 +1359,7 @@ void k_gemm(GemmArgs ga) {
         for (int nb = 0; nb < NB; ++nb) {
           const int n = n0 + wn * NB * 32 + nb * 32 + r32;
           if (n < N)
-            store_out<OUT>(ga.Y, (int64_t)m * N + n, acc[mb][nb][4 * i + j] - sx[j], gamma, scj[j]);
+            store_out<OUT>(ga.Y, (int64_t)m * N + n, acc[mb][nb][4 * i + j], gamma, scj[j]);
         }
       }
     }
@@ -1772,15 +1785,13 @@ hipError_t launch_gemm_t(GemmArgs ga, hipStream_t stream) {
 inline GemmCfg gemm_cfg(int M, int N, int K) {
   GemmCfg c{128, 128, 1};
   if (M <= 128) c = {64, 64, 1};
-  // 1024+ tokens with K <= 8192: 128 x 256 tiles at two waves per SIMD, the
-  // four waves side by side along N (a 128 x 64 sub-tile each, so every
-  // expanded code word feeds four matrix instructions).  Timed on MI355X
-  // (bench operands, same process): prefill-7b (2048 x 11008 x 4096) 92.1
-  // against 92.9 us with 2 x 2 waves, and 3-6 % faster than 128 x 128.  At
-  // K = 28672 (8192 outputs) the 256 tiles leave half the CUs' second
-  // workgroup slots idle and 128 x 128 stays ahead (215 against 218 us on
-  // the ffn-70b pair).
-  else if (M >= 1024 && K <= 8192) c = {128, 256, 1};
+  // 1024+ tokens: 128 x 256 tiles at two waves per SIMD, 2 x 2 waves (a 64 x
+  // 128 sub-tile each).  Timed on MI355X (same process, three runs): ffn-70b
+  // at 1024 tokens, 8192 -> 28672 in 197-200 us against 200-204 with the
+  // four waves side by side along N, and 28672 -> 8192 in 191-199 against
+  // 197-201 with 128 x 128 tiles; prefill-7b (2048 x 11008 x 4096) the same
+  // within 0.5 %.
+  else if (M >= 1024) c = {128, 256, 1};
   const int tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
   const int nk = K / kGBK;
   if (tiles <= 128) c.splits = max(1, min(kMaxSplits, min(nk / 4, K / (16 * M))));
@@ -1798,7 +1809,7 @@ hipError_t launch_gemm(const GemmCfg& c, GemmArgs ga, hipStream_t stream) {
   ga.splits = c.splits;
   if (c.bm == 128 && c.bn == 128) return launch_gemm_t<A64, OUT, 128, 128, 2, 2, 3>(ga, stream);
   if (c.bm == 128 && c.bn == 256)
-    return launch_gemm_t<A64, OUT, 128, 256, 1, 4, 3, false, 2>(ga, stream);
+    return launch_gemm_t<A64, OUT, 128, 256, 2, 2, 3, false, 2>(ga, stream);
   // 64 x 64 tiles run one workgroup per CU (a single wave per SIMD), so the
   // fragment reads are pipelined a step ahead there (timed 5-7 % faster);
   // at 128 x 128 two workgroups per CU already hide them.
@@ -1820,7 +1831,8 @@ template <bool A64, int OUT>
 hipError_t dispatch(const uint8_t* Wp, const float* gamma, int N, int K, const int8_t* Xq,
                     const float* xs, const int32_t* xsum, int M, void* Y, void* workspace,
                     hipStream_t stream) {
-  // 2: bf16 rows through LDS with 16-byte stores; 1: 4-wide stores; 0: scalar.
+  // 2: bf16 rows through LDS with 16-byte stores; 1: 4-wide stores (split-K
+  // reduction); 0: scalar.
   const uintptr_t ya = reinterpret_cast<uintptr_t>(Y);
   int vec_out = (N % 4 == 0) && (ya % (OUT == kOutBF16 ? 8 : 16) == 0);
   if (OUT == kOutBF16 && N % 8 == 0 && ya % 16 == 0) vec_out = 2;

@@ -4,8 +4,8 @@
 // a read of one buffer by every workgroup, the rate at which a CU takes in
 // data all CUs share (the skinny kernels' activations); and a loop of int8
 // matrix instructions on register operands with the value
-// distributions of the projection (codes in {0, 1, 2}, quantised activations),
-// the ceiling of the matrix cores for those operands.
+// distributions of the projection (codes in {0, 1, 2}, quantised activations)
+// in either operand order, the ceiling of the matrix cores for those operands.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,12 +60,14 @@ __global__ __launch_bounds__(512) void k_bcast_read(const uint4* __restrict__ p,
 }
 
 // iters x 16 independent v_mfma_i32_32x32x32_i8 per wave (4 accumulator
-// sets), operands from registers: with `real` set, A holds codes in {0, 1, 2}
-// and B int8 values spread like quantised activations (a triangular spread,
-// |x| < 64); otherwise both are zero (the matrix cores draw less power on
-// constant operands).  The accumulators are stored only if their sum equals
-// an unlikely value.
-__global__ __launch_bounds__(256) void k_mfma_loop(int iters, int real, int32_t* __restrict__ sink) {
+// sets), operands from registers.  mode 1: the first operand holds codes in
+// {0, 1, 2} and the second int8 values spread like quantised activations (a
+// triangular spread, |x| < 64); mode 2: the same values with the operands
+// exchanged (activations first, the GEMM's order); mode 0: both zero.  The
+// matrix cores draw less power on constant operands, and less with the
+// codes second than first.  The accumulators are stored only if their sum
+// equals an unlikely value.
+__global__ __launch_bounds__(256) void k_mfma_loop(int iters, int mode, int32_t* __restrict__ sink) {
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t h = (blockIdx.x * 4 + wave) * 64 + lane;
   auto next = [&]() {
@@ -83,8 +85,8 @@ __global__ __launch_bounds__(256) void k_mfma_loop(int iters, int real, int32_t*
         const int x = (int)((r >> 8) & 63u) - (int)((r >> 16) & 63u);
         xb |= ((uint32_t)x & 0xffu) << (8 * byte);
       }
-      a[s][d] = real ? (int32_t)ca : 0;
-      b[s][d] = real ? (int32_t)xb : 0;
+      a[s][d] = mode == 1 ? (int32_t)ca : mode == 2 ? (int32_t)xb : 0;
+      b[s][d] = mode == 1 ? (int32_t)xb : mode == 2 ? (int32_t)ca : 0;
     }
   }
   i32x16 acc[4];
@@ -124,11 +126,12 @@ int probe_bcast_read(const void* p, size_t bytes, int grid, void* sink, void* st
 }
 
 // int8 matrix-instruction loop: grid x 4 waves x iters x 16 instructions of
-// 2 * 32 * 32 * 32 operations each, on the projection's operand values (real
-// != 0) or on zeros.  Returns a hipError_t.
-int probe_mfma_loop(int iters, int real, int grid, void* sink, void* stream) {
+// 2 * 32 * 32 * 32 operations each, on the projection's operand values (mode
+// 1: codes first; mode 2: activations first) or on zeros (mode 0).  Returns
+// a hipError_t.
+int probe_mfma_loop(int iters, int mode, int grid, void* sink, void* stream) {
   k_mfma_loop<<<dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
-      iters, real, reinterpret_cast<int32_t*>(sink));
+      iters, mode, reinterpret_cast<int32_t*>(sink));
   return (int)hipGetLastError();
 }
 

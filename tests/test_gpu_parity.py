@@ -169,10 +169,10 @@ FWD_SHAPES = [
     (33, 1030, 2048), (48, 11990, 5440), (63, 4100, 4096), (64, 64, 4096), (64, 20, 64),
     (45, 6000, 192), (40, 16000, 1024), (64, 16400, 1088), (37, 20000, 320),
     (40, 5000, 8320),
-    # 128 x 256 GEMM tiles (1024+ tokens, K <= 8192, four waves along N):
-    # ragged M and N, a K tail; past K = 8192 128 x 128 tiles with a 64-wide
-    # K tail
-    (1030, 300, 1040), (1024, 520, 4160), (1024, 264, 16448),
+    # 128 x 256 GEMM tiles (1024+ tokens, 2 x 2 waves): ragged M and N, K
+    # tails 16 and 64 wide, and K split two ways (16 tiles) with the tail in
+    # the last split
+    (1030, 300, 1040), (1024, 520, 4160), (1024, 264, 16448), (1024, 40, 32784),
 ]
 
 
