@@ -539,7 +539,7 @@ def probes(torch):
     lib = ctypes.CDLL(PROBES_LIB)
     lib.probe_stream_read.restype = ctypes.c_int
     lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                      ctypes.c_void_p, ctypes.c_void_p]
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.probe_bcast_read.restype = ctypes.c_int
     lib.probe_bcast_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_void_p]
@@ -563,29 +563,59 @@ def chip_rows(ctx, projs):
     if pr is not None:
         sink = torch.zeros(16, dtype=torch.int32, device=ctx.dev)
         cus = torch.cuda.get_device_properties(ctx.dev).multi_processor_count
-        best = None
-        for grid in (cus, 2 * cus, 3 * cus):
-            def rd(w, grid=grid):
-                rc = pr.probe_stream_read(w.data_ptr(), nbytes, grid, sink.data_ptr(),
-                                          stream.cuda_stream)
-                if rc:
-                    raise RuntimeError(f"probe_stream_read failed ({rc})")
-            g_read = ctx.graph_of([lambda w=w: rd(w) for w in dom["Wc"]])
-            g_read.replay()
-            reps = max(1, 400 // copies)
-            t = timer(g_read.replay, reps) / (reps * copies)
-            if best is None or t < best[0]:
-                best = (t, grid)
-            del g_read
-        t_read, grid = best
-        rows["plain_read"] = {"bytes": nbytes, "us": round(t_read * 1e6, 3),
-                              "GB/s": round(nbytes / t_read / 1e9, 1),
-                              "frac_of_hbm": round(nbytes / t_read / 1e9 / HBM_PEAK_GBS, 4),
-                              "grid": grid,
-                              "note": "probe_stream_read (16-byte loads, 4 in flight per thread, "
-                                      "best of 1-3 workgroups of 256 per CU) over the dominant "
-                                      "projection's packed bytes, rotated copies: the floor of a "
-                                      "kernel that reads the same bytes"}
+
+        def best_read(ptrs, nb):
+            # (seconds per launch, grid, nt) of the fastest read of nb bytes at each
+            # pointer in turn, over 1-3 workgroups of 256 per CU, plain or
+            # non-temporal loads; and the fastest with plain loads
+            best, best_plain = None, None
+            for nt in (0, 1):
+                for grid in (cus, 2 * cus, 3 * cus):
+                    def rd(ptr, grid=grid, nt=nt):
+                        rc = pr.probe_stream_read(ptr, nb, grid, nt, sink.data_ptr(),
+                                                  stream.cuda_stream)
+                        if rc:
+                            raise RuntimeError(f"probe_stream_read failed ({rc})")
+                    g_read = ctx.graph_of([lambda ptr=ptr: rd(ptr) for ptr in ptrs])
+                    g_read.replay()
+                    reps = max(1, 400 // len(ptrs))
+                    t = timer(g_read.replay, reps) / (reps * len(ptrs))
+                    if best is None or t < best[0]:
+                        best = (t, grid, nt)
+                    if not nt and (best_plain is None or t < best_plain):
+                        best_plain = t
+                    del g_read
+            return best, best_plain
+
+        def read_row(nb, best, best_plain, note):
+            t_read, grid, nt = best
+            return {"bytes": nb, "us": round(t_read * 1e6, 3),
+                    "GB/s": round(nb / t_read / 1e9, 1),
+                    "frac_of_hbm": round(nb / t_read / 1e9 / HBM_PEAK_GBS, 4),
+                    "grid": grid, "loads": "non-temporal" if nt else "plain",
+                    "plain_loads_GB/s": round(nb / best_plain / 1e9, 1),
+                    "note": note}
+
+        best, best_plain = best_read([w.data_ptr() for w in dom["Wc"]], nbytes)
+        rows["plain_read"] = read_row(
+            nbytes, best, best_plain,
+            "probe_stream_read (16-byte loads, 4 in flight per thread; best of 1-3 workgroups "
+            "of 256 per CU and of plain or non-temporal loads) over the dominant projection's "
+            "packed bytes, rotated copies: the floor of a kernel that reads the same bytes")
+        if len(projs) > 1:
+            # the step's packed bytes of all projections as one read (the
+            # multi-projection launch reads them all at once), over copies that
+            # together pass the 256 MB Infinity Cache
+            tot = sum(q["p"].N * q["p"].K // 4 for q in projs) // 16 * 16
+            stride = (tot + 255) // 256 * 256
+            ncp = max(2, -(-(512 << 20) // stride))
+            buf = torch.ones(stride * ncp, dtype=torch.uint8, device=ctx.dev)
+            best, best_plain = best_read([buf.data_ptr() + i * stride for i in range(ncp)], tot)
+            rows["plain_read_step"] = read_row(
+                tot, best, best_plain,
+                "the same probe over the packed bytes of all the step's projections as one "
+                "buffer: the floor of one launch that reads them all")
+            del buf
         M = dom["Xq"].shape[0]
         if 2 <= M <= 64:
             xb = dom["Xq"].numel()

@@ -402,6 +402,20 @@ __device__ __forceinline__ void store_out(void* Y, int64_t idx, int32_t acc, flo
 // ---- MFMA int8 operand types --------------------------------------------------
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes that the kernel reads exactly once (packed weights), loaded with
+// the non-temporal hint.  Timed on MI355X: a streaming read with the hint
+// runs 4-7 % faster than with plain loads; the multi-projection and
+// vector-ALU single-token kernels 6 % faster, the skinny kernel 0-4 % (its
+// direct-to-LDS code loads).  Not every access pattern gains: the matrix
+// decode kernel lost 7-11 % with it and keeps plain loads.
+__device__ __forceinline__ uint4 load_once16(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+// The same hint as the cache-policy argument of a direct global->LDS load.
+constexpr int kLdsLoadOnce = 2;
+
 // v_mfma_i32_16x16x64_i8: C[16x16] += A[16x64] * B[64x16].
 // Lane l supplies A row (l % 16) and B column (l % 16) for k-group (l / 16);
 // the 16 bytes of a lane's A and B operands pair up byte for byte, so any

@@ -1,6 +1,7 @@
 // Chip-limit probes for the bench (not part of the BitLinear ABI; built into
 // libbitlinear_probes.so and loaded only by bench.py): a plain streaming read
-// of a buffer, the floor any kernel that must read the same bytes can reach;
+// of a buffer (plain loads or with the non-temporal hint), the floor any
+// kernel that must read the same bytes can reach;
 // a read of one buffer by every workgroup, the rate at which a CU takes in
 // data all CUs share (the skinny kernels' activations); and a loop of int8
 // matrix instructions on register operands with the value
@@ -14,19 +15,28 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
-// Grid-stride read of n16 16-byte pieces, UNROLL loads in flight per thread;
-// the XOR of everything read is stored only if it equals an unlikely value, so
-// the loads cannot be removed and nothing is written.
-template <int UNROLL>
+// Grid-stride read of n16 16-byte pieces, UNROLL loads in flight per thread,
+// plain or with the non-temporal hint (NT); the XOR of everything read is
+// stored only if it equals an unlikely value, so the loads cannot be removed
+// and nothing is written.
+template <int UNROLL, bool NT>
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p, int64_t n16,
                                                      uint32_t* __restrict__ sink) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   uint32_t a = 0;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
     uint4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < UNROLL; ++u) {
+      if constexpr (NT) {
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i + u * stride));
+        v[u] = make_uint4(t.x, t.y, t.z, t.w);
+      } else {
+        v[u] = p[i + u * stride];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) a ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
@@ -110,10 +120,16 @@ __global__ __launch_bounds__(256) void k_mfma_loop(int iters, int mode, int32_t*
 extern "C" {
 
 // Plain read of `bytes` (a multiple of 16, 16-byte aligned) at `p` with
-// `grid` workgroups of 256 threads.  Returns a hipError_t.
-int probe_stream_read(const void* p, size_t bytes, int grid, void* sink, void* stream) {
-  k_stream_read<4><<<dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
-      reinterpret_cast<const uint4*>(p), (int64_t)(bytes / 16), reinterpret_cast<uint32_t*>(sink));
+// `grid` workgroups of 256 threads; nt != 0: loads with the non-temporal
+// hint.  Returns a hipError_t.
+int probe_stream_read(const void* p, size_t bytes, int grid, int nt, void* sink, void* stream) {
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint32_t* s = reinterpret_cast<uint32_t*>(sink);
+  if (nt)
+    k_stream_read<4, true><<<dim3(grid), dim3(256), 0, st>>>(q, (int64_t)(bytes / 16), s);
+  else
+    k_stream_read<4, false><<<dim3(grid), dim3(256), 0, st>>>(q, (int64_t)(bytes / 16), s);
   return (int)hipGetLastError();
 }
 

@@ -19,7 +19,7 @@
 //   - The workgroup's work is a list of steps (row group of R rows, chunk of
 //     4096 weights); wave w takes a contiguous share of it.  A step loads one
 //     16-byte piece of each of the R rows per lane (whole 1 KB lines per
-//     wave), reads the lane's 64 activations once from LDS for all R rows, and
+//     wave, with the non-temporal hint: the weights are read once), reads the lane's 64 activations once from LDS for all R rows, and
 //     multiplies on the vector ALU (v_dot4_i32_i8 on codes expanded in
 //     registers).  Loads run P steps ahead through P + 1 register buffers, so
 //     the next loads go out before the current step computes.
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(WV * kWave) void k_stream(StreamArgs sa) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = min((g0 + gl) * R + r, N - 1);
-      wq[bf][r] = *reinterpret_cast<const uint4*>(pj.Wp + (int64_t)row * kbytes + 16 * pc);
+      wq[bf][r] = load_once16(pj.Wp + (int64_t)row * kbytes + 16 * pc);
     }
   };
   const bool has = s0 < s1;
