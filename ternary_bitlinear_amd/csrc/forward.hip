@@ -5,19 +5,27 @@
 // Y = acc * gamma * beta / 127, applied once per output after the integer sum
 // (section 6, "Scaling Factor Fusion").
 //
-// The packed codes are c = W~ + 1 in {0, 1, 2}.  They feed the int8 matrix
-// cores unchanged and the kernels subtract sum_k x~_k afterwards:
+// The packed codes are c = W~ + 1 in {0, 1, 2}.  They feed the int8 dot
+// products unchanged and sum_k x~_k removes the offset afterwards:
 //   sum_k W~_k x~_k = sum_k c_k x~_k - sum_k x~_k,
-// which costs one shift and one mask per four weights to unpack.  Zero padding
-// beyond K is harmless because the activation there is zero.
+// which costs shifts and masks only (7 vector instructions per 16 weights)
+// to unpack.  Zero padding beyond K is harmless because the activation there
+// is zero.
 //
-// Two kernels, both on v_mfma_i32_16x16x64_i8 (A = activations, tokens as
-// rows; B = codes, weight rows as columns):
-//   k_decode (M <= 16): a software-pipelined stream over packed rows, see
-//     below; the activation operand comes straight from global memory
-//     (L2-resident) and is reused across the workgroup's row blocks.
-//   k_gemm (M > 16): output tiles up to 256 x 256, K in steps of 128 through
-//     double-buffered LDS; codes are expanded in registers (see below).
+// Kernels, by token count M (the host-side rule is in the dispatchers below):
+//   k_decode_dot (M = 1, rows up to 4096 values, and the fused single-token
+//     calls): v_dot4 on codes expanded in registers, the quantiser optionally
+//     in the prologue;
+//   k_decode (M <= 16): v_mfma_i32_16x16x64_i8, activations first, a
+//     software-pipelined stream over packed rows;
+//   k_skinny (2 <= M <= 64, K % 64 == 0): the same instruction over an LDS
+//     ring of activations and codes, with an optional K split;
+//   k_gemm (M > 16 where k_skinny does not apply): v_mfma_i32_32x32x32_i8,
+//     activations first, 64 x 64 / 128 x 128 / 128 x 256 tiles, K in steps
+//     of 128 through a 3- or 4-stage LDS ring of direct loads; split-K with
+//     k_splitk_reduce when there are few tiles;
+//   k_stream (stream.hpp, M = 1): several projections in one persistent
+//     launch.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "stream.hpp"
