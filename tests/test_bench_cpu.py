@@ -63,3 +63,16 @@ def test_probe_library_exports_the_bench_probes():
     lib = ctypes.CDLL(PROBES_LIB)
     for name in ("probe_stream_read", "probe_bcast_read", "probe_mfma_loop"):
         assert hasattr(lib, name), name
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path runs on one GPU: bench.py exits with a message (status 2)
+    before touching any device when asked for more."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout + r.stderr
