@@ -14,7 +14,13 @@
 // travel together in the 16-bit halves of one register (3 x 255 < 2^10), so
 // two multiplies step all four bytes, and digit j of the four bytes lands as
 // one int8x4 word: the codes of k = 20g + 4j .. 20g + 4j + 3, in the order
-// of four consecutive int8 activations.
+// of four consecutive int8 activations.  Word d = 5g + j of a 16-byte piece
+// therefore holds k = 4d .. 4d + 3 of the piece's 80: the decoded piece is 80
+// consecutive codes, four words per 16-wide slice of K.
+//
+// Kernels: k_decode_b3 (one token, v_dot4 on the vector ALU), k_b3_mma (2-16
+// tokens, v_mfma_i32_16x16x64_i8 on whole decoded pieces) and k_b3_to_b2 (the
+// rewrite to the 2-bit format for the other projection kernels).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -132,6 +138,113 @@ __global__ __launch_bounds__(kB3Waves * kWave) void k_decode_b3(B3Args a) {
     }
 }
 
+// Projection on base-3 weights for 2 <= M <= 16 tokens on the matrix cores
+// (v_mfma_i32_16x16x64_i8, activations first, codes second).  A workgroup
+// owns RBW blocks of 16 weight rows; its 4 waves split the rows' pieces into
+// contiguous ranges, and each wave runs all RBW blocks on every fragment of
+// activations it loads.  Lane (j, g) = (lane & 15, lane >> 4) works on row j
+// of each block and, per step of 4 pieces, piece 4 m + g: its 80 codes decode
+// to 20 code words whose k run consecutively (word d holds k = 4d .. 4d + 3
+// of the piece), so slice s (words 4s .. 4s + 3) is the instruction's second
+// operand for k = 80 p + 16 s .. + 15, and the lane's first operand is the 16
+// activation bytes of token j at the same k.  Each piece is decoded once for
+// all tokens.  Pieces are loaded P steps ahead; slices at or past K read zero
+// activations (the padding codes then add nothing), as do tokens past M.
+// The waves' partial sums are added exactly in LDS; register r of lane
+// (j, g) is token 4 g + r of row j.
+template <int OUT, int P, int RBW>
+__global__ __launch_bounds__(kB3Waves * kWave) void k_b3_mma(B3Args a) {
+  __shared__ i32x4 part[kB3Waves - 1][RBW][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int N = a.N, K = a.K, M = a.M;
+  const int npieces = (K + kB3Piece - 1) / kB3Piece;
+  const int nsteps = (npieces + 3) / 4;
+  const int64_t rowb = 16 * (int64_t)npieces;
+  const int nb0 = 16 * RBW * blockIdx.x + j;   // row of this lane in block 0
+  const uint8_t* row[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) row[rb] = a.Wp + (int64_t)min(nb0 + 16 * rb, N - 1) * rowb;
+  const int8_t* xr = a.Xq + (int64_t)min(j, M - 1) * K;
+  const bool tok = j < M;
+  const int m0 = (int)((int64_t)wave * nsteps / kB3Waves);
+  const int m1 = (int)((int64_t)(wave + 1) * nsteps / kB3Waves);
+
+  constexpr int NB = P + 1;
+  uint4 wq[NB][RBW];
+  auto fill = [&](int b, int m) {
+    const int p = 4 * min(m, m1 - 1) + g;
+    const int64_t off = 16 * (int64_t)(p < npieces ? p : 0);
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) wq[b][rb] = *reinterpret_cast<const uint4*>(row[rb] + off);
+  };
+  i32x4 acc[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) acc[rb] = i32x4{0, 0, 0, 0};
+  if (m0 < m1) {
+#pragma unroll
+    for (int b = 0; b < P; ++b) fill(b, m0 + b);
+    for (int mb = m0; mb < m1; mb += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int m = mb + u;
+        if (m >= m1) break;
+        fill((u + P) % NB, m + P);
+        const int p = 4 * m + g;
+        i32x4 xa[5];
+#pragma unroll
+        for (int sl = 0; sl < 5; ++sl) {
+          const int k0 = kB3Piece * p + 16 * sl;
+          xa[sl] = (tok && k0 < K) ? *reinterpret_cast<const i32x4*>(xr + k0) : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+          const uint32_t w4[4] = {wq[u][rb].x, wq[u][rb].y, wq[u][rb].z, wq[u][rb].w};
+          uint32_t cw[20];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t c[5];
+            decode_b3(w4[q], c);
+#pragma unroll
+            for (int d = 0; d < 5; ++d) cw[5 * q + d] = c[d];
+          }
+#pragma unroll
+          for (int sl = 0; sl < 5; ++sl) {
+            const i32x4 b = {(int32_t)cw[4 * sl], (int32_t)cw[4 * sl + 1], (int32_t)cw[4 * sl + 2],
+                             (int32_t)cw[4 * sl + 3]};
+            acc[rb] = mfma_i8_16x16x64(xa[sl], b, acc[rb]);
+          }
+        }
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) part[wave - 1][rb][lane] = acc[rb];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  const float gamma = a.gamma[0];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int n = nb0 + 16 * rb;
+    if (n >= N) continue;
+    i32x4 t = acc[rb];
+#pragma unroll
+    for (int w = 0; w < kB3Waves - 1; ++w) {
+      const i32x4 o = part[w][rb][lane];
+      t.x += o.x; t.y += o.y; t.z += o.z; t.w += o.w;
+    }
+    const int32_t v[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * g + r;
+      if (tk < M) store_out<OUT>(a.Y, (int64_t)tk * N + n, v[r] - a.xsum[tk], gamma, a.xs[tk]);
+    }
+  }
+}
+
 template <int OUT, int R, int MT>
 hipError_t launch_b3_q(const B3Args& a, hipStream_t stream) {
   static_assert(R * MT <= kWave, "one storing lane per output");
@@ -146,19 +259,33 @@ hipError_t launch_b3_q(const B3Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Rows per wave and token capacity by M.  Decoding costs about two vector
-// instructions per weight, so at one token the rows are spread over more
-// waves: 2 rows per wave below 16384 rows (timed on MI355X: 8640 <- 3200
-// 5.8 vs 6.8 us at 4 rows, 4096 <- 11008 7.6 vs 8.1 us), 4 rows on wider
-// outputs (28672 <- 8192: 22.3 vs 22.8 us at 2).  At 5-8 tokens an 8-token
-// instance (11008 <- 4096 at 8 tokens: 21.2 vs 22.0 us for the 16-token one).
+// One token: the vector-ALU kernel.  Decoding costs about two vector
+// instructions per weight, so the rows are spread over more waves: 2 rows per
+// wave below 16384 rows (timed on MI355X: 8640 <- 3200 5.8 vs 6.8 us at 4
+// rows, 4096 <- 11008 7.6 vs 8.1 us), 4 rows on wider outputs (28672 <- 8192:
+// 22.3 vs 22.8 us at 2).
+// 2-16 tokens: the matrix-core kernel, which decodes each piece once for all
+// tokens (timed against the vector-ALU kernel, same process, identical
+// outputs: 28672 <- 8192 at 2 / 8 / 16 tokens 22.1 / 30.6 / 29.9 us against
+// 30.2 / 112.7 / 193.2; 4096 <- 11008 9.7 / 10.7 / 11.2 against 9.4 / 21.4 /
+// 39.6).  Above 8 tokens the fragments of activations are shared by 4 row
+// blocks per wave on outputs of 16384+ rows and by 2 on 8192+ (28672 <- 8192
+// at 16 tokens: 29.9 us at 4 blocks, 34.4 at 2, 46.2 at 1; 8192 <- 28672:
+// 33.7 at 2, 45.4 at 1, 49.8 at 4); up to 8 tokens one block is fastest.
+template <int OUT, int RBW>
+hipError_t launch_b3_mma(const B3Args& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.N + 16 * RBW - 1) / (16 * RBW)));
+  k_b3_mma<OUT, 2, RBW><<<grid, dim3(kB3Waves * kWave), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int OUT>
 hipError_t launch_b3_out(const B3Args& a, hipStream_t stream) {
   if (a.M <= 1) return a.N >= 16384 ? launch_b3_q<OUT, 4, 1>(a, stream)
                                     : launch_b3_q<OUT, 2, 1>(a, stream);
-  if (a.M <= 4) return launch_b3_q<OUT, 2, 4>(a, stream);
-  if (a.M <= 8) return launch_b3_q<OUT, 1, 8>(a, stream);
-  return launch_b3_q<OUT, 1, 16>(a, stream);
+  if (a.M > 8 && a.N >= 16384) return launch_b3_mma<OUT, 4>(a, stream);
+  if (a.M > 8 && a.N >= 8192) return launch_b3_mma<OUT, 2>(a, stream);
+  return launch_b3_mma<OUT, 1>(a, stream);
 }
 
 // BLT3-v1 -> BLT2-v1: thread per (row, piece); the 80 decoded codes of a

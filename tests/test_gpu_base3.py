@@ -55,13 +55,15 @@ def test_pack3_threshold_neighbours_and_zero_rows(gpu_lib):
     assert_equal(host(P3), want, "BLT3 bytes")
 
 
-# (M, N, K): one token (4 rows per wave), 2-4 tokens (2 rows), 5-16 tokens
-# (1 row); ragged N; K with a cut last piece, one piece per lane, and rows
-# that need several 256-piece blocks.
+# (M, N, K): one token on the vector ALU (2 or 4 rows per wave); 2-16 tokens
+# on the matrix cores with 1 block of 16 rows per wave, and above 8 tokens 2
+# (8192+ rows) or 4 (16384+ rows); ragged N against every block; K with a cut
+# last piece, fewer steps than waves, and rows that need several 256-piece
+# blocks.
 FWD3_SHAPES = [(1, 1, 16), (1, 17, 80), (1, 300, 1040), (1, 8640, 3200), (1, 3200, 8640),
                (1, 100, 20480), (1, 37, 28672), (1, 5, 40960), (2, 33, 96), (3, 129, 4096),
                (4, 1000, 8640), (5, 64, 1040), (8, 257, 4096), (13, 31, 28672), (16, 300, 3200),
-               (16, 1, 16)]
+               (16, 1, 16), (12, 8200, 1040), (9, 8192, 80), (16, 16400, 336), (10, 16385, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", FWD3_SHAPES, ids=[f"M{m}N{n}K{k}" for m, n, k in FWD3_SHAPES])
