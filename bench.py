@@ -200,19 +200,24 @@ def multi_step(tb, projs, M, grouped):
 
 def make_step(ctx, projs, M, grouped, separate=False):
     """step(r, scratch=False): quantise + project every projection once, on
-    weight copy r: one launch for all of them where the multi-projection call
-    (separate inputs) or a grouped decode (one shared input) applies, else one
-    launch per projection where the shape fuses, two where it does not
+    weight copy r. Separate inputs: one bitlinear_forward_f32_multi call (one
+    launch for all projections at one token; above, one quantiser launch for
+    all inputs and one launch per projection where no projection fuses). One
+    shared input: one grouped call. One projection: one bitlinear_forward_f32
     (`separate`: always one bitlinear_forward_f32 per projection)."""
     tb, out, stream = ctx.tb, ctx.out, ctx.stream
     Ns = [q["p"].N for q in projs]
-    if not separate and multi_step(tb, projs, M, grouped):
+    if not separate and not grouped and len(projs) >= 2:
+        m_need = tb.forward_f32_multi_workspace_bytes(M, Ns, [q["p"].K for q in projs])
+        ws_multi = (ctx.torch.empty(m_need, dtype=ctx.torch.uint8, device=ctx.dev)
+                    if m_need else None)
+
         def step(r, scratch=False):
             tb.bitlinear_forward_f32_multi([q["Wc"][r % ctx.copies] for q in projs],
                                            [q["g"] for q in projs], [q["X"] for q in projs],
                                            Ns=Ns, y_dtype=out,
                                            Y=[q["Y_scratch" if scratch else "Y"] for q in projs],
-                                           stream=stream)
+                                           workspace=ws_multi, stream=stream)
         return step
     if grouped:
         g_need = tb.forward_f32_grouped_workspace_bytes(M, Ns, projs[0]["p"].K)

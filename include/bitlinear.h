@@ -310,7 +310,10 @@ bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_pa
  * 4: decode time is the time to read the weights, so the projections share
  * one pass instead of paying a launch each): each workgroup quantises its
  * projection's X once and reads its share of the rows.  Other shapes run the
- * projections one after another.
+ * projections one after another; where none of them has a single-launch
+ * fused path (more than two tokens, or rows past the fused kernels' reach),
+ * all G inputs are quantised by ONE launch first (the same per-row
+ * arithmetic, into the workspace), then each projection is one launch.
  *
  * G          1 .. BITLINEAR_MAX_GROUP.
  * W_packed, gamma, N, K, X, Y   HOST arrays of G entries (read during the call,
@@ -320,7 +323,10 @@ bitlinear_status bitlinear_forward_f32_grouped(int G, const uint8_t* const* W_pa
  * workspace  >= bitlinear_forward_f32_multi_workspace_bytes(M, G, N, K) bytes
  *            (16-byte aligned), scratch after the call; may be NULL when that is
  *            0 (it is 0 for the single launch, and for single-token calls that
- *            fall back to one call per projection).
+ *            fall back to one call per projection).  With the shared quantiser
+ *            launch it holds every input's X~, scales and sums (each region
+ *            rounded up to 256 bytes) and then the largest projection
+ *            workspace.
  * bitlinear_forward_f32_multi_kernel tells which way a call runs.
  */
 size_t bitlinear_forward_f32_multi_workspace_bytes(int64_t M, int G, const int64_t* N,
@@ -480,10 +486,10 @@ int bitlinear_forward_kernel(int entry, int64_t M, int G, const int64_t* N, int6
  * How a bitlinear_forward_f32_multi call with these sizes runs (host only, no
  * GPU call): BITLINEAR_KERNEL_STREAM | BITLINEAR_KERNEL_FUSED_QUANT when all G
  * projections run as one launch (one token, every K[g] a multiple of 64 up to
- * 32768, and rows few enough per workgroup), 0 when they run one
- * bitlinear_forward_f32 call after another (bitlinear_forward_kernel with
- * entry 1 then names each call's kernel), -BITLINEAR_ERR_SHAPE for sizes the
- * call would reject.
+ * 32768, and rows few enough per workgroup), 0 when they run one after
+ * another (bitlinear_forward_kernel with entry 1 then names each projection's
+ * kernel; with the shared quantiser launch, entry 0 does), -BITLINEAR_ERR_SHAPE
+ * for sizes the call would reject.
  */
 int bitlinear_forward_f32_multi_kernel(int64_t M, int G, const int64_t* N, const int64_t* K);
 

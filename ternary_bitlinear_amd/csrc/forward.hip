@@ -2209,9 +2209,29 @@ bool stream_multi_ok(int64_t M, int G, const int64_t* N, const int64_t* K) {
   return stream_plan(sa, 64, kStreamR) > 0;
 }
 
+// Shapes the persistent launch does not take: where no projection has a
+// single-launch fused path, one quantiser launch for every input, then one
+// projection launch each (G - 1 launches fewer than a bitlinear_forward_f32
+// per projection); else one bitlinear_forward_f32 per projection.
+inline bool multi_quant_once(int64_t M, int G, const int64_t* N, const int64_t* K) {
+  if (G < 2 || G > kQuantMaxMulti) return false;
+  for (int g = 0; g < G; ++g)
+    if (fused_dot(M, K[g], false) || afuse(M, 1, &N[g], K[g])) return false;
+  return true;
+}
+
 size_t forward_f32_multi_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K) {
   if (stream_multi_ok(M, G, N, K)) return 0;
   size_t need = 0;
+  if (multi_quant_once(M, G, N, K)) {
+    // every input's quantiser region, then the largest projection workspace
+    size_t q = 0;
+    for (int g = 0; g < G; ++g) {
+      q += quant_region_bytes(M, K[g]);
+      need = std::max(need, forward_grouped_workspace_bytes(M, 1, &N[g], K[g]));
+    }
+    return q + need;
+  }
   for (int g = 0; g < G; ++g)
     need = std::max(need, forward_f32_workspace_bytes(M, N[g], K[g], false));
   return need;
@@ -2232,6 +2252,23 @@ hipError_t launch_forward_f32_multi(int G, const uint8_t* const* W_packed,
       case kOutBF16: return launch_stream_out<kOutBF16>(sa, nwg, maxK, stream);
       default: return launch_stream_out<kOutI32>(sa, nwg, maxK, stream);
     }
+  }
+  if (multi_quant_once(M, G, N, K)) {
+    char* w = reinterpret_cast<char*>(workspace);
+    int8_t* xq[kQuantMaxMulti];
+    float* xs[kQuantMaxMulti];
+    int32_t* xsum[kQuantMaxMulti];
+    for (int g = 0; g < G; ++g) {
+      xq[g] = reinterpret_cast<int8_t*>(w);
+      xs[g] = reinterpret_cast<float*>(w + ((M * K[g] + 255) / 256) * 256);
+      xsum[g] = reinterpret_cast<int32_t*>(xs[g] + M);
+      w += quant_region_bytes(M, K[g]);
+    }
+    hipError_t e = launch_quant_multi(G, X, M, K, xq, xs, xsum, stream);
+    for (int g = 0; g < G && e == hipSuccess; ++g)
+      e = launch_forward_grouped(1, &W_packed[g], &gamma[g], &N[g], K[g], xq[g], xs[g], xsum[g], M,
+                                 &Y[g], y_dtype, w, stream);
+    return e;
   }
   for (int g = 0; g < G; ++g) {
     const hipError_t e = launch_forward_f32(W_packed[g], gamma[g], N[g], K[g], X[g], nullptr, M,

@@ -17,6 +17,13 @@ hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float
                         int32_t* x_sum, hipStream_t stream,
                         int bits = 8);
 
+// The int8 quantiser over up to kQuantMaxMulti activation matrices [M][K[g]]
+// in one launch (the same per-row arithmetic as launch_quant).
+constexpr int kQuantMaxMulti = 4;
+hipError_t launch_quant_multi(int G, const float* const* X, int64_t M, const int64_t* K,
+                              int8_t* const* X_q, float* const* x_scale, int32_t* const* x_sum,
+                              hipStream_t stream);
+
 // RMS normalisation with gain G [K], then the same quantiser.
 hipError_t launch_rmsnorm_quant(const float* X, const float* G, int64_t M, int64_t K,
                                 int8_t* X_q, float* x_scale, int32_t* x_sum, hipStream_t stream);

@@ -14,6 +14,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace bl {
 
 namespace {
@@ -62,16 +64,13 @@ __device__ __forceinline__ int32_t block_sum(int32_t v, int32_t* sh) {
 // qmax = Q_b - 1: 127 for int8 activations, 7 for 4-bit ones (stored one
 // per byte).  The per-element clip to +-127 is inactive at either width:
 // |x| (qmax / (beta + eps)) stays below qmax + 1/2.
-template <int R, int T = kQuantThreads>
-__global__ __launch_bounds__(T) void k_quant_acts(const float* __restrict__ X,
-                                                  int64_t K, int8_t* __restrict__ Xq,
-                                                  float* __restrict__ x_scale,
-                                                  int32_t* __restrict__ x_sum, float qmax) {
-  __shared__ uint32_t s_max[T / kWave];
-  __shared__ int32_t s_sum[T / kWave];
-  const int64_t m = blockIdx.x;
-  const float4* row = reinterpret_cast<const float4*>(X + m * K);
-  uint32_t* qrow = reinterpret_cast<uint32_t*>(Xq + m * K);
+template <int R, int T>
+__device__ __forceinline__ void quant_row(const float* __restrict__ X, int64_t K,
+                                          int8_t* __restrict__ Xq, float* __restrict__ x_scale,
+                                          int32_t* __restrict__ x_sum, float qmax,
+                                          uint32_t* s_max, int32_t* s_sum) {
+  const float4* row = reinterpret_cast<const float4*>(X);
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(Xq);
   const int64_t K4 = K / 4;
 
   uint32_t amax = 0;
@@ -107,9 +106,50 @@ __global__ __launch_bounds__(T) void k_quant_acts(const float* __restrict__ X,
   }
   sum = block_sum<T>(sum, s_sum);
   if (threadIdx.x == 0) {
-    x_sum[m] = sum;
-    x_scale[m] = __uint_as_float(amax) / qmax;
+    *x_sum = sum;
+    *x_scale = __uint_as_float(amax) / qmax;
   }
+}
+
+template <int R, int T = kQuantThreads>
+__global__ __launch_bounds__(T) void k_quant_acts(const float* __restrict__ X,
+                                                  int64_t K, int8_t* __restrict__ Xq,
+                                                  float* __restrict__ x_scale,
+                                                  int32_t* __restrict__ x_sum, float qmax) {
+  __shared__ uint32_t s_max[T / kWave];
+  __shared__ int32_t s_sum[T / kWave];
+  const int64_t m = blockIdx.x;
+  quant_row<R, T>(X + m * K, K, Xq + m * K, x_scale + m, x_sum + m, qmax, s_max, s_sum);
+}
+
+// Several activation matrices (each with its own K) in one launch: workgroup
+// b quantises row b % M of matrix b / M, with the same per-row arithmetic.
+// R and T are chosen for the longest row (shorter rows leave registers idle).
+struct QuantMulti {
+  const float* X[kQuantMaxMulti];
+  int64_t K[kQuantMaxMulti];
+  int8_t* Xq[kQuantMaxMulti];
+  float* xs[kQuantMaxMulti];
+  int32_t* xsum[kQuantMaxMulti];
+};
+
+template <int R, int T>
+__global__ __launch_bounds__(T) void k_quant_acts_multi(QuantMulti q, int64_t M, float qmax) {
+  __shared__ uint32_t s_max[T / kWave];
+  __shared__ int32_t s_sum[T / kWave];
+  const int g = (int)(blockIdx.x / M);
+  const int64_t m = blockIdx.x - g * M;
+  const float* X = q.X[0];
+  int64_t K = q.K[0];
+  int8_t* Xq = q.Xq[0];
+  float* xs = q.xs[0];
+  int32_t* xsum = q.xsum[0];
+#pragma unroll
+  for (int i = 1; i < kQuantMaxMulti; ++i)
+    if (g == i) {
+      X = q.X[i]; K = q.K[i]; Xq = q.Xq[i]; xs = q.xs[i]; xsum = q.xsum[i];
+    }
+  quant_row<R, T>(X + m * K, K, Xq + m * K, xs + m, xsum + m, qmax, s_max, s_sum);
 }
 
 // RMS normalisation, then the absmax quantiser, per token (page section 2:
@@ -241,6 +281,39 @@ hipError_t launch_quant(const float* X, int64_t M, int64_t K, int8_t* X_q, float
     else BL_Q(0, kQuantWideThreads);   // 32 float4 would spill at 128 VGPRs
   }
 #undef BL_Q
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_multi(int G, const float* const* X, int64_t M, const int64_t* K,
+                              int8_t* const* X_q, float* const* x_scale, int32_t* const* x_sum,
+                              hipStream_t stream) {
+  if (G < 1 || G > kQuantMaxMulti || M < 1) return hipErrorInvalidValue;
+  QuantMulti q{};
+  int64_t maxK = 0;
+  for (int g = 0; g < G; ++g) {
+    q.X[g] = X[g]; q.K[g] = K[g]; q.Xq[g] = X_q[g]; q.xs[g] = x_scale[g]; q.xsum[g] = x_sum[g];
+    maxK = std::max(maxK, K[g]);
+  }
+  const dim3 grid((unsigned)(G * M));
+  const bool wide = maxK > kQuantWideKPlain;
+  const int T = wide ? kQuantWideThreads : kQuantThreads;
+  const int64_t per = (maxK / 4 + T - 1) / T;
+  const float qmax = 127.0f;
+#define BL_QM(RR, TT) k_quant_acts_multi<RR, TT><<<grid, dim3(TT), 0, stream>>>(q, M, qmax)
+  if (!wide) {
+    if (per <= 1) BL_QM(1, kQuantThreads);
+    else if (per <= 2) BL_QM(2, kQuantThreads);
+    else if (per <= 4) BL_QM(4, kQuantThreads);
+    else if (per <= 8) BL_QM(8, kQuantThreads);
+    else BL_QM(16, kQuantThreads);
+  } else {
+    if (per <= 2) BL_QM(2, kQuantWideThreads);
+    else if (per <= 4) BL_QM(4, kQuantWideThreads);
+    else if (per <= 8) BL_QM(8, kQuantWideThreads);
+    else if (per <= 16) BL_QM(16, kQuantWideThreads);
+    else BL_QM(0, kQuantWideThreads);
+  }
+#undef BL_QM
   return hipGetLastError();
 }
 

@@ -381,3 +381,21 @@ def test_multi_kernel_query(lib):
     assert q(1, [100] * 5, [512] * 5) == -2   # G > 4
     assert q(1, [0], [512]) == -2
     assert q(1, [100], [40]) == -2            # K % 16 != 0
+
+
+def test_multi_workspace_holds_every_input(lib):
+    # above one token (no projection fusing) the multi call quantises every
+    # input into its workspace first: each X~ rounded to 256 bytes, then 8
+    # bytes per token of scales and sums rounded to 256, then the largest
+    # projection workspace (a K-split skinny projection here)
+    C = ctypes
+    r = lambda b: (b + 255) // 256 * 256
+    q = lambda M, Ns, Ks: lib.bitlinear_forward_f32_multi_workspace_bytes(
+        M, len(Ns), (C.c_int64 * len(Ns))(*Ns), (C.c_int64 * len(Ks))(*Ks))
+    Ns, Ks = [3000, 1000], [1024, 3008]
+    assert q(16, Ns, Ks) == sum(r(16 * k) + r(8 * 16) for k in Ks)
+    Ns, Ks = [1024, 300, 64], [11008, 512, 4096]
+    split = lib.bitlinear_forward_workspace_bytes(32, 1024, 11008)
+    assert split > 0
+    assert q(32, Ns, Ks) == sum(r(32 * k) + r(8 * 32) for k in Ks) + split
+    assert q(1, [28672, 8192], [8192, 28672]) == 0   # the one-launch path

@@ -62,7 +62,16 @@ CASES = [
     (1, [(640, 3200), (3200, 640), (5, 128), (1000, 16384)]),
     (1, [(4096, 4096)]),
     (1, [(200, 1040), (300, 512)]),        # K % 64 != 0: one call per projection
-    (3, [(300, 512), (77, 1024)]),         # three tokens: one call per projection
+    # more tokens: one quantiser launch for every input, then one launch per
+    # projection (skinny, decode, GEMM and a K-split projection whose
+    # workspace follows the inputs' quantiser regions); two tokens, where a
+    # projection may fuse, one call per projection
+    (3, [(300, 512), (77, 1024)]),
+    (5, [(200, 1040), (300, 528)]),
+    (16, [(3000, 1024), (1000, 3008)]),
+    (32, [(1024, 11008), (300, 512), (64, 4096)]),
+    (40, [(700, 2048), (130, 1040), (2, 64), (513, 320)]),
+    (2, [(300, 512), (77, 1040)]),
 ]
 
 
