@@ -5,9 +5,13 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens 
 
 A step is one pass of the per-token path over one batch of synthetic input:
 for every projection of the workload, per-token activation quantisation and
-the projection with its fused rescale, through bitlinear_forward_f32 (one
-launch for decode shapes, where the quantiser runs in the projection's
-prologue; otherwise bitlinear_quant_acts then bitlinear_forward).  Weights are
+the projection with its fused rescale.  Projections with their own inputs
+run as one bitlinear_forward_f32_multi call (one persistent launch at one
+token; above, one quantiser launch for every input and one launch per
+projection), projections sharing one input as one
+bitlinear_forward_f32_grouped call, a single projection through
+bitlinear_forward_f32 (one launch for decode shapes, where the quantiser runs
+in the projection's prologue; otherwise the quantiser, then the projection).  Weights are
 ternarised and packed once at set-up (bitlinear_pack_weights), as at
 inference; that step is timed separately and reported under "rows", as are
 the standalone quantiser and the projection on pre-quantised activations.
@@ -334,7 +338,7 @@ def measure(ctx, M, steps, warmup, args, rows=True, cpu_tokens=None):
     }
     if rows:
         res["rows"] = side_rows(ctx, projs, M, proj_roof, step, grouped)
-        if multi:
+        if not grouped and len(projs) >= 2:
             # the same step as one bitlinear_forward_f32 per projection
             sep = make_step(ctx, projs, M, grouped, separate=True)
             g_sep = ctx.graph_of([lambda r=r: sep(r) for r in range(ctx.copies)])
@@ -344,8 +348,8 @@ def measure(ctx, M, steps, warmup, args, rows=True, cpu_tokens=None):
             res["rows"]["step_separate_calls"] = {
                 "us": round(t_sep * 1e6, 3),
                 "GB/s": round(wbytes_step / t_sep / 1e9, 1),
-                "note": "one bitlinear_forward_f32 per projection, one launch each (the step "
-                        "runs them as one bitlinear_forward_f32_multi launch)"}
+                "note": "one bitlinear_forward_f32 per projection (the step runs them as one "
+                        "bitlinear_forward_f32_multi call)"}
     if not args.no_cpu_baseline:
         # the timed step once more, its outputs for the oracle leg to check
         with torch.cuda.stream(stream):
