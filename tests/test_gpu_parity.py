@@ -173,6 +173,9 @@ FWD_SHAPES = [
     # tails 16 and 64 wide, and K split two ways (16 tiles) with the tail in
     # the last split
     (1030, 300, 1040), (1024, 520, 4160), (1024, 264, 16448), (1024, 40, 32784),
+    # many tiles (several rounds of the chip) with a 16-wide K tail: aligned,
+    # then ragged M and N
+    (2048, 12288, 272), (1030, 24600, 1040),
 ]
 
 
