@@ -2166,13 +2166,12 @@ StreamArgs stream_args(int G, const uint8_t* const* Wp, const float* const* gamm
   StreamArgs sa{};
   sa.G = G;
   for (int g = 0; g < G; ++g) {
-    StreamProj& p = sa.p[g];
-    p.Wp = Wp[g];
-    p.gamma = gamma[g];
-    p.Y = Y[g];
-    p.N = (int)N[g];
-    p.K = (int)K[g];
-    p.X = X[g];
+    sa.rec[g].Wp = Wp[g];
+    sa.rec[g].X = X[g];
+    sa.rec[g].N = (int)N[g];
+    sa.rec[g].K = (int)K[g];
+    sa.gamma[g] = gamma[g];
+    sa.Y[g] = Y[g];
   }
   return sa;
 }
@@ -2203,8 +2202,8 @@ bool stream_multi_ok(int64_t M, int G, const int64_t* N, const int64_t* K) {
   StreamArgs sa{};
   sa.G = G;
   for (int g = 0; g < G; ++g) {
-    sa.p[g].N = (int)N[g];
-    sa.p[g].K = (int)K[g];
+    sa.rec[g].N = (int)N[g];
+    sa.rec[g].K = (int)K[g];
   }
   return stream_plan(sa, 64, kStreamR) > 0;
 }
