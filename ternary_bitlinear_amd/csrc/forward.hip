@@ -629,10 +629,17 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
   // order, so activations requested after the weights could not be used
   // before the weights had arrived; the scheduling barriers keep the
   // compiler from sinking the weight loads below the chain.
-  if constexpr (FUSE == kDotFuseNone) load_weights();
+  // The epilogue's gamma and output pointer are read after the weight loads
+  // are issued: a wait for their scalar loads (one of them a global one)
+  // must not hold up the weight stream.
+  float gamma;
+  void* yout;
+  if constexpr (FUSE == kDotFuseNone) {
+    load_weights();
+    gamma = view.gamma[0];
+    yout = view.Y;
+  }
   int32_t xa[Q][16];
-  const float gamma = view.gamma[0];
-  void* const yout = view.Y;
   int32_t sx;
   float sc;
   if constexpr (FUSE == kDotFuseBlock) {
@@ -649,6 +656,8 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
     __builtin_amdgcn_sched_barrier(0);
     load_weights();
     __builtin_amdgcn_sched_barrier(0);
+    gamma = view.gamma[0];
+    yout = view.Y;
     asm volatile("" ::"s"(gamma), "s"(yout));
     if constexpr (NORM) {
       // RMS normalisation first: the standalone normalising quantiser's
@@ -1064,6 +1073,12 @@ void k_gemm(GemmArgs ga) {
   int8_t* const sA[8] = {sA0, sA1, sA2, sA3, sA4, sA5, sA6, sA7};
   uint8_t* const sB[8] = {sB0, sB1, sB2, sB3, sB4, sB5, sB6, sB7};
 
+  // Every argument the prologue uses, requested in one round of scalar loads
+  // (left to itself the compiler loads them where first used, in three
+  // dependent rounds, each waiting for the last).
+  asm volatile("" ::"s"(ga.Wp), "s"(ga.Xq), "s"(ga.xsum), "s"(ga.xs), "s"(ga.N), "s"(ga.K),
+               "s"(ga.M), "s"(ga.tiles_m), "s"(ga.tiles_n), "s"(ga.band), "s"(ga.splits));
+  __builtin_amdgcn_sched_barrier(0);
   const int N = ga.N, K = ga.K, M = ga.M;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
