@@ -447,4 +447,25 @@ __device__ __forceinline__ i32x4 expand_codes(uint32_t w) {
   return r;
 }
 
+// sum_k c_k x~_k of one 16-code word w (BLT2-v1) against its 16 activations,
+// four per dword in k order (x[d] holds k = 4d .. 4d + 3), on the vector ALU
+// without expanding the codes to bytes: field f of the code bytes (bits 2f,
+// 2f + 1 of byte b: the code of k = 4f + b) is masked in place, so its bytes
+// are c 4^f for f = 0, 1, 2, and field 3 is shifted down one bit (c 32, at
+// most 64, still a signed byte).  One accumulator per field; fields_total
+// divides each back exactly (every field sum is a multiple of its scale).
+// Five masks and four v_dot4 per word, against seven and four for the byte
+// expansion.  An accumulator stays below 2^31 while |sum| <= 2 * 127 * 32 K,
+// i.e. for any K below 2^18.
+__device__ __forceinline__ void dot_word_fields(uint32_t w, const int32_t* x, int32_t (&acc)[4]) {
+  acc[0] = __builtin_amdgcn_sdot4((int32_t)(w & 0x03030303u), x[0], acc[0], false);
+  acc[1] = __builtin_amdgcn_sdot4((int32_t)(w & 0x0c0c0c0cu), x[1], acc[1], false);
+  acc[2] = __builtin_amdgcn_sdot4((int32_t)(w & 0x30303030u), x[2], acc[2], false);
+  acc[3] = __builtin_amdgcn_sdot4((int32_t)((w >> 1) & 0x60606060u), x[3], acc[3], false);
+}
+
+__device__ __forceinline__ int32_t fields_total(const int32_t (&acc)[4]) {
+  return acc[0] + (acc[1] >> 2) + (acc[2] >> 4) + (acc[3] >> 5);
+}
+
 }  // namespace bl

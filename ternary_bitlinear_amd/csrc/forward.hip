@@ -14,8 +14,8 @@
 //
 // Kernels, by token count M (the host-side rule is in the dispatchers below):
 //   k_decode_dot (M = 1, rows up to 4096 values, and the fused single-token
-//     calls): v_dot4 on codes expanded in registers, the quantiser optionally
-//     in the prologue;
+//     calls): v_dot4 on the 2-bit code fields masked in registers, the
+//     quantiser optionally in the prologue;
 //   k_decode (M <= 16): v_mfma_i32_16x16x64_i8, activations first, a
 //     software-pipelined stream over packed rows;
 //   k_skinny (2 <= M <= 64, K % 64 == 0): the same instruction over an LDS
@@ -571,10 +571,10 @@ hipError_t launch_decode(const DecodeCfg& c, const DecodeArgs& da, hipStream_t s
 // p = l, l + 64, ... (Q of them; 64 weights each) of a row, so the wave's
 // loads of one row are contiguous and whole cache lines.  The lane's 64
 // activations per piece are loaded once into registers and serve all R
-// rows.  Codes expand to int8 in registers as in the matrix kernels and
-// multiply with v_dot4_i32_i8 (four products per instruction); a wave
-// shuffle sums each row.  At one token the matrix instruction would compute
-// 16 columns to keep one.  Lanes past a row's end re-read its first piece and
+// rows.  Each 2-bit field of the code bytes is masked in place and
+// multiplied with v_dot4_i32_i8 (four products per instruction, one
+// accumulator per field: dot_word_fields); a wave shuffle sums each row.  At
+// one token the matrix instruction would compute 16 columns to keep one.  Lanes past a row's end re-read its first piece and
 // multiply it by zeroed activations.
 //
 // FUSE = kDotFuseBlock (fp32 input) quantises the token inside the kernel,
@@ -762,9 +762,11 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
   if constexpr (FUSE == kDotFuseBlock && Q > kDotHeldQ) {
     // Long rows: each piece's codes are read from LDS when its turn comes
     // (piece outer, rows inner), so only one piece of activations is held.
-    int32_t accr[R];
+    int32_t accr[R][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) accr[r] = 0;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) accr[r][f] = 0;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int p = lane + kWave * q;
@@ -783,37 +785,25 @@ __global__ __launch_bounds__(WV * kWave) void k_decode_dot(DecodeArgs da) {
       for (int r = 0; r < R; ++r) {
         const uint32_t w4[4] = {wq[r][q].x, wq[r][q].y, wq[r][q].z, wq[r][q].w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const i32x4 c = expand_codes(w4[t]);
-          accr[r] = __builtin_amdgcn_sdot4(c.x, xq[4 * t + 0], accr[r], false);
-          accr[r] = __builtin_amdgcn_sdot4(c.y, xq[4 * t + 1], accr[r], false);
-          accr[r] = __builtin_amdgcn_sdot4(c.z, xq[4 * t + 2], accr[r], false);
-          accr[r] = __builtin_amdgcn_sdot4(c.w, xq[4 * t + 3], accr[r], false);
-        }
+        for (int t = 0; t < 4; ++t) dot_word_fields(w4[t], &xq[4 * t], accr[r]);
       }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int32_t acc = wave_sum_i32(accr[r]);
+      const int32_t acc = wave_sum_i32(fields_total(accr[r]));
       if (lane == r) mine = acc;
     }
   } else {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      int32_t acc = 0;
+      int32_t fa[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const uint32_t w4[4] = {wq[r][q].x, wq[r][q].y, wq[r][q].z, wq[r][q].w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const i32x4 c = expand_codes(w4[t]);
-          acc = __builtin_amdgcn_sdot4(c.x, xa[q][4 * t + 0], acc, false);
-          acc = __builtin_amdgcn_sdot4(c.y, xa[q][4 * t + 1], acc, false);
-          acc = __builtin_amdgcn_sdot4(c.z, xa[q][4 * t + 2], acc, false);
-          acc = __builtin_amdgcn_sdot4(c.w, xa[q][4 * t + 3], acc, false);
-        }
+        for (int t = 0; t < 4; ++t) dot_word_fields(w4[t], &xa[q][4 * t], fa);
       }
-      acc = wave_sum_i32(acc);
+      const int32_t acc = wave_sum_i32(fields_total(fa));
       if (lane == r) mine = acc;
     }
   }

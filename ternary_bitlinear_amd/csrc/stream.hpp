@@ -26,7 +26,8 @@
 //     16-byte piece of each of the R rows per lane (whole 1 KB lines per
 //     wave, with the non-temporal hint: the weights are read once), reads
 //     the lane's 64 activations once from LDS for all R rows, and multiplies
-//     on the vector ALU (v_dot4_i32_i8 on codes expanded in registers).
+//     on the vector ALU (v_dot4_i32_i8 on each 2-bit field of the code bytes
+//     masked in place, one accumulator per field: dot_word_fields).
 //     Loads run P steps ahead through P + 1 register buffers, so the next
 //     loads go out before the current step computes.
 //   - A wave's partial sums of a row group are reduced across the wave (DPP)
@@ -168,9 +169,13 @@ __global__ __launch_bounds__(WV * kWave) void k_stream(StreamArgs sa) {
   for (int w = 0; w < WV; ++w) sx += (int32_t)s_red[1][w];
   const float sc = beta / 127.0f;
 
-  int32_t acc[R];
+  // Per row, one accumulator per 2-bit field of the code bytes
+  // (dot_word_fields), added up when the wave leaves the row group.
+  int32_t facc[R][4];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0;
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) facc[r][f] = 0;
   // One step: the loads P steps ahead, then the dot products of step s from
   // ring buffer u.
   auto step = [&](const int u, const int s) {
@@ -188,21 +193,16 @@ __global__ __launch_bounds__(WV * kWave) void k_stream(StreamArgs sa) {
     for (int r = 0; r < R; ++r) {
       const uint32_t w4[4] = {wq[u][r].x, wq[u][r].y, wq[u][r].z, wq[u][r].w};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const i32x4 cd = expand_codes(w4[t]);
-        acc[r] = __builtin_amdgcn_sdot4(cd.x, xq[4 * t + 0], acc[r], false);
-        acc[r] = __builtin_amdgcn_sdot4(cd.y, xq[4 * t + 1], acc[r], false);
-        acc[r] = __builtin_amdgcn_sdot4(cd.z, xq[4 * t + 2], acc[r], false);
-        acc[r] = __builtin_amdgcn_sdot4(cd.w, xq[4 * t + 3], acc[r], false);
-      }
+      for (int t = 0; t < 4; ++t) dot_word_fields(w4[t], &xq[4 * t], facc[r]);
     }
     if (c == (int)Q - 1 || s == s1 - 1) {
       // the wave leaves this row group: its partial sums into LDS
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int32_t t = wave_sum_i32(acc[r]);
+        const int32_t t = wave_sum_i32(fields_total(facc[r]));
         if (lane == 0) atomicAdd(&acc_l[gl * R + r], t);
-        acc[r] = 0;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) facc[r][f] = 0;
       }
     }
   };
