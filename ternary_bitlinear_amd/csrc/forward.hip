@@ -2157,13 +2157,16 @@ int device_cus() {
   return v;
 }
 
-// Launch shape (timed on MI355X over the 3B and 70B feed-forward pairs, both
-// projections in one launch): 4 rows per step, loads 2 steps ahead, 8 waves,
-// one workgroup per CU.  70B 8192 -> 28672 with 28672 -> 8192 in 25.8-26.1 us
-// against 15.6 + 18.7 us as two fused single-projection calls; 3B 3200 <->
-// 8640 in 9.2 us against 5.4 + 5.7 us.  (One projection alone is slower than
-// the single-projection kernels, which keep those calls.)
-constexpr int kStreamR = 4, kStreamP = 2, kStreamWV = 8;
+// Launch shape (timed on MI355X over the 3B, 7B and 70B single-token steps,
+// all projections in one launch): 4 rows per step, loads 1 step ahead, 8
+// waves, one workgroup per CU.  Loads 1 step ahead against 2: 70B 8192 ->
+// 28672 with 28672 -> 8192 22.08 against 22.13 us, 7B 7.99 against 8.89 us,
+// 3B 6.26 against 7.25 us (at 3B and 7B sizes a wave has 2-4 steps, which a
+// ring of two runs as whole unguarded rounds); 2 rows per step, or deeper
+// rings, were slower.  Against two fused single-projection calls: 70B 22.1
+// against 33.6 us.  (One projection alone is slower than the
+// single-projection kernels, which keep those calls.)
+constexpr int kStreamR = 4, kStreamP = 1, kStreamWV = 8;
 
 StreamArgs stream_args(int G, const uint8_t* const* Wp, const float* const* gamma,
                        const int64_t* N, const int64_t* K, const float* const* X,
