@@ -199,9 +199,12 @@ size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * X~, same x_scale, same x_sum, same accumulators; page section 2, absmax
  * activation quantiser and the linear transformation), as one launch for
  * single-token shapes (K a multiple of 64 up to 16384, or longer rows whose
- * int8 copy fits the on-chip staging) and two-token narrow ones (every
- * workgroup quantises the activations it needs), else as those two
- * launches.  This is the quantiser folded into the projection's prologue.
+ * int8 copy fits the on-chip staging; one projection of 2^25 weights or
+ * more, with K a multiple of 64 up to 32768, takes the persistent launch of
+ * bitlinear_forward_f32_multi)
+ * and two-token narrow ones (every workgroup quantises the activations it
+ * needs), else as those two launches.  This is the quantiser folded into
+ * the projection's prologue.
  *
  * X        [M][K] fp32, device, 16-byte aligned (read only).
  * Y        [M][N], device, as in bitlinear_forward.
@@ -462,8 +465,9 @@ typedef enum bitlinear_kernel {
   BITLINEAR_KERNEL_SKINNY = 3,     /* 2-64 tokens: activations and codes through an LDS ring
                                       (K split over workgroups on long-K shapes) */
   BITLINEAR_KERNEL_GEMM = 4,       /* tiled matrix product (K split over workgroups when tiles are few) */
-  BITLINEAR_KERNEL_STREAM = 5,     /* one token, several projections with their own activations
-                                      in one persistent launch (bitlinear_forward_f32_multi) */
+  BITLINEAR_KERNEL_STREAM = 5,     /* one token, one persistent launch over every projection
+                                      (bitlinear_forward_f32_multi; bitlinear_forward_f32 from
+                                      2^25 weights) */
   BITLINEAR_KERNEL_FUSED_QUANT = 16 /* or'ed in: the activation quantiser runs in the same launch */
 } bitlinear_kernel;
 

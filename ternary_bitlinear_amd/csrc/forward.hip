@@ -2039,10 +2039,31 @@ inline bool afuse(int64_t M, int G, const int64_t* N, int64_t K) {
   return M <= 2 && fused_cfg(M, G, N, K).am == kAFuse && !skinny_ok(M, group_rows(G, N), K);
 }
 
+// One projection, one token, no normalisation, at least 2^25 weights: the
+// persistent launch (k_stream) instead of the fused vector-ALU or matrix
+// decode.  Timed on MI355X with graph replay over rotated weight copies
+// (identical output bytes): 8192 -> 28672 12.6 against 14.4 us, 28672 ->
+// 8192 15.8 against 19.0 us, 4096 <-> 11008 6.07 / 6.18 against 6.23 / 6.66
+// us; below the threshold it was slower (4096 -> 4096 3.99 against 3.41 us)
+// or even (8640 -> 3200 5.43 against 5.36 us), and for q/k/v as one grouped
+// call it gained nothing in the step (5.95 against 5.69 us).
+constexpr int64_t kStreamSingleMinWeights = int64_t(1) << 25;
+
+inline bool stream_single(int64_t M, int G, const int64_t* N, int64_t K) {
+  if (M != 1 || G != 1) return false;
+  return N[0] * K >= kStreamSingleMinWeights && stream_multi_ok(1, 1, N, &K);
+}
+
+hipError_t launch_stream_shared(int G, const uint8_t* const* W_packed, const float* const* gamma,
+                                const int64_t* N, int64_t K, const float* X, void* const* Y,
+                                int y_dtype, int8_t* X_q_out, float* x_scale_out,
+                                int32_t* x_sum_out, hipStream_t stream);
+
 // norm: RMS normalisation first; the single-token vector-ALU prologue fuses
 // it, the multi-token matrix prologue does not (two launches there).
 size_t forward_f32_grouped_workspace_bytes(int64_t M, int G, const int64_t* N, int64_t K,
                                            bool norm) {
+  if (!norm && stream_single(M, G, N, K)) return 0;
   if (fused_dot(M, K, norm) || (!norm && afuse(M, G, N, K))) return 0;
   return quant_region_bytes(M, K) + forward_grouped_workspace_bytes(M, G, N, K);
 }
@@ -2065,6 +2086,9 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
                                       void* const* Y, int y_dtype, int8_t* X_q_out,
                                       float* x_scale_out, int32_t* x_sum_out, void* workspace,
                                       hipStream_t stream) {
+  if (norm_g == nullptr && stream_single(M, G, N, K))
+    return launch_stream_shared(G, W_packed, gamma, N, K, X, Y, y_dtype, X_q_out, x_scale_out,
+                                x_sum_out, stream);
   if (fused_dot(M, K, norm_g != nullptr)) {
     DecodeArgs da = decode_args_group(G, W_packed, gamma, N, (int)K, (int)M, Y);
     da.X = X;
@@ -2115,6 +2139,7 @@ hipError_t launch_forward_f32_grouped(int G, const uint8_t* const* W_packed,
 int forward_kernel(int entry, int64_t M, int G, const int64_t* N, int64_t K) {
   constexpr int kFused = 16;
   if (entry != 0) {
+    if (entry == 1 && stream_single(M, G, N, K)) return kKernelStream | kFused;
     if (fused_dot(M, K, entry == 2)) return kKernelDecodeDot | kFused;
     if (entry == 1 && afuse(M, G, N, K)) return kKernelDecode | kFused;
   }
@@ -2186,8 +2211,12 @@ StreamArgs stream_args(int G, const uint8_t* const* Wp, const float* const* gamm
 
 template <int OUT, int KJ>
 hipError_t launch_stream_kj(const StreamArgs& sa, int nwg, hipStream_t stream) {
-  k_stream<OUT, kStreamR, kStreamP, kStreamWV, KJ>
-      <<<dim3(nwg), dim3(kStreamWV * kWave), 0, stream>>>(sa);
+  if (sa.xq_out != nullptr)
+    k_stream<OUT, kStreamR, kStreamP, kStreamWV, KJ, true>
+        <<<dim3(nwg), dim3(kStreamWV * kWave), 0, stream>>>(sa);
+  else
+    k_stream<OUT, kStreamR, kStreamP, kStreamWV, KJ, false>
+        <<<dim3(nwg), dim3(kStreamWV * kWave), 0, stream>>>(sa);
   return hipGetLastError();
 }
 
@@ -2284,6 +2313,29 @@ hipError_t launch_forward_f32_multi(int G, const uint8_t* const* W_packed,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_stream_shared(int G, const uint8_t* const* W_packed, const float* const* gamma,
+                                const int64_t* N, int64_t K, const float* X, void* const* Y,
+                                int y_dtype, int8_t* X_q_out, float* x_scale_out,
+                                int32_t* x_sum_out, hipStream_t stream) {
+  const float* Xs[kStreamMaxProj];
+  int64_t Ks[kStreamMaxProj];
+  for (int g = 0; g < G; ++g) {
+    Xs[g] = X;
+    Ks[g] = K;
+  }
+  StreamArgs sa = stream_args(G, W_packed, gamma, N, Ks, Xs, Y);
+  sa.xq_out = X_q_out;
+  sa.xs_out = x_scale_out;
+  sa.xsum_out = x_sum_out;
+  const int nwg = stream_plan(sa, std::max(device_cus(), 64), kStreamR);
+  if (nwg <= 0) return hipErrorInvalidValue;
+  switch (y_dtype) {
+    case kOutF32: return launch_stream_out<kOutF32>(sa, nwg, K, stream);
+    case kOutBF16: return launch_stream_out<kOutBF16>(sa, nwg, K, stream);
+    default: return launch_stream_out<kOutI32>(sa, nwg, K, stream);
+  }
 }
 
 }  // namespace bl

@@ -65,6 +65,11 @@ struct StreamArgs {
   const float* gamma[kStreamMaxProj];
   void* Y[kStreamMaxProj];
   int G;
+  // copies of projection 0's quantiser outputs (X~ [K], x_scale, x_sum),
+  // written by its first workgroup in the kernel's QOUT form
+  int8_t* xq_out;
+  float* xs_out;
+  int32_t* xsum_out;
 };
 
 // The LDS layout of the kernel: activations (K bytes, padded) and a 64-byte
@@ -72,7 +77,8 @@ struct StreamArgs {
 constexpr int kStreamMaxK = 32768;
 constexpr int kStreamMaxRowsWg = 4096;
 
-template <int OUT, int R, int P, int WV, int KJ>
+// QOUT: copy projection 0's quantiser outputs out (xq_out, xs_out, xsum_out).
+template <int OUT, int R, int P, int WV, int KJ, bool QOUT>
 __global__ __launch_bounds__(WV * kWave) void k_stream(StreamArgs sa) {
   static_assert(KJ > 0, "the fp32 row is held in registers");
   constexpr int NB = P + 1;
@@ -168,6 +174,14 @@ __global__ __launch_bounds__(WV * kWave) void k_stream(StreamArgs sa) {
 #pragma unroll
   for (int w = 0; w < WV; ++w) sx += (int32_t)s_red[1][w];
   const float sc = beta / 127.0f;
+  if (QOUT && b == 0) {
+    // projection 0's first workgroup hands out its quantiser outputs
+    for (int i = threadIdx.x; i < K; i += T) sa.xq_out[i] = xl[i];
+    if (threadIdx.x == 0) {
+      sa.xs_out[0] = sc;
+      sa.xsum_out[0] = sx;
+    }
+  }
 
   // Per row, one accumulator per 2-bit field of the code bytes
   // (dot_word_fields), added up when the wave leaves the row group.

@@ -211,7 +211,14 @@ def test_forward_kernel_query(lib):
     assert fk("forward", 1, [4096], 4096) == ("k_decode_dot", False)
     assert fk("f32", 1, [4096], 4096) == ("k_decode_dot", True)
     assert fk("rmsnorm", 1, [4096], 11008) == ("k_decode_dot", True)
-    assert fk("f32", 1, [8192], 16384) == ("k_decode_dot", True)
+    assert fk("f32", 1, [8192], 16384) == ("k_stream", True)          # >= 2^25 weights
+    assert fk("f32", 1, [2048], 16384) == ("k_stream", True)          # exactly 2^25
+    assert fk("f32", 1, [2047], 16384) == ("k_decode_dot", True)
+    assert fk("f32", 1, [4096] * 3, 4096) == ("k_decode_dot", True)   # a group: not stream
+    assert fk("f32", 1, [28672], 8192) == ("k_stream", True)
+    assert fk("f32", 1, [8192], 28672) == ("k_stream", True)          # K past the fused rows
+    assert fk("f32", 1, [8192], 40960) == ("k_decode", False)         # K past 32768
+    assert fk("rmsnorm", 1, [8192], 4096) == ("k_decode_dot", True)   # normalisation: not stream
     assert fk("rmsnorm", 1, [8192], 16384)[1] is False
     assert fk("forward", 1, [4096], 11008) == ("k_decode", False)
     assert fk("forward", 4, [4096], 4096) == ("k_decode", False)        # narrow, few tokens

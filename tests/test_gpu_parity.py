@@ -400,6 +400,9 @@ FUSED_SHAPES = [
     # two pieces per lane on 16384+ rows (8 waves per workgroup), the last
     # wave and workgroup partly past the end
     (1, 16390, 4160),
+    # the persistent launch (2^25 weights and more): exactly 2^25, a partial
+    # last 4-row group, the longest rows it takes
+    (1, 2048, 16384), (1, 8193, 4096), (1, 1030, 32768),
     # outside the fused kernel's reach: two launches
     (9, 77, 1040), (16, 300, 4096), (8, 64, 8640), (40, 130, 1024), (2, 50, 40960),
     # two launches with K split across workgroups (workspace needed either
@@ -486,8 +489,9 @@ def test_forward_grouped(gpu_lib, M, K, Ns):
 
 @pytest.mark.parametrize("with_outputs", [True, False], ids=["outs", "noouts"])
 @pytest.mark.parametrize("M,K,Ns", [(1, 4096, (1024, 512, 512)), (2, 3200, (8640, 64)),
-                                    (5, 1040, (300, 17)), (48, 4096, (200, 64))],
-                         ids=["fusedM1", "twoM2", "smallM5", "gemmM48"])
+                                    (5, 1040, (300, 17)), (48, 4096, (200, 64)),
+                                    (1, 4096, (11008, 4096, 1004))],
+                         ids=["fusedM1", "twoM2", "smallM5", "gemmM48", "wideM1"])
 def test_forward_f32_grouped(gpu_lib, M, K, Ns, with_outputs):
     """Quantise once, then every projection: the quantiser outputs and each
     projection's accumulators as the oracle's."""
