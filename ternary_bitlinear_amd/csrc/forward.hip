@@ -2188,9 +2188,9 @@ int device_cus() {
 // 28672 with 28672 -> 8192 22.08 against 22.13 us, 7B 7.99 against 8.89 us,
 // 3B 6.26 against 7.25 us (at 3B and 7B sizes a wave has 2-4 steps, which a
 // ring of two runs as whole unguarded rounds); 2 rows per step, or deeper
-// rings, were slower.  Against two fused single-projection calls: 70B 22.1
-// against 33.6 us.  (One projection alone is slower than the
-// single-projection kernels, which keep those calls.)
+// rings, were slower.  Against two fused single-projection calls on the
+// earlier kernels: 70B 22.1 against 33.6 us.  (Single projections take this
+// launch from 2^25 weights: stream_single.)
 constexpr int kStreamR = 4, kStreamP = 1, kStreamWV = 8;
 
 StreamArgs stream_args(int G, const uint8_t* const* Wp, const float* const* gamma,
