@@ -1086,12 +1086,28 @@ def traffic_key(kernel, shapes, M, out, fused=False):
             + ",".join(f"{P.K}->{P.N}" for P in shapes) + f" {out}")
 
 
-def forward_source_digest():
-    """Digest of the sources the projection kernels are compiled from."""
+def source_code_text(text):
+    """C++ source with its comments removed and every run of whitespace made
+    one space (so that an edit of a comment or of the layout does not mark
+    the counters taken on the code as stale)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
+def forward_source_digest(read=None):
+    """Digest of the code (source_code_text) of the sources the
+    projection kernels are compiled from.  read(name) -> text; default: the
+    files in the tree."""
     import hashlib
+    if read is None:
+        def read(name):
+            with open(os.path.join(ROOT, "ternary_bitlinear_amd", "csrc", name)) as f:
+                return f.read()
     h = hashlib.sha256()
     for name in ("forward.hip", "common.hpp", "stream.hpp"):
-        h.update(open(os.path.join(ROOT, "ternary_bitlinear_amd", "csrc", name), "rb").read())
+        h.update(source_code_text(read(name)).encode())
     return h.hexdigest()[:16]
 
 
