@@ -1480,7 +1480,10 @@ __device__ __forceinline__ void skinny_step(const int8_t* __restrict__ Ac,
 }
 
 // Work unit: one workgroup (RB row blocks of one projection).
-template <int TG, int RB, int NWK, int SP, int OUT>
+// TS: the tokens split in halves of 16 TG, one workgroup per (row group,
+// half); the halves of a row group sit 8 workgroups apart, on one XCD, when
+// the row groups are a multiple of 8.
+template <int TG, int RB, int NWK, int SP, int OUT, bool TS = false>
 __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
   constexpr int NWV = RB * NWK;               // waves
   constexpr int CK = 256 * NWK;               // k per chunk
@@ -1511,9 +1514,26 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
   // With K split S ways (one projection), the S workgroups of a row group
   // are adjacent and split sp takes chunks [cb, cb + nch).
   const int S = da.splits > 1 ? da.splits : 1;
-  const int wg = blockIdx.x / S, sp = blockIdx.x - wg * S;
+  int wg = blockIdx.x / S, half = 0;
+  if constexpr (TS) {
+    const int units = (int)(gridDim.x >> 1);
+    if ((units & 7) == 0) {
+      const int slot = (int)blockIdx.x >> 3;
+      wg = (slot >> 1) * 8 + ((int)blockIdx.x & 7);
+      half = slot & 1;
+    } else {
+      wg = (int)blockIdx.x % units;
+      half = (int)blockIdx.x / units;
+    }
+  }
+  const int sp = TS ? 0 : (int)blockIdx.x - wg * S;
   const DecodeView view = decode_view(da, wg);
-  const int N = view.N, K = da.K, M = da.M;
+  // this workgroup's tokens: [mh, mh + M)
+  const int mh = half * 16 * TG;
+  const int N = view.N, K = da.K, M = TS ? min(da.M - mh, 16 * TG) : da.M;
+  const int8_t* const Xq = da.Xq + (int64_t)mh * K;
+  const float* const xsc = da.xs + mh;
+  const int32_t* const xsm = da.xsum + mh;
   const uint8_t* const Wp = view.Wp;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1536,8 +1556,8 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = min(16 * tg + 4 * g + r, M - 1);
-      sxv[tg][r] = da.xsum[m];
-      scv[tg][r] = da.xs[m];
+      sxv[tg][r] = xsm[m];
+      scv[tg][r] = xsc[m];
     }
 
   // Direct loads of chunk c: activation blocks wave, wave + NWV, ... and the
@@ -1554,7 +1574,7 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
       const int q = ((off % CK) / 16) ^ (r & 15);
       const int m = min(r, M - 1);
       const int k = min((cb + c) * CK + 16 * q, K - 16);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(da.Xq + (int64_t)m * K + k),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Xq + (int64_t)m * K + k),
                                        static_cast<void*>(A + 1024 * b), 16, 0, 0);
     }
     {
@@ -1638,9 +1658,18 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * tg + 4 * g + r;
-      if (m < M) store_out<OUT>(view.Y, (int64_t)m * N + n, v[r] - sxv[tg][r], gamma, scv[tg][r]);
+      if (m < M)
+        store_out<OUT>(view.Y, (int64_t)(mh + m) * N + n, v[r] - sxv[tg][r], gamma, scv[tg][r]);
     }
   }
+}
+
+// 33-64 tokens as two halves of 32 (TS form of k_skinny; no K split)
+template <int RB, int NWK, int OUT>
+hipError_t launch_skinny_ts_t(DecodeArgs da, hipStream_t stream) {
+  const int grid = set_units(da, 16 * RB) * 2;
+  k_skinny<2, RB, NWK, 2, OUT, true><<<dim3(grid), dim3(RB * NWK * kWave), 0, stream>>>(da);
+  return hipGetLastError();
 }
 
 template <int TG, int RB, int NWK, int SP, int OUT>
@@ -1710,18 +1739,26 @@ hipError_t launch_skinny(const DecodeArgs& da, hipStream_t stream) {
   const int nrb = decode_rows(da) / 16;
   if (da.M <= 16) return launch_skinny_tg<1, OUT>(da, nrb, stream);
   if (da.M <= 32) return launch_skinny_tg<2, OUT>(da, nrb, stream);
-  // 33-64 tokens (at 2 waves per row block, activation stages of 32 KB and
-  // one workgroup per CU): as
-  // many row blocks per workgroup as keep the launch to one round of at most
-  // 256 workgroups, 2 waves per row block, and 8 one-wave row blocks past
-  // 1024 row blocks.  Timed at 64 tokens: 4096 rows 8.9 us at 2 row blocks
-  // (9.4 at 1); 11008 rows 10.3 us at 3 (16.6 at 2, two rounds); 28672 rows
-  // 23.7 us at 8 one-wave row blocks (29.5 at 4 of 2 waves, two rounds).
+  // 33-64 tokens, one workgroup per CU.  Up to 512 row blocks: the tokens in
+  // two halves of 32 (the TS form), each workgroup taking twice the rows of
+  // one half, so that a CU takes in half the activations.  Timed at 33 / 48
+  // / 64 tokens (bf16 out, rotated weights): 4096 <- 4096 7.13 / 7.14 / 7.53
+  // against 8.23 / 8.40 / 8.83 us for all 64 tokens per workgroup, 8192 <-
+  // 8192 10.83 / 10.87 / 11.22 against 12.78 / 13.05 / 13.87 us.  Wider
+  // outputs keep all tokens per workgroup (11008 rows: 9.83 / 9.84 / 10.04
+  // split against 9.57 / 10.09 / 10.57 us; 28672 rows: 29.1-29.7 split
+  // against 25.5-27.7 us): as many row blocks per workgroup as keep the
+  // launch to one round of at most 256 workgroups, 2 waves per row block,
+  // and 8 one-wave row blocks past 1024 row blocks (at 64 tokens 11008 rows
+  // 10.3 us at 3 row blocks, 16.6 at 2 in two rounds; 28672 rows 23.7 us at 8
+  // one-wave row blocks, 29.5 at 4 of 2 waves in two rounds).
+  if (nrb <= 512) {
+    if (nrb > 128) return launch_skinny_ts_t<4, 2, OUT>(da, stream);
+    return launch_skinny_ts_t<2, 2, OUT>(da, stream);
+  }
   if (nrb > 1024) return launch_skinny_t<4, 8, 1, 2, OUT>(da, stream);
   if (nrb > 768) return launch_skinny_t<4, 4, 2, 2, OUT>(da, stream);
-  if (nrb > 512) return launch_skinny_t<4, 3, 2, 2, OUT>(da, stream);
-  if (nrb > 128) return launch_skinny_t<4, 2, 2, 2, OUT>(da, stream);
-  return launch_skinny_t<4, 1, 2, 2, OUT>(da, stream);
+  return launch_skinny_t<4, 3, 2, 2, OUT>(da, stream);
 }
 
 // 17-64 tokens on one projection whose K is long against its rows (K >= 2 N,
