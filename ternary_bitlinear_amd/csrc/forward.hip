@@ -1664,11 +1664,11 @@ __global__ __launch_bounds__(RB * NWK * kWave) void k_skinny(DecodeArgs da) {
   }
 }
 
-// 33-64 tokens as two halves of 32 (TS form of k_skinny; no K split)
-template <int RB, int NWK, int OUT>
+// The tokens as two halves of 16 TG (TS form of k_skinny; no K split)
+template <int TG, int RB, int NWK, int SP, int OUT>
 hipError_t launch_skinny_ts_t(DecodeArgs da, hipStream_t stream) {
   const int grid = set_units(da, 16 * RB) * 2;
-  k_skinny<2, RB, NWK, 2, OUT, true><<<dim3(grid), dim3(RB * NWK * kWave), 0, stream>>>(da);
+  k_skinny<TG, RB, NWK, SP, OUT, true><<<dim3(grid), dim3(RB * NWK * kWave), 0, stream>>>(da);
   return hipGetLastError();
 }
 
@@ -1738,7 +1738,18 @@ template <int OUT>
 hipError_t launch_skinny(const DecodeArgs& da, hipStream_t stream) {
   const int nrb = decode_rows(da) / 16;
   if (da.M <= 16) return launch_skinny_tg<1, OUT>(da, nrb, stream);
-  if (da.M <= 32) return launch_skinny_tg<2, OUT>(da, nrb, stream);
+  if (da.M <= 32) {
+    // 17-32 tokens on up to 512 row blocks: two halves of 16 tokens, each
+    // workgroup taking twice the rows (the TS form, as at 33-64 tokens
+    // below).  Timed at 17 / 24 / 32 tokens: 4096 <- 4096 4.76 / 4.88 / 4.92
+    // against 5.31 / 5.59 / 5.73 us, 8192 <- 8192 8.86 / 8.99 / 9.05 against
+    // 9.00 / 9.70 / 10.06 us (identical output bytes).
+    if (da.M > 16 && nrb <= 512) {
+      if (nrb >= 384) return launch_skinny_ts_t<1, 4, 2, 3, OUT>(da, stream);
+      return launch_skinny_ts_t<1, 2, 4, 3, OUT>(da, stream);
+    }
+    return launch_skinny_tg<2, OUT>(da, nrb, stream);
+  }
   // 33-64 tokens, one workgroup per CU.  Up to 512 row blocks: the tokens in
   // two halves of 32 (the TS form), each workgroup taking twice the rows of
   // one half, so that a CU takes in half the activations.  Timed at 33 / 48
@@ -1753,8 +1764,8 @@ hipError_t launch_skinny(const DecodeArgs& da, hipStream_t stream) {
   // 10.3 us at 3 row blocks, 16.6 at 2 in two rounds; 28672 rows 23.7 us at 8
   // one-wave row blocks, 29.5 at 4 of 2 waves in two rounds).
   if (nrb <= 512) {
-    if (nrb > 128) return launch_skinny_ts_t<4, 2, OUT>(da, stream);
-    return launch_skinny_ts_t<2, 2, OUT>(da, stream);
+    if (nrb > 128) return launch_skinny_ts_t<2, 4, 2, 2, OUT>(da, stream);
+    return launch_skinny_ts_t<2, 2, 2, 2, OUT>(da, stream);
   }
   if (nrb > 1024) return launch_skinny_t<4, 8, 1, 2, OUT>(da, stream);
   if (nrb > 768) return launch_skinny_t<4, 4, 2, 2, OUT>(da, stream);
