@@ -1788,6 +1788,11 @@ struct SkinnySplit {
 inline SkinnySplit skinny_split_cfg(int64_t M, int64_t N, int64_t K) {
   SkinnySplit c{0, 0, 1};
   if (M < 17 || M > 64 || K % 64 != 0 || K < 2 * N || M * K <= 256 * 1024) return c;
+  // 17-32 tokens on up to 512 row blocks: the token halves of launch_skinny
+  // instead (no reduction launch).  Timed at 24 / 32 tokens: 4096 <- 11008
+  // 8.05 / 8.48 against 9.55 / 9.74 us split, 8192 <- 28672 20.90 / 21.59
+  // against 22.79 / 24.99 us (identical output bytes).
+  if (M <= 32 && (N + 15) / 16 <= 512) return c;
   const int64_t nrb = (N + 15) / 16;
   c.tg = M <= 32 ? 2 : 4;
   c.rb = (c.tg == 4 && nrb >= 512) ? 8 : 4;

@@ -264,15 +264,19 @@ def test_skinny_split_rule():
     ws = tb.forward_workspace_bytes
     assert ws(64, 4096, 11008) == 4 * 64 * 4096 * 4        # 64 row groups, S = 4
     assert ws(64, 8192, 28672) == 4 * 64 * 8192 * 4        # 8 row blocks: 64 groups, S = 4
-    assert ws(32, 8192, 28672) == 2 * 32 * 8192 * 4        # 128 groups, S = 2
-    assert ws(32, 4096, 11008) == 4 * 32 * 4096 * 4
-    assert ws(17, 1000, 16384) == -(-4 * 17 * 1000 * 4 // 256) * 256   # ragged N; 256 B units
+    assert ws(32, 9000, 28672) == 2 * 32 * 9000 * 4        # 141 groups, S = 2
+    assert ws(17, 8200, 16448) == -(-2 * 17 * 8200 * 4 // 256) * 256   # 256 B units
+    assert ws(33, 999, 8192) == -(-4 * 33 * 999 * 4 // 256) * 256      # ragged N
+    # 17-32 tokens on up to 512 row blocks: token halves, no split
+    assert ws(32, 8192, 28672) == 0
+    assert ws(32, 4096, 11008) == 0
+    assert ws(17, 1000, 16384) == 0
     assert ws(16, 4096, 11008) == 0                        # 16 tokens: unsplit skinny
     assert ws(64, 11008, 4096) == 0                        # K < 2 N
     assert ws(20, 4096, 8192) == 0                         # M K <= 256 Ki
     # 9 chunks: 4 splits of ceil(9 / 4) = 3 would leave the last one empty
     assert ws(64, 2000, 4160) == 3 * 64 * 2000 * 4
-    for M, N, K in ((64, 4096, 11008), (17, 1000, 16384), (32, 8192, 28672)):
+    for M, N, K in ((64, 4096, 11008), (17, 8200, 16448), (32, 9000, 28672)):
         assert tb.forward_kernel("forward", M, [N], K) == ("k_skinny", False)
         assert tb.forward_f32_workspace_bytes(M, N, K) >= ws(M, N, K) > 0
 
@@ -402,7 +406,7 @@ def test_multi_workspace_holds_every_input(lib):
     Ns, Ks = [3000, 1000], [1024, 3008]
     assert q(16, Ns, Ks) == sum(r(16 * k) + r(8 * 16) for k in Ks)
     Ns, Ks = [1024, 300, 64], [11008, 512, 4096]
-    split = lib.bitlinear_forward_workspace_bytes(32, 1024, 11008)
+    split = lib.bitlinear_forward_workspace_bytes(48, 1024, 11008)
     assert split > 0
-    assert q(32, Ns, Ks) == sum(r(32 * k) + r(8 * 32) for k in Ks) + split
+    assert q(48, Ns, Ks) == sum(r(48 * k) + r(8 * 48) for k in Ks) + split
     assert q(1, [28672, 8192], [8192, 28672]) == 0   # the one-launch path

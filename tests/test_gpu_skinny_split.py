@@ -17,8 +17,11 @@ pytestmark = pytest.mark.gpu
 # ragged N (1000, 999, 8200: the last row group part-empty; 999 also rules
 # out vector stores); K ending inside a 512-wide chunk (11008) or 64 into one
 # (16448); 2 to 4 splits (3 where 4 would leave a split without a chunk).
-SPLIT_SHAPES = [(17, 1000, 16384), (32, 4096, 11008), (33, 999, 8192), (48, 2000, 8192),
+SPLIT_SHAPES = [(17, 8200, 16448), (32, 8200, 16448), (33, 999, 8192), (48, 2000, 8192),
                 (40, 300, 65536), (64, 8200, 16448), (64, 2000, 4160)]
+# 17-32 tokens on up to 512 row blocks with a long K: no split, the token
+# halves of the skinny kernel instead (ragged N, K past a 512-wide chunk)
+HALVES_SHAPES = [(17, 1000, 16384), (32, 4096, 11008), (24, 64, 65536), (29, 999, 8256)]
 
 
 def _is_split(M, N, K):
@@ -48,7 +51,7 @@ def test_split_extreme_accumulators(gpu_lib):
     """All weights +-1 and activations +-127 over K = 65536: |acc| = 127 K,
     each split's partial and the total within int32."""
     import torch
-    M, N, K = 24, 64, 65536
+    M, N, K = 40, 64, 65536
     assert _is_split(M, N, K)
     Wt = np.ones((N, K), np.int8)
     Wt[1::2] = -1
@@ -62,7 +65,7 @@ def test_split_extreme_accumulators(gpu_lib):
     assert_equal(host(acc).astype(np.int64), O.integer_matmul(Wt, Xq), "accumulators")
 
 
-WHOLE = [(17, 1000, 16384), (33, 999, 8192), (40, 300, 65536)]
+WHOLE = [(48, 1000, 16384), (33, 999, 8192), (40, 300, 65536)]
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "i32"])
@@ -121,3 +124,22 @@ def test_split_workspace_reuse_and_side_stream(gpu_lib):
     s.synchronize()
     for m, acc in zip((48, 33), outs):
         assert_equal(host(acc).astype(np.int64), O.integer_matmul(Wt, Xq[:m]), f"M={m}")
+
+
+@pytest.mark.parametrize("M,N,K", HALVES_SHAPES, ids=[f"M{m}N{n}K{k}" for m, n, k in HALVES_SHAPES])
+def test_halves_instead_of_split_int32(gpu_lib, M, N, K):
+    """Long-K shapes that the split used to take at 17-32 tokens: the token
+    halves, no workspace, and exact int32 accumulators."""
+    import torch
+    import ternary_bitlinear_amd as tb
+    assert tb.forward_kernel("forward", M, [N], K) == ("k_skinny", False)
+    assert tb.forward_workspace_bytes(M, N, K) == 0
+    rng = np.random.default_rng(M * 7919 + N * 31 + K + 1)
+    Wt = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    Xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    xsum = Xq.astype(np.int64).sum(1).astype(np.int32)
+    acc = gpu_lib.bitlinear_forward(dev(O.pack_codes(Wt)), dev(np.array([1.0], np.float32)),
+                                    dev(Xq), dev(np.ones(M, np.float32)), dev(xsum), N=N, K=K,
+                                    y_dtype="i32")
+    torch.cuda.synchronize()
+    assert_equal(host(acc).astype(np.int64), O.integer_matmul(Wt, Xq), "int32 accumulators")
